@@ -1,0 +1,164 @@
+"""fp64 CPU oracle for exact attention -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  The product library
+(``exact_attention_79_amd``) never imports it and the two share no code.
+
+The arithmetic lives in ``attn_oracle.c`` (plain fp64 loops, OpenMP over
+rows); this module only marshals numpy arrays through ctypes.  What each
+routine computes, and which passage of the pages it follows, is written in
+the C file's comments.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "attn_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+# -ffp-contract=off keeps every fp64 multiply and add separately rounded, so
+# the oracle gives the same bits on any x86-64 host it is run on.
+CFLAGS = ["-O3", "-march=x86-64-v2", "-ffp-contract=off", "-fopenmp",
+          "-shared", "-fPIC", "-std=c11"]
+
+
+def build(force: bool = True) -> str:
+    """Compile attn_oracle.c into liboracle.so with gcc."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call(["gcc", *CFLAGS, _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build(force=True)
+        L = ctypes.CDLL(_LIB)
+        dp = ctypes.POINTER(ctypes.c_double)
+        i, lg, d = ctypes.c_int, ctypes.c_long, ctypes.c_double
+        L.oracle_bf16_decode.argtypes = [ctypes.c_void_p, dp, lg]
+        L.oracle_e4m3_decode.argtypes = [ctypes.c_void_p, d, dp, lg]
+        L.oracle_e4m3_to_f64.argtypes = [ctypes.c_uint8]
+        L.oracle_e4m3_to_f64.restype = d
+        L.oracle_visible.argtypes = [lg, lg, i, lg]
+        L.oracle_visible.restype = i
+        L.oracle_fwd.argtypes = [i, i, i, d, i, lg, dp, dp, dp, dp, dp, i]
+        L.oracle_fwd_rows.argtypes = [i, i, d, i, lg, dp, dp, dp,
+                                      ctypes.POINTER(lg), i, dp, dp, i]
+        L.oracle_probs_row.argtypes = [i, i, d, i, lg, dp, dp, dp, lg, dp]
+        L.oracle_bwd.argtypes = [i, i, i, d, i, lg, dp, dp, dp, dp, dp, dp, dp, dp, i]
+        L.oracle_online_fwd.argtypes = [i, i, d, i, lg, dp, dp, dp,
+                                        ctypes.POINTER(lg), i, i, dp, dp]
+        _lib = L
+    return _lib
+
+
+def _p(a: np.ndarray):
+    assert a.dtype == np.float64 and a.flags.c_contiguous
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def _f64(a) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def decode_bf16(bits: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns (uint16) -> exact fp64 values."""
+    bits = np.ascontiguousarray(bits, dtype=np.uint16)
+    out = np.empty(bits.shape, np.float64)
+    lib().oracle_bf16_decode(bits.ctypes.data, _p(out), bits.size)
+    return out
+
+
+def decode_e4m3(codes: np.ndarray, descale: float = 1.0) -> np.ndarray:
+    """OCP e4m3 codes (uint8) -> code value * descale, in fp64."""
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    out = np.empty(codes.shape, np.float64)
+    lib().oracle_e4m3_decode(codes.ctypes.data, float(descale), _p(out), codes.size)
+    return out
+
+
+def visible(i: int, j: int, causal: bool, window: int) -> bool:
+    return bool(lib().oracle_visible(i, j, int(causal), int(window)))
+
+
+def fwd(q, k, v, scale: float, causal: bool = False, window: int = 0,
+        nthreads: int = 0):
+    """O and L (natural-log LSE of the scaled scores) for tensors [..., N, d]."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    assert q.shape == k.shape == v.shape and q.ndim >= 2
+    N, d = q.shape[-2:]
+    BH = int(np.prod(q.shape[:-2])) if q.ndim > 2 else 1
+    o = np.empty_like(q)
+    lse = np.empty(q.shape[:-1], np.float64)
+    lib().oracle_fwd(BH, N, d, float(scale), int(causal), int(window),
+                     _p(q), _p(k), _p(v), _p(o), _p(lse), int(nthreads))
+    return o, lse
+
+
+def fwd_rows(q, k, v, rows, scale: float, causal: bool = False, window: int = 0,
+             nthreads: int = 0):
+    """O and L for the listed query rows of ONE head (q, k, v: [N, d])."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    N, d = q.shape
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    assert rows.ndim == 1 and (rows >= 0).all() and (rows < N).all()
+    o = np.empty((rows.size, d), np.float64)
+    lse = np.empty(rows.size, np.float64)
+    lib().oracle_fwd_rows(N, d, float(scale), int(causal), int(window),
+                          _p(q), _p(k), _p(v),
+                          rows.ctypes.data_as(ctypes.POINTER(ctypes.c_long)),
+                          rows.size, _p(o), _p(lse), int(nthreads))
+    return o, lse
+
+
+def probs_row(q, k, v, i: int, scale: float, causal: bool = False, window: int = 0):
+    """The probability row P_i of ONE head."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    N, d = q.shape
+    p = np.empty(N, np.float64)
+    lib().oracle_probs_row(N, d, float(scale), int(causal), int(window),
+                           _p(q), _p(k), _p(v), int(i), _p(p))
+    return p
+
+
+def bwd(q, k, v, dout, scale: float, causal: bool = False, window: int = 0,
+        nthreads: int = 0):
+    """dQ, dK, dV and D (D_i = sum_j P_ij dP_ij) for tensors [..., N, d]."""
+    q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+    assert q.shape == k.shape == v.shape == dout.shape
+    N, d = q.shape[-2:]
+    BH = int(np.prod(q.shape[:-2])) if q.ndim > 2 else 1
+    dq, dk, dv = np.empty_like(q), np.empty_like(q), np.empty_like(q)
+    D = np.empty(q.shape[:-1], np.float64)
+    lib().oracle_bwd(BH, N, d, float(scale), int(causal), int(window),
+                     _p(q), _p(k), _p(v), _p(dout), _p(dq), _p(dk), _p(dv),
+                     _p(D), int(nthreads))
+    return dq, dk, dv, D
+
+
+def online_fwd(q, k, v, bounds, form: int, scale: float, causal: bool = False,
+               window: int = 0):
+    """Block recurrence over the key partition ``bounds`` (form 1 or 2), ONE head."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    N, d = q.shape
+    b = np.ascontiguousarray(bounds, dtype=np.int64)
+    assert b[0] == 0 and b[-1] == N and (np.diff(b) > 0).all()
+    o = np.empty_like(q)
+    lse = np.empty(N, np.float64)
+    lib().oracle_online_fwd(N, d, float(scale), int(causal), int(window),
+                            _p(q), _p(k), _p(v),
+                            b.ctypes.data_as(ctypes.POINTER(ctypes.c_long)),
+                            b.size - 1, int(form), _p(o), _p(lse))
+    return o, lse

@@ -1,0 +1,310 @@
+/*
+ * attn_oracle.c -- plain, slow fp64 CPU oracle for exact attention.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may link, load or
+ * call this file; only tests/, the smoke check and the CPU-baseline leg of the
+ * benchmark do.  It shares no code, header or constant with the HIP library.
+ *
+ * What it computes (per head, all tensors row-major [N][d], fp64):
+ *
+ *   S = s * Q K^T,  P = softmax(S) row-wise,  O = P V,  L_i = m_i + ln(l_i)
+ *
+ * following the standard-attention definition and the softmax decomposition
+ * (m, f, l) in the FLASH-ATTN page (taking-lying-flat), FlashAttention paper
+ * summary, sections "Background" (standard attention) and "Tiling and
+ * Recomputation" (definitions of m(x), f(x), l(x), softmax(x)); the LSE
+ * statistic L = m + log(l) is from the same page's FlashAttention-2 section.
+ * The causal mask (S_ij = -inf for j > i) is from the FlashAttention-2 section
+ * of that page.  The softmax scale s and the sliding window are not written in
+ * the pages' formulas; s multiplies Q K^T, and a window W > 0 keeps key j for
+ * query i when i - j < W (causal) or |i - j| < W (non-causal).
+ *
+ * The backward follows the chain rule listed in the FlashAttention-2 section
+ * "Background" of the FLASH-ATTN page: dV = P^T dO, dP = dO V^T,
+ * dS = dsoftmax(dP), dQ = dS K, dK = dS^T Q, with dsoftmax written out as the
+ * softmax Jacobian dS_ij = P_ij (dP_ij - sum_k P_ik dP_ik) and the scale s
+ * carried through the chain rule into dQ and dK.
+ *
+ * Every quantity is an explicit fp64 array: one full score row per query in
+ * the forward, and the full N x N matrices P and dS of one head in the
+ * backward.  No blocking, no fused recurrence: the online (block-by-block)
+ * recurrences live in oracle_online_fwd only, which exists to check the
+ * plain definition against the pages' decomposition identities.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#include <omp.h>
+
+/* ---- number formats: decoding only (the inputs arrive already encoded) ---- */
+
+/* bf16 is the upper half of an IEEE binary32; widening is exact. */
+double oracle_bf16_to_f64(uint16_t b) {
+  uint32_t u = ((uint32_t)b) << 16;
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return (double)f;
+}
+
+void oracle_bf16_decode(const uint16_t* src, double* dst, long n) {
+  for (long i = 0; i < n; ++i) dst[i] = oracle_bf16_to_f64(src[i]);
+}
+
+/* OCP FP8 E4M3 ("fn" variant): 1 sign, 4 exponent bits (bias 7), 3 mantissa
+ * bits; exponent field 0 is subnormal (m * 2^-9); S.1111.111 is NaN; there is
+ * no infinity, so the largest finite value is 1.75 * 2^8 = 448. */
+double oracle_e4m3_to_f64(uint8_t c) {
+  int sign = (c >> 7) & 1;
+  int e = (c >> 3) & 0xF;
+  int m = c & 0x7;
+  double v;
+  if (e == 0xF && m == 0x7) return NAN;
+  if (e == 0)
+    v = ldexp((double)m, -9);
+  else
+    v = ldexp(1.0 + (double)m / 8.0, e - 7);
+  return sign ? -v : v;
+}
+
+/* x = code_value * descale */
+void oracle_e4m3_decode(const uint8_t* src, double descale, double* dst, long n) {
+  for (long i = 0; i < n; ++i) dst[i] = oracle_e4m3_to_f64(src[i]) * descale;
+}
+
+/* ---- visibility: which keys a query may attend to ---- */
+int oracle_visible(long i, long j, int causal, long window) {
+  if (causal && j > i) return 0;
+  if (window > 0) {
+    long diff = i - j;
+    if (diff < 0) diff = -diff;
+    if (diff >= window) return 0;
+  }
+  return 1;
+}
+
+static double dot(const double* a, const double* b, int d) {
+  double acc = 0.0;
+  for (int k = 0; k < d; ++k) acc += a[k] * b[k];
+  return acc;
+}
+
+/* One query row i of one head: explicit score row S_i, its max m_i, the sum
+ * l_i = sum_j exp(S_ij - m_i), the probability row P_i, O_i = P_i V and
+ * L_i = m_i + ln(l_i).  srow and prow are caller scratch of length N. */
+static void fwd_row(int N, int d, double scale, int causal, long window,
+                    const double* q, const double* k, const double* v, long i,
+                    double* srow, double* prow, double* o_row, double* lse_out) {
+  const double* qi = q + (long)i * d;
+  double m = -INFINITY;
+  for (long j = 0; j < N; ++j) {
+    if (oracle_visible(i, j, causal, window)) {
+      srow[j] = scale * dot(qi, k + j * (long)d, d);
+      if (srow[j] > m) m = srow[j];
+    } else {
+      srow[j] = -INFINITY;
+    }
+  }
+  double l = 0.0;
+  for (long j = 0; j < N; ++j) {
+    prow[j] = (srow[j] == -INFINITY) ? 0.0 : exp(srow[j] - m);
+    l += prow[j];
+  }
+  for (long j = 0; j < N; ++j) prow[j] /= l;
+  for (int c = 0; c < d; ++c) o_row[c] = 0.0;
+  for (long j = 0; j < N; ++j) {
+    if (prow[j] == 0.0) continue;
+    const double* vj = v + j * (long)d;
+    for (int c = 0; c < d; ++c) o_row[c] += prow[j] * vj[c];
+  }
+  if (lse_out) *lse_out = m + log(l);
+}
+
+/* Forward over BH heads, every row.  q,k,v,o: [BH][N][d]; lse: [BH][N]
+ * (may be NULL).  Rows are independent, so they are spread over threads. */
+void oracle_fwd(int BH, int N, int d, double scale, int causal, long window,
+                const double* q, const double* k, const double* v, double* o,
+                double* lse, int nthreads) {
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+  long total = (long)BH * N;
+#pragma omp parallel
+  {
+    double* srow = (double*)malloc(sizeof(double) * (size_t)N);
+    double* prow = (double*)malloc(sizeof(double) * (size_t)N);
+#pragma omp for schedule(dynamic, 16)
+    for (long r = 0; r < total; ++r) {
+      long h = r / N, i = r % N;
+      long off = h * (long)N * d;
+      fwd_row(N, d, scale, causal, window, q + off, k + off, v + off, i, srow,
+              prow, o + r * d, lse ? lse + r : NULL);
+    }
+    free(srow);
+    free(prow);
+  }
+}
+
+/* Forward for selected rows of one head (rows[t] in [0,N)); o_rows: [nrows][d]. */
+void oracle_fwd_rows(int N, int d, double scale, int causal, long window,
+                     const double* q, const double* k, const double* v,
+                     const long* rows, int nrows, double* o_rows,
+                     double* lse_rows, int nthreads) {
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+#pragma omp parallel
+  {
+    double* srow = (double*)malloc(sizeof(double) * (size_t)N);
+    double* prow = (double*)malloc(sizeof(double) * (size_t)N);
+#pragma omp for schedule(dynamic, 1)
+    for (int t = 0; t < nrows; ++t)
+      fwd_row(N, d, scale, causal, window, q, k, v, rows[t], srow, prow,
+              o_rows + (long)t * d, lse_rows ? lse_rows + t : NULL);
+    free(srow);
+    free(prow);
+  }
+}
+
+/* The probability row P_i of one head (for the row-sum and closed-form pins). */
+void oracle_probs_row(int N, int d, double scale, int causal, long window,
+                      const double* q, const double* k, const double* v, long i,
+                      double* prow) {
+  double* srow = (double*)malloc(sizeof(double) * (size_t)N);
+  double* o_row = (double*)malloc(sizeof(double) * (size_t)d);
+  fwd_row(N, d, scale, causal, window, q, k, v, i, srow, prow, o_row, NULL);
+  free(srow);
+  free(o_row);
+}
+
+/* Backward over BH heads.  Inputs q,k,v,dout: [BH][N][d].  Outputs dq,dk,dv:
+ * [BH][N][d]; Dvec: [BH][N] receives D_i = sum_j P_ij dP_ij (may be NULL).
+ * Per head: pass 1 builds the explicit rows of P and dS (and dQ) one query
+ * at a time; pass 2 forms dV_j = sum_i P_ij dO_i and dK_j = s sum_i dS_ij Q_i
+ * one key at a time from the stored matrices. */
+void oracle_bwd(int BH, int N, int d, double scale, int causal, long window,
+                const double* q, const double* k, const double* v,
+                const double* dout, double* dq, double* dk, double* dv,
+                double* Dvec, int nthreads) {
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+  double* P = (double*)malloc(sizeof(double) * (size_t)N * (size_t)N);
+  double* dS = (double*)malloc(sizeof(double) * (size_t)N * (size_t)N);
+  for (int h = 0; h < BH; ++h) {
+    long off = (long)h * N * d;
+    const double *qh = q + off, *kh = k + off, *vh = v + off, *doh = dout + off;
+#pragma omp parallel
+    {
+      double* srow = (double*)malloc(sizeof(double) * (size_t)N);
+      double* dprow = (double*)malloc(sizeof(double) * (size_t)N);
+      double* o_row = (double*)malloc(sizeof(double) * (size_t)d);
+#pragma omp for schedule(dynamic, 8)
+      for (long i = 0; i < N; ++i) {
+        double* prow = P + i * (long)N;
+        double* dsrow = dS + i * (long)N;
+        fwd_row(N, d, scale, causal, window, qh, kh, vh, i, srow, prow, o_row, NULL);
+        /* dP_i = dO_i V^T */
+        for (long j = 0; j < N; ++j)
+          dprow[j] = oracle_visible(i, j, causal, window)
+                         ? dot(doh + i * (long)d, vh + j * (long)d, d)
+                         : 0.0;
+        /* D_i = sum_j P_ij dP_ij ; dS_ij = P_ij (dP_ij - D_i) */
+        double Di = 0.0;
+        for (long j = 0; j < N; ++j) Di += prow[j] * dprow[j];
+        for (long j = 0; j < N; ++j) dsrow[j] = prow[j] * (dprow[j] - Di);
+        if (Dvec) Dvec[(long)h * N + i] = Di;
+        /* dQ_i = s sum_j dS_ij K_j */
+        double* dqi = dq + off + i * (long)d;
+        for (int c = 0; c < d; ++c) dqi[c] = 0.0;
+        for (long j = 0; j < N; ++j) {
+          if (dsrow[j] == 0.0) continue;
+          const double* kj = kh + j * (long)d;
+          for (int c = 0; c < d; ++c) dqi[c] += dsrow[j] * kj[c];
+        }
+        for (int c = 0; c < d; ++c) dqi[c] *= scale;
+      }
+      free(srow);
+      free(dprow);
+      free(o_row);
+    }
+#pragma omp parallel for schedule(dynamic, 8)
+    for (long j = 0; j < N; ++j) {
+      double* dvj = dv + off + j * (long)d;
+      double* dkj = dk + off + j * (long)d;
+      for (int c = 0; c < d; ++c) dvj[c] = dkj[c] = 0.0;
+      for (long i = 0; i < N; ++i) {
+        double p = P[i * (long)N + j], ds = dS[i * (long)N + j];
+        const double* doi = doh + i * (long)d;
+        const double* qi = qh + i * (long)d;
+        if (p != 0.0)
+          for (int c = 0; c < d; ++c) dvj[c] += p * doi[c];
+        if (ds != 0.0)
+          for (int c = 0; c < d; ++c) dkj[c] += ds * qi[c];
+      }
+      for (int c = 0; c < d; ++c) dkj[c] *= scale;
+    }
+  }
+  free(P);
+  free(dS);
+}
+
+/* Block-by-block recurrences over a partition of the keys of one head, for
+ * cross-checking oracle_fwd against the decomposition identities of the
+ * FLASH-ATTN page.  bounds[0]=0 < bounds[1] < ... < bounds[nparts]=N.
+ *   form 1: the FlashAttention online softmax, where the output is kept
+ *           normalised after every block, O <- diag(l_old/l_new * e^{m_old-m_new}) O
+ *           + diag(l_new)^{-1} e^{S_blk - m_new} V_blk ("Tiling and Recomputation"
+ *           and the two-block online-softmax equations of the FlashAttention-2
+ *           section);
+ *   form 2: the FlashAttention-2 form with an unnormalised accumulator,
+ *           O~ <- diag(e^{m_old-m_new}) O~ + e^{S_blk - m_new} V_blk, divided by
+ *           l once at the end (FlashAttention-2 section).
+ * Rows whose visible set is still empty keep m = -inf, l = 0, O = 0. */
+void oracle_online_fwd(int N, int d, double scale, int causal, long window,
+                       const double* q, const double* k, const double* v,
+                       const long* bounds, int nparts, int form, double* o,
+                       double* lse) {
+  double* sblk = (double*)malloc(sizeof(double) * (size_t)N);
+  for (long i = 0; i < N; ++i) {
+    const double* qi = q + i * (long)d;
+    double* oi = o + i * (long)d;
+    double m = -INFINITY, l = 0.0;
+    for (int c = 0; c < d; ++c) oi[c] = 0.0;
+    for (int b = 0; b < nparts; ++b) {
+      long j0 = bounds[b], j1 = bounds[b + 1];
+      double mb = -INFINITY;
+      for (long j = j0; j < j1; ++j) {
+        sblk[j - j0] = oracle_visible(i, j, causal, window)
+                           ? scale * dot(qi, k + j * (long)d, d)
+                           : -INFINITY;
+        if (sblk[j - j0] > mb) mb = sblk[j - j0];
+      }
+      double m_new = (mb > m) ? mb : m;
+      if (m_new == -INFINITY) continue; /* nothing visible yet */
+      double alpha = (m == -INFINITY) ? 0.0 : exp(m - m_new);
+      double lb = 0.0;
+      for (long j = j0; j < j1; ++j)
+        lb += (sblk[j - j0] == -INFINITY) ? 0.0 : exp(sblk[j - j0] - m_new);
+      double l_new = alpha * l + lb;
+      if (form == 1) {
+        double keep = (l_new > 0.0) ? alpha * l / l_new : 0.0;
+        for (int c = 0; c < d; ++c) oi[c] *= keep;
+        for (long j = j0; j < j1; ++j) {
+          if (sblk[j - j0] == -INFINITY) continue;
+          double p = exp(sblk[j - j0] - m_new) / l_new;
+          const double* vj = v + j * (long)d;
+          for (int c = 0; c < d; ++c) oi[c] += p * vj[c];
+        }
+      } else {
+        for (int c = 0; c < d; ++c) oi[c] *= alpha;
+        for (long j = j0; j < j1; ++j) {
+          if (sblk[j - j0] == -INFINITY) continue;
+          double p = exp(sblk[j - j0] - m_new);
+          const double* vj = v + j * (long)d;
+          for (int c = 0; c < d; ++c) oi[c] += p * vj[c];
+        }
+      }
+      m = m_new;
+      l = l_new;
+    }
+    if (form != 1)
+      for (int c = 0; c < d; ++c) oi[c] /= l;
+    if (lse) lse[i] = m + log(l);
+  }
+  free(sblk);
+}
