@@ -1,0 +1,160 @@
+"""Exact attention for AMD Instinct MI355X (gfx950).
+
+Thin Python binding over the C ABI in ``include/attn.h`` (``libattn.so``):
+the functions below only check tensor metadata, allocate outputs with
+PyTorch, and pass raw device pointers and the current HIP stream to the
+library.  Every step of the computation runs in the library's HIP kernels.
+There is no fallback: if ``libattn.so`` is missing, importing the binding
+raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libattn.so")
+
+ATTN_OK, ATTN_EINVAL, ATTN_EUNSUPPORTED, ATTN_EHIP = 0, 1, 2, 3
+ATTN_OUT_BF16, ATTN_OUT_F32 = 0, 1
+
+# Entry points declared in include/attn.h.
+EXPORTS = ("attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_fwd_fp8",
+           "attn_status_str")
+
+
+class AttnDesc(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32),
+                ("N", ctypes.c_int32), ("d", ctypes.c_int32),
+                ("scale", ctypes.c_float), ("causal", ctypes.c_int32),
+                ("window", ctypes.c_int32)]
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {status_str(status)} (status {status})")
+        self.status = status
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is not built; run `python exact_attention_79_amd/build.py` "
+            "(or __graft_entry__.build()) first")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+    dp = ctypes.POINTER(AttnDesc)
+    L.attn_fwd.argtypes = [dp, vp, vp, vp, vp, i32, vp, vp]
+    L.attn_fwd.restype = ctypes.c_int
+    L.attn_bwd_workspace_bytes.argtypes = [dp]
+    L.attn_bwd_workspace_bytes.restype = sz
+    L.attn_bwd.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.attn_bwd.restype = ctypes.c_int
+    L.attn_fwd_fp8.argtypes = [dp, vp, vp, vp, f32, f32, f32, vp, i32, vp, vp]
+    L.attn_fwd_fp8.restype = ctypes.c_int
+    L.attn_status_str.argtypes = [ctypes.c_int]
+    L.attn_status_str.restype = ctypes.c_char_p
+    return L
+
+
+lib = _load()
+
+
+def status_str(status: int) -> str:
+    return lib.attn_status_str(int(status)).decode()
+
+
+def make_desc(B: int, H: int, N: int, d: int, scale: float, causal: bool,
+              window: int) -> AttnDesc:
+    return AttnDesc(int(B), int(H), int(N), int(d), float(scale), int(bool(causal)),
+                    int(window))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _check(status: int, where: str):
+    if status != ATTN_OK:
+        raise AttnError(status, where)
+
+
+def _check_qkv(q, k, v, dtypes):
+    for t in (q, k, v):
+        if not t.is_cuda or t.dtype not in dtypes or not t.is_contiguous():
+            raise ValueError("q, k, v must be contiguous device tensors of dtype "
+                             f"{dtypes}")
+        if t.dim() != 4 or t.shape != q.shape:
+            raise ValueError("q, k, v must all have shape [B, H, N, d]")
+
+
+def attn_fwd(q, k, v, scale: float | None = None, causal: bool = False,
+             window: int = 0, out_dtype=torch.bfloat16, return_lse: bool = True,
+             out=None, lse=None):
+    """O (and the fp32 LSE) for bf16 q, k, v of shape [B, H, N, d]."""
+    _check_qkv(q, k, v, (torch.bfloat16,))
+    B, H, N, d = q.shape
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    if out_dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("out_dtype must be torch.bfloat16 or torch.float32")
+    o = torch.empty_like(q, dtype=out_dtype) if out is None else out
+    if return_lse and lse is None:
+        lse = torch.empty((B, H, N), device=q.device, dtype=torch.float32)
+    desc = make_desc(B, H, N, d, scale, causal, window)
+    od = ATTN_OUT_F32 if out_dtype == torch.float32 else ATTN_OUT_BF16
+    _check(lib.attn_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(o), od,
+                        _ptr(lse), _stream()), "attn_fwd")
+    return (o, lse) if return_lse else o
+
+
+def attn_bwd_workspace_bytes(B: int, H: int, N: int, d: int) -> int:
+    desc = make_desc(B, H, N, d, 1.0, False, 0)
+    return int(lib.attn_bwd_workspace_bytes(ctypes.byref(desc)))
+
+
+def attn_bwd(q, k, v, o, dout, lse, scale: float | None = None,
+             causal: bool = False, window: int = 0, workspace=None, grads=None):
+    """dQ, dK, dV (fp32) for bf16 q, k, v, o, dout and the forward's fp32 lse."""
+    _check_qkv(q, k, v, (torch.bfloat16,))
+    for t in (o, dout):
+        if t.shape != q.shape or t.dtype != torch.bfloat16 or not t.is_contiguous():
+            raise ValueError("o and dout must be contiguous bf16 like q")
+    B, H, N, d = q.shape
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    desc = make_desc(B, H, N, d, scale, causal, window)
+    nbytes = int(lib.attn_bwd_workspace_bytes(ctypes.byref(desc)))
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), device=q.device, dtype=torch.uint8)
+    if grads is None:
+        grads = tuple(torch.empty(q.shape, device=q.device, dtype=torch.float32)
+                      for _ in range(3))
+    dq, dk, dv = grads
+    _check(lib.attn_bwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
+                        _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
+                        _ptr(workspace), workspace.numel(), _stream()), "attn_bwd")
+    return dq, dk, dv
+
+
+def attn_fwd_fp8(q8, k8, v8, q_descale: float, k_descale: float, v_descale: float,
+                 scale: float | None = None, causal: bool = False, window: int = 0,
+                 out_dtype=torch.bfloat16, return_lse: bool = True):
+    """O (and LSE) for e4m3 codes q8, k8, v8 (uint8 or float8_e4m3fn) [B, H, N, d]."""
+    _check_qkv(q8, k8, v8, (torch.uint8, torch.float8_e4m3fn))
+    B, H, N, d = q8.shape
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    o = torch.empty(q8.shape, device=q8.device, dtype=out_dtype)
+    lse = (torch.empty((B, H, N), device=q8.device, dtype=torch.float32)
+           if return_lse else None)
+    desc = make_desc(B, H, N, d, scale, causal, window)
+    od = ATTN_OUT_F32 if out_dtype == torch.float32 else ATTN_OUT_BF16
+    _check(lib.attn_fwd_fp8(ctypes.byref(desc), _ptr(q8), _ptr(k8), _ptr(v8),
+                            float(q_descale), float(k_descale), float(v_descale),
+                            _ptr(o), od, _ptr(lse), _stream()), "attn_fwd_fp8")
+    return (o, lse) if return_lse else o

@@ -1,0 +1,139 @@
+// attn_api.hip -- the extern "C" boundary (include/attn.h): argument checks on
+// the host, then one launch sequence on the caller's stream.  Nothing here
+// allocates device memory or synchronises.
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/attn.h"
+#include "attn_kernels.hpp"
+
+namespace {
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+attn_status check_desc(const attn_desc* d) {
+  if (!d) return ATTN_EINVAL;
+  if (d->B < 1 || d->H < 1 || d->N < 1) return ATTN_EINVAL;
+  if (d->window < 0) return ATTN_EINVAL;
+  if (d->causal != 0 && d->causal != 1) return ATTN_EINVAL;
+  if (!isfinite(d->scale) || !(d->scale > 0.f)) return ATTN_EINVAL;
+  if (d->d != 64 && d->d != 128) return ATTN_EUNSUPPORTED;
+  const int64_t elems = (int64_t)d->B * d->H * d->N * d->d;
+  if (elems >= ((int64_t)1 << 31)) return ATTN_EUNSUPPORTED;
+  return ATTN_OK;
+}
+
+attn_status check_ptrs(std::initializer_list<const void*> required,
+                       std::initializer_list<const void*> optional) {
+  for (const void* p : required)
+    if (!p || !aligned16(p)) return ATTN_EINVAL;
+  for (const void* p : optional)
+    if (p && !aligned16(p)) return ATTN_EINVAL;
+  return ATTN_OK;
+}
+
+attn_status from_hip(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_EHIP; }
+
+attn::FwdArgs fwd_args(const attn_desc* d, const void* q, const void* k,
+                       const void* v, void* o, int32_t o_dtype, float* lse) {
+  attn::FwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.BH = d->B * d->H;
+  a.N = d->N;
+  a.d = d->d;
+  a.scale = d->scale;
+  a.causal = d->causal;
+  a.window = d->window;
+  a.out_f32 = (o_dtype == ATTN_OUT_F32);
+  a.q_descale = a.k_descale = a.v_descale = 1.f;
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+attn_status attn_fwd(const attn_desc* desc, const void* q, const void* k,
+                     const void* v, void* o, int32_t o_dtype, float* lse,
+                     void* stream) {
+  attn_status st = check_desc(desc);
+  if (st != ATTN_OK) return st;
+  if (o_dtype != ATTN_OUT_BF16 && o_dtype != ATTN_OUT_F32) return ATTN_EINVAL;
+  st = check_ptrs({q, k, v, o}, {lse});
+  if (st != ATTN_OK) return st;
+  return from_hip(attn::launch_fwd_bf16(fwd_args(desc, q, k, v, o, o_dtype, lse),
+                                        (hipStream_t)stream));
+}
+
+size_t attn_bwd_workspace_bytes(const attn_desc* desc) {
+  if (check_desc(desc) != ATTN_OK) return 0;
+  const size_t rows = (size_t)desc->B * desc->H * desc->N;
+  return (rows * sizeof(float) + 255) & ~(size_t)255;
+}
+
+attn_status attn_bwd(const attn_desc* desc, const void* q, const void* k,
+                     const void* v, const void* o, const void* dout,
+                     const float* lse, float* dq, float* dk, float* dv,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  attn_status st = check_desc(desc);
+  if (st != ATTN_OK) return st;
+  st = check_ptrs({q, k, v, o, dout, lse, dq, dk, dv, workspace}, {});
+  if (st != ATTN_OK) return st;
+  if (workspace_bytes < attn_bwd_workspace_bytes(desc)) return ATTN_EINVAL;
+  attn::BwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.dout = dout;
+  a.lse = lse;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.delta = (float*)workspace;
+  a.BH = desc->B * desc->H;
+  a.N = desc->N;
+  a.d = desc->d;
+  a.scale = desc->scale;
+  a.causal = desc->causal;
+  a.window = desc->window;
+  return from_hip(attn::launch_bwd(a, (hipStream_t)stream));
+}
+
+attn_status attn_fwd_fp8(const attn_desc* desc, const uint8_t* q8,
+                         const uint8_t* k8, const uint8_t* v8, float q_descale,
+                         float k_descale, float v_descale, void* o,
+                         int32_t o_dtype, float* lse, void* stream) {
+  attn_status st = check_desc(desc);
+  if (st != ATTN_OK) return st;
+  if (o_dtype != ATTN_OUT_BF16 && o_dtype != ATTN_OUT_F32) return ATTN_EINVAL;
+  for (float s : {q_descale, k_descale, v_descale})
+    if (!isfinite(s) || !(s > 0.f)) return ATTN_EINVAL;
+  st = check_ptrs({q8, k8, v8, o}, {lse});
+  if (st != ATTN_OK) return st;
+  attn::FwdArgs a = fwd_args(desc, q8, k8, v8, o, o_dtype, lse);
+  a.q_descale = q_descale;
+  a.k_descale = k_descale;
+  a.v_descale = v_descale;
+  return from_hip(attn::launch_fwd_fp8(a, (hipStream_t)stream));
+}
+
+const char* attn_status_str(attn_status s) {
+  switch (s) {
+    case ATTN_OK:
+      return "ok";
+    case ATTN_EINVAL:
+      return "invalid argument";
+    case ATTN_EUNSUPPORTED:
+      return "unsupported shape (head dim must be 64 or 128; B*H*N*d < 2^31)";
+    case ATTN_EHIP:
+      return "HIP runtime error at launch";
+  }
+  return "unknown status";
+}
+
+}  // extern "C"

@@ -1,0 +1,43 @@
+// attn_kernels.hpp -- host-side launch interface between the C ABI layer and
+// the HIP kernels (internal; not installed).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+struct FwdArgs {
+  const void* q;       // bf16 [BH][N][d], or e4m3 codes for the fp8 kernel
+  const void* k;
+  const void* v;
+  void* o;             // bf16 or fp32 [BH][N][d]
+  float* lse;          // fp32 [BH][N] or nullptr
+  int BH, N, d;
+  float scale;         // softmax scale s
+  int causal, window;
+  int out_f32;         // 1: o is fp32, 0: bf16
+  float q_descale, k_descale, v_descale;  // fp8 only
+};
+
+struct BwdArgs {
+  const void* q;       // bf16 [BH][N][d]
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;    // fp32 [BH][N]
+  float* dq;           // fp32 [BH][N][d]
+  float* dk;
+  float* dv;
+  float* delta;        // fp32 [BH][N] workspace: D_i = sum_k dO_ik O_ik
+  int BH, N, d;
+  float scale;
+  int causal, window;
+};
+
+hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream);
+hipError_t launch_fwd_fp8(const FwdArgs& a, hipStream_t stream);
+hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream);
+
+}  // namespace attn

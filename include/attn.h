@@ -1,0 +1,124 @@
+/*
+ * attn.h -- C ABI of the exact-attention library for AMD Instinct MI355X
+ * (gfx950).  Built as libattn.so; every entry point is extern "C" and takes
+ * plain pointers and sizes.
+ *
+ * What is computed.  For every batch b and head h, with Q, K, V in R^{N x d}:
+ *
+ *   S = scale * Q K^T,  P = softmax(S) row by row,  O = P V,
+ *   L_i = m_i + ln(l_i)  (the log-sum-exp of row i of the masked S),
+ *
+ * the standard-attention definition and the LSE statistic of the FLASH-ATTN
+ * page (taking-lying-flat): "Background" of the FlashAttention summary for S,
+ * P and O, and the FlashAttention-2 section for L = m + log(l) and the causal
+ * mask (S_ij = -inf for j > i).  The N x N matrices S and P are never written
+ * to memory: the forward streams K/V tiles through on-chip memory with the
+ * online-softmax recurrence of that section and stores only O and L; the
+ * backward rebuilds P tile by tile from L (the same page's "Tiling and
+ * Recomputation").
+ *
+ * Masking (key j visible to query i):
+ *   causal == 0, window == 0 : always
+ *   causal == 1              : j <= i
+ *   window == W > 0          : additionally |i - j| < W  (so with causal,
+ *                              i - W < j <= i: the window counts the query's
+ *                              own key).  W >= N with causal equals causal.
+ * Every query sees at least its own key when causal or windowed, so no row of
+ * P is empty.
+ *
+ * Layouts.  Q, K, V, O, dO, dQ, dK, dV are dense [B][H][N][d] row-major (d
+ * fastest, no padding); L and the backward workspace rows are [B][H][N].
+ * bf16 is IEEE binary32 truncated to its upper 16 bits (round-to-nearest-even
+ * when produced here).  fp8 inputs are OCP E4M3 ("fn": bias 7, max 448, no
+ * infinities) with a per-tensor descale: value = code_value * descale.
+ *
+ * Ownership and streams.  Every tensor pointer is a device pointer allocated
+ * by the caller; the library allocates nothing and keeps no state between
+ * calls.  All work is enqueued on `stream` (a hipStream_t; NULL is the
+ * default stream) and the call returns without waiting: faults in the
+ * kernels surface at the caller's next synchronisation.  Outputs must not
+ * alias inputs; outputs are overwritten, never accumulated into.
+ *
+ * Errors.  Arguments are checked on the host before anything is launched:
+ *   ATTN_EINVAL        null required pointer, B/H/N < 1, window < 0, scale not
+ *                      finite or <= 0, causal not 0/1, pointer not 16-byte
+ *                      aligned, output dtype unknown, workspace too small;
+ *   ATTN_EUNSUPPORTED  d not in {64, 128}, or B*H*N*d >= 2^31;
+ *   ATTN_EHIP          the HIP runtime reported an error at launch.
+ * On ATTN_EINVAL / ATTN_EUNSUPPORTED nothing has been enqueued.
+ */
+#ifndef EXACT_ATTN_H
+#define EXACT_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_EINVAL = 1,
+  ATTN_EUNSUPPORTED = 2,
+  ATTN_EHIP = 3
+} attn_status;
+
+typedef enum { ATTN_OUT_BF16 = 0, ATTN_OUT_F32 = 1 } attn_out_dtype;
+
+typedef struct {
+  int32_t B, H, N, d; /* batch, heads, sequence length, head dim (64 or 128) */
+  float scale;        /* s in softmax(s * Q K^T); finite and > 0             */
+  int32_t causal;     /* 0 or 1                                              */
+  int32_t window;     /* 0 = no window; W > 0 as in the masking rule above   */
+} attn_desc;
+
+/* Forward, bf16 inputs (FLASH-ATTN page, FlashAttention-2 section: the
+ * unnormalised accumulator O~ <- diag(e^{m_old - m_new}) O~ + e^{S - m_new} V,
+ * divided by l once at the end).
+ *   q, k, v : bf16 [B,H,N,d]
+ *   o       : [B,H,N,d], bf16 (o_dtype = ATTN_OUT_BF16) or fp32 (ATTN_OUT_F32)
+ *   lse     : fp32 [B,H,N], natural-log LSE of the scaled, masked scores;
+ *             may be NULL when the caller does not need it.               */
+attn_status attn_fwd(const attn_desc* desc, const void* q, const void* k,
+                     const void* v, void* o, int32_t o_dtype, float* lse,
+                     void* stream);
+
+/* Bytes of device workspace attn_bwd needs for `desc` (D = rowsum(dO * O),
+ * fp32 [B,H,N], rounded up to 256 bytes). */
+size_t attn_bwd_workspace_bytes(const attn_desc* desc);
+
+/* Backward (FLASH-ATTN page, FlashAttention-2 summary "Background": dV = P^T dO,
+ * dP = dO V^T, dS = dsoftmax(dP), dQ = dS K, dK = dS^T Q; with the scale s
+ * carried through, dQ = s dS K and dK = s dS^T Q, and dsoftmax written out as
+ * dS_ij = P_ij (dP_ij - D_i), D_i = sum_k dO_ik O_ik).  P is recomputed from
+ * Q, K and the forward's L; it is never read from memory.
+ *   q, k, v, o, dout : bf16 [B,H,N,d]  (o is the forward's bf16 output)
+ *   lse              : fp32 [B,H,N] from attn_fwd with the same desc
+ *   dq, dk, dv       : fp32 [B,H,N,d], overwritten
+ *   workspace        : device memory of at least attn_bwd_workspace_bytes */
+attn_status attn_bwd(const attn_desc* desc, const void* q, const void* k,
+                     const void* v, const void* o, const void* dout,
+                     const float* lse, float* dq, float* dk, float* dv,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* Forward with fp8 inputs (FLASH-ATTN page, FlashAttention-3 summary,
+ * "Low-precision with FP8": both products on the fp8 matrix cores, one scale
+ * per tensor).  q8, k8, v8 are E4M3 codes [B,H,N,d]; the real inputs are
+ * code * descale.  Within each K/V tile the probabilities of every query row
+ * are rescaled so that the row's largest entry maps to 448 before they are
+ * rounded to E4M3 for the P V product; that scale is divided out again in
+ * the fp32 accumulator.  o and lse as in attn_fwd. */
+attn_status attn_fwd_fp8(const attn_desc* desc, const uint8_t* q8,
+                         const uint8_t* k8, const uint8_t* v8, float q_descale,
+                         float k_descale, float v_descale, void* o,
+                         int32_t o_dtype, float* lse, void* stream);
+
+/* Static, human-readable text for a status code. */
+const char* attn_status_str(attn_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EXACT_ATTN_H */

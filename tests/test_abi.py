@@ -1,0 +1,103 @@
+"""Host-side checks of the C ABI: the library loads, exports every entry point
+that include/attn.h declares, and rejects bad arguments before launching
+anything (these paths make no HIP call, so they run without a GPU)."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def ea():
+    import exact_attention_79_amd as ea
+    return ea
+
+
+def test_header_declares_the_boundary():
+    assert declared_functions() == sorted(
+        ["attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_fwd_fp8",
+         "attn_status_str"])
+
+
+def test_library_exports_every_declared_symbol(ea):
+    for name in declared_functions():
+        assert hasattr(ea.lib, name), name
+    assert set(ea.EXPORTS) == set(declared_functions())
+
+
+def test_status_strings(ea):
+    for s in range(4):
+        assert ea.status_str(s)
+    assert ea.status_str(99) == "unknown status"
+
+
+FAKE = 0x10000  # 16-byte aligned, never dereferenced: validation fails first
+
+
+def call_fwd(ea, desc, q=FAKE, k=FAKE, v=FAKE, o=FAKE, od=0, lse=None):
+    vp = ctypes.c_void_p
+    return ea.lib.attn_fwd(ctypes.byref(desc), vp(q), vp(k), vp(v), vp(o), od,
+                           vp(lse) if lse else None, None)
+
+
+@pytest.mark.parametrize("field,value,expect", [
+    ("B", 0, 1), ("H", -1, 1), ("N", 0, 1), ("window", -1, 1), ("causal", 2, 1),
+    ("scale", 0.0, 1), ("scale", -1.0, 1), ("scale", math.inf, 1), ("scale", math.nan, 1),
+    ("d", 32, 2), ("d", 96, 2), ("d", 256, 2),
+])
+def test_fwd_rejects_bad_descriptors(ea, field, value, expect):
+    desc = ea.make_desc(1, 1, 16, 64, 0.125, False, 0)
+    setattr(desc, field, value)
+    assert call_fwd(ea, desc) == expect
+
+
+def test_fwd_rejects_bad_pointers_and_dtype(ea):
+    desc = ea.make_desc(1, 1, 16, 64, 0.125, False, 0)
+    assert call_fwd(ea, desc, q=0) == ea.ATTN_EINVAL
+    assert call_fwd(ea, desc, o=0) == ea.ATTN_EINVAL
+    assert call_fwd(ea, desc, k=FAKE + 8) == ea.ATTN_EINVAL
+    assert call_fwd(ea, desc, lse=FAKE + 4) == ea.ATTN_EINVAL
+    assert call_fwd(ea, desc, od=7) == ea.ATTN_EINVAL
+    big = ea.make_desc(1 << 10, 1 << 10, 1 << 10, 128, 0.1, False, 0)
+    assert call_fwd(ea, big) == ea.ATTN_EUNSUPPORTED
+
+
+def test_bwd_workspace_and_rejections(ea):
+    desc = ea.make_desc(2, 3, 100, 128, 0.1, True, 0)
+    ws = ea.lib.attn_bwd_workspace_bytes(ctypes.byref(desc))
+    assert ws >= 2 * 3 * 100 * 4 and ws % 256 == 0
+    bad = ea.make_desc(2, 3, 100, 80, 0.1, True, 0)
+    assert ea.lib.attn_bwd_workspace_bytes(ctypes.byref(bad)) == 0
+    vp = ctypes.c_void_p
+    args = [vp(FAKE)] * 10
+    assert ea.lib.attn_bwd(ctypes.byref(desc), *args, ws - 1, None) == ea.ATTN_EINVAL
+    args[5] = None  # lse
+    assert ea.lib.attn_bwd(ctypes.byref(desc), *args, ws, None) == ea.ATTN_EINVAL
+    assert ea.lib.attn_bwd(ctypes.byref(bad), *([vp(FAKE)] * 10), ws, None) == \
+        ea.ATTN_EUNSUPPORTED
+
+
+def test_fp8_rejects_bad_descales(ea):
+    desc = ea.make_desc(1, 1, 16, 128, 0.1, False, 0)
+    vp = ctypes.c_void_p
+    for qs, ks, vs in ((0.0, 1.0, 1.0), (1.0, -1.0, 1.0), (1.0, 1.0, math.nan)):
+        assert ea.lib.attn_fwd_fp8(ctypes.byref(desc), vp(FAKE), vp(FAKE), vp(FAKE),
+                                   qs, ks, vs, vp(FAKE), 0, None, None) == ea.ATTN_EINVAL
+
+
+def test_binding_refuses_host_tensors(ea):
+    import torch
+    q = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        ea.attn_fwd(q, q, q)
