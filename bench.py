@@ -1,0 +1,290 @@
+#!/usr/bin/env python3
+"""Throughput of the exact-attention hot path on one MI355X.
+
+One step = every entry point of the library once over one batch of seeded
+synthetic inputs of the B=4, H=16, N=2048 sweep: for d in {64, 128} and for
+non-causal and causal masks, the bf16 forward (attn_fwd) and the three
+backward stages (attn_bwd_preprocess, attn_bwd_dkdv, attn_bwd_dq), plus the
+fp8 forward (attn_fwd_fp8) at d=128 non-causal.  Inputs are resident in HBM
+before timing starts; outputs are preallocated.
+
+value = credited FLOPs per step / step time, with the usual convention:
+forward 4*B*H*N^2*d (halved for causal), backward 2.5x the forward, fp8
+forward 4*B*H*N^2*d.  Each kernel launch is bracketed by HIP events on the
+stream it runs on; the dominant kernel (most GPU time per step) is reported
+against its roofline.  The fp64 CPU oracle is timed on a bounded sample of
+the same workload as a reference point (rank 0 only).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+METRIC = "attention fwd/bwd TFLOPS (bf16, causal & non-causal) and % of MFMA peak"
+# MI355X dense peaks: 256 CUs x 2.4 GHz x (4096 bf16 | 8192 fp8) flop/clk/CU.
+PEAK_BF16_TFLOPS = 2516.6
+PEAK_FP8_TFLOPS = 5033.2
+HBM_GBPS = 8000.0
+# The fp8 forward joins the step once its kernel is built into the library.
+INCLUDE_FP8 = False
+
+
+def visible_pairs(N: int, causal: bool, window: int) -> int:
+    """Number of (query, key) pairs that survive the mask, per head."""
+    if window <= 0 or window >= N:
+        return N * (N + 1) // 2 if causal else N * N
+    W = window
+    if causal:
+        return W * (W + 1) // 2 + (N - W) * W
+    # |i - j| < W
+    return N * (2 * W - 1) - W * (W - 1)
+
+
+def credited_fwd_flops(BH: int, N: int, d: int, causal: bool, window: int) -> float:
+    """4*BH*N^2*d, halved for causal; exact visible pairs for a window."""
+    if window > 0 and window < N:
+        return 4.0 * d * BH * visible_pairs(N, causal, window)
+    return 4.0 * BH * N * N * d * (0.5 if causal else 1.0)
+
+
+def parse_args():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+class Launch:
+    """One kernel launch per step: its name, credited FLOPs, executed FLOPs
+    and bound, plus the events around it."""
+
+    def __init__(self, name, kernel, fn, credited, executed, peak):
+        self.name, self.kernel, self.fn = name, kernel, fn
+        self.credited, self.executed, self.peak = credited, executed, peak
+        self.times_ms = []
+
+
+def build_step(ea, torch, attn_synth):
+    """All launches of one step, with inputs resident on the device."""
+    B, H, N = 4, 16, 2048
+    BH = B * H
+    launches = []
+
+    def dev_bf16(bits):
+        import numpy as np
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(
+            torch.bfloat16).cuda()
+
+    for d in (64, 128):
+        bits = attn_synth.bf16_attention_inputs(2, B, H, N, d, with_dout=True)
+        q, k, v, do = (dev_bf16(bits[n]) for n in ("q", "k", "v", "do"))
+        for causal in (False, True):
+            tag = f"d{d} {'causal' if causal else 'non-causal'}"
+            t = dict(q=q, k=k, v=v, do=do, causal=causal,
+                     o=torch.empty_like(q),
+                     lse=torch.empty((B, H, N), device="cuda", dtype=torch.float32),
+                     dq=torch.empty(q.shape, device="cuda", dtype=torch.float32),
+                     dk=torch.empty(q.shape, device="cuda", dtype=torch.float32),
+                     dv=torch.empty(q.shape, device="cuda", dtype=torch.float32),
+                     ws=torch.empty(ea.attn_bwd_workspace_bytes(B, H, N, d),
+                                    device="cuda", dtype=torch.uint8))
+            # Every launch reads only the tensors bound in its own dict `t`; the
+            # binding derives the descriptor from their shapes.
+            def fwd(t=t):
+                ea.attn_fwd(t["q"], t["k"], t["v"], causal=t["causal"], out=t["o"],
+                            lse=t["lse"])
+
+            def pre(t=t):
+                ea.attn_bwd_preprocess(t["o"], t["do"], t["ws"], causal=t["causal"])
+
+            def dkdv(t=t):
+                ea.attn_bwd_dkdv(t["q"], t["k"], t["v"], t["do"], t["lse"], t["ws"],
+                                 t["dk"], t["dv"], causal=t["causal"])
+
+            def dq(t=t):
+                ea.attn_bwd_dq(t["q"], t["k"], t["v"], t["do"], t["lse"], t["ws"],
+                               t["dq"], causal=t["causal"])
+
+            fwd()  # O and L for the backward launches
+            f = credited_fwd_flops(BH, N, d, causal, 0)
+            # Backward credit (2.5x fwd) is split over the five products:
+            # dK/dV kernel S, dP, dV, dK (4/5 of it), dQ kernel dQ (1/5); the
+            # dQ kernel also recomputes S and dP (executed, not credited).
+            bwd = 2.5 * f
+            launches.append(Launch(f"attn_fwd {tag}", f"fwd_bf16_kernel<d{d}>", fwd,
+                                   f, f, PEAK_BF16_TFLOPS))
+            launches.append(Launch(f"attn_bwd_preprocess {tag}",
+                                   f"bwd_delta_kernel<d{d}>", pre, 0.0, 0.0, None))
+            launches[-1].bytes = BH * N * (2 * d * 2 + 4)
+            launches.append(Launch(f"attn_bwd_dkdv {tag}", f"bwd_dkdv_kernel<d{d}>", dkdv,
+                                   0.8 * bwd, 0.8 * bwd, PEAK_BF16_TFLOPS))
+            launches.append(Launch(f"attn_bwd_dq {tag}", f"bwd_dq_kernel<d{d}>", dq,
+                                   0.2 * bwd, 0.6 * bwd, PEAK_BF16_TFLOPS))
+    if INCLUDE_FP8:
+        d = 128
+        f8 = attn_synth.fp8_attention_inputs(5, B, H, N, d)
+        q8, k8, v8 = (torch.from_numpy(f8[n]).cuda() for n in ("q", "k", "v"))
+        o8 = torch.empty((B, H, N, d), device="cuda", dtype=torch.bfloat16)
+        l8 = torch.empty((B, H, N), device="cuda", dtype=torch.float32)
+        f = credited_fwd_flops(BH, N, d, False, 0)
+        launches.append(Launch(
+            "attn_fwd_fp8 d128 non-causal", "fwd_fp8_kernel<d128>",
+            (lambda: ea.attn_fwd_fp8(q8, k8, v8, f8["q_descale"], f8["k_descale"],
+                                     f8["v_descale"], out=o8, lse=l8)),
+            f, f, PEAK_FP8_TFLOPS))
+    return launches
+
+
+def run_step(launches, torch, record):
+    evs = []
+    for L in launches:
+        if record:
+            e = torch.cuda.Event(enable_timing=True)
+            e.record()
+            evs.append(e)
+        L.fn()
+    if record:
+        e = torch.cuda.Event(enable_timing=True)
+        e.record()
+        evs.append(e)
+    return evs
+
+
+def cpu_baseline(attn_synth, seconds_budget=16.0):
+    """The fp64 oracle, as it stands, on a bounded sample of the same workload:
+    for each of the four variants, forward + backward of heads (0,0), (0,1), ...
+    until that variant's share of the budget is spent."""
+    import oracle
+    B, H, N = 4, 16, 2048
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or os.cpu_count()
+    per_variant = seconds_budget / 4
+    done_flops, t_total, parts = 0.0, 0.0, []
+    for d in (64, 128):
+        bits = attn_synth.bf16_attention_inputs(2, B, H, N, d, with_dout=True)
+        s = 1.0 / math.sqrt(d)
+        for causal in (False, True):
+            t_var, heads = 0.0, 0
+            while t_var < per_variant and heads < B * H:
+                b, h = divmod(heads, H)
+                ref = {k: oracle.decode_bf16(v[b, h]) for k, v in bits.items()}
+                t0 = time.perf_counter()
+                oracle.fwd(ref["q"], ref["k"], ref["v"], s, causal, 0, nthreads=threads)
+                oracle.bwd(ref["q"], ref["k"], ref["v"], ref["do"], s, causal, 0,
+                           nthreads=threads)
+                t_var += time.perf_counter() - t0
+                heads += 1
+                done_flops += 3.5 * credited_fwd_flops(1, N, d, causal, 0)
+            t_total += t_var
+            parts.append(f"d{d} {'causal' if causal else 'non-causal'}: {heads} heads")
+    return {
+        "value": done_flops / t_total / 1e12,
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": (f"fp64 oracle forward + backward on the first heads of the B4 H16 "
+                   f"N2048 workload ({'; '.join(parts)}), {t_total:.1f} s; credited "
+                   f"FLOPs as for the GPU"),
+    }
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the "
+              "kernels are independent per (batch, head), so more GPUs would each "
+              "run this same single-GPU workload.", file=sys.stderr)
+        return 2
+    import torch
+    import attn_synth
+    import exact_attention_79_amd as ea
+
+    launches = build_step(ea, torch, attn_synth)
+    for _ in range(args.warmup):
+        run_step(launches, torch, record=False)
+    torch.cuda.synchronize()
+
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    all_evs = []
+    start.record()
+    for _ in range(args.steps):
+        all_evs.append(run_step(launches, torch, record=True))
+    end.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    for evs in all_evs:
+        for i, L in enumerate(launches):
+            L.times_ms.append(evs[i].elapsed_time(evs[i + 1]))
+
+    ms_per_step = total_ms / args.steps
+    credited = sum(L.credited for L in launches)
+    value = credited / (ms_per_step * 1e-3) / 1e12
+
+    breakdown = []
+    for L in launches:
+        t = sum(L.times_ms) / len(L.times_ms)
+        row = {"launch": L.name, "kernel": L.kernel, "ms": round(t, 4)}
+        if L.peak:
+            tf = L.credited / (t * 1e-3) / 1e12
+            row.update({"tflops": round(tf, 1), "pct_peak": round(100 * tf / L.peak, 1)})
+            if L.executed != L.credited:
+                row["executed_tflops"] = round(L.executed / (t * 1e-3) / 1e12, 1)
+        else:
+            row["gbps"] = round(L.bytes / (t * 1e-3) / 1e9, 1)
+        breakdown.append(row)
+
+    # Dominant kernel: the kernel symbol with the most GPU time per step.
+    per_kernel = {}
+    for L in launches:
+        k = per_kernel.setdefault(L.kernel, {"ms": 0.0, "n": 0, "credited": 0.0,
+                                             "peak": L.peak})
+        k["ms"] += sum(L.times_ms) / len(L.times_ms)
+        k["n"] += 1
+        k["credited"] += L.credited
+    dom_name, dom = max(per_kernel.items(), key=lambda kv: kv[1]["ms"])
+    avg_ms = dom["ms"] / dom["n"]
+    achieved = (dom["credited"] / dom["n"]) / (avg_ms * 1e-3) / 1e12
+    roofline = {"kernel": dom_name, "bound": "mfma", "achieved": round(achieved, 1),
+                "peak": dom["peak"], "unit": "TFLOP/s",
+                "frac": round(achieved / dom["peak"], 4), "traffic": None,
+                "avg_launch_ms": round(avg_ms, 4)}
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": ("B4 H16 N2048 sweep: d in {64,128} x {non-causal, causal}, "
+                         "bf16 forward + backward; fp8 (e4m3) forward at d128 "
+                         "non-causal" + ("" if INCLUDE_FP8 else " (not yet built)")),
+            "global_batch": 4, "heads": 16, "seq_len": 2048, "head_dims": [64, 128],
+            "parallelism": "none (1 GPU)",
+        },
+        "roofline": roofline,
+        "breakdown": breakdown,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(attn_synth)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -22,8 +22,8 @@ ATTN_OK, ATTN_EINVAL, ATTN_EUNSUPPORTED, ATTN_EHIP = 0, 1, 2, 3
 ATTN_OUT_BF16, ATTN_OUT_F32 = 0, 1
 
 # Entry points declared in include/attn.h.
-EXPORTS = ("attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_fwd_fp8",
-           "attn_status_str")
+EXPORTS = ("attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_bwd_preprocess",
+           "attn_bwd_dkdv", "attn_bwd_dq", "attn_fwd_fp8", "attn_status_str")
 
 
 class AttnDesc(ctypes.Structure):
@@ -53,6 +53,12 @@ def _load():
     L.attn_bwd_workspace_bytes.restype = sz
     L.attn_bwd.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.attn_bwd.restype = ctypes.c_int
+    L.attn_bwd_preprocess.argtypes = [dp, vp, vp, vp, sz, vp]
+    L.attn_bwd_preprocess.restype = ctypes.c_int
+    L.attn_bwd_dkdv.argtypes = [dp, vp, vp, vp, vp, vp, vp, sz, vp, vp, vp]
+    L.attn_bwd_dkdv.restype = ctypes.c_int
+    L.attn_bwd_dq.argtypes = [dp, vp, vp, vp, vp, vp, vp, sz, vp, vp]
+    L.attn_bwd_dq.restype = ctypes.c_int
     L.attn_fwd_fp8.argtypes = [dp, vp, vp, vp, f32, f32, f32, vp, i32, vp, vp]
     L.attn_fwd_fp8.restype = ctypes.c_int
     L.attn_status_str.argtypes = [ctypes.c_int]
@@ -105,8 +111,12 @@ def attn_fwd(q, k, v, scale: float | None = None, causal: bool = False,
     if out_dtype not in (torch.bfloat16, torch.float32):
         raise ValueError("out_dtype must be torch.bfloat16 or torch.float32")
     o = torch.empty_like(q, dtype=out_dtype) if out is None else out
+    _check_like(q, out_dtype, out=o)
     if return_lse and lse is None:
         lse = torch.empty((B, H, N), device=q.device, dtype=torch.float32)
+    if lse is not None and (not lse.is_cuda or lse.dtype != torch.float32
+                            or lse.shape != (B, H, N) or not lse.is_contiguous()):
+        raise ValueError("lse must be a contiguous fp32 device tensor [B, H, N]")
     desc = make_desc(B, H, N, d, scale, causal, window)
     od = ATTN_OUT_F32 if out_dtype == torch.float32 else ATTN_OUT_BF16
     _check(lib.attn_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(o), od,
@@ -123,12 +133,8 @@ def attn_bwd(q, k, v, o, dout, lse, scale: float | None = None,
              causal: bool = False, window: int = 0, workspace=None, grads=None):
     """dQ, dK, dV (fp32) for bf16 q, k, v, o, dout and the forward's fp32 lse."""
     _check_qkv(q, k, v, (torch.bfloat16,))
-    for t in (o, dout):
-        if t.shape != q.shape or t.dtype != torch.bfloat16 or not t.is_contiguous():
-            raise ValueError("o and dout must be contiguous bf16 like q")
-    B, H, N, d = q.shape
-    scale = 1.0 / math.sqrt(d) if scale is None else scale
-    desc = make_desc(B, H, N, d, scale, causal, window)
+    _check_like(q, torch.bfloat16, o=o, dout=dout)
+    desc = _bwd_desc(q, scale, causal, window)
     nbytes = int(lib.attn_bwd_workspace_bytes(ctypes.byref(desc)))
     if workspace is None:
         workspace = torch.empty(max(nbytes, 1), device=q.device, dtype=torch.uint8)
@@ -136,9 +142,92 @@ def attn_bwd(q, k, v, o, dout, lse, scale: float | None = None,
         grads = tuple(torch.empty(q.shape, device=q.device, dtype=torch.float32)
                       for _ in range(3))
     dq, dk, dv = grads
+    _check_like(q, torch.float32, dq=dq, dk=dk, dv=dv)
+    _check_lse_ws(q, lse, workspace, desc)
     _check(lib.attn_bwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
                         _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
-                        _ptr(workspace), workspace.numel(), _stream()), "attn_bwd")
+                        _ptr(workspace), workspace.numel() * workspace.element_size(),
+                        _stream()), "attn_bwd")
+    return dq, dk, dv
+
+
+def _bwd_desc(q, scale, causal, window):
+    B, H, N, d = q.shape
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    return make_desc(B, H, N, d, scale, causal, window)
+
+
+def _check_like(ref, dtype, **tensors):
+    for name, t in tensors.items():
+        if (not t.is_cuda or t.shape != ref.shape or t.dtype != dtype
+                or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous {dtype} device tensor "
+                             f"of shape {tuple(ref.shape)}")
+
+
+def _check_lse_ws(q, lse, workspace, desc):
+    B, H, N, _ = q.shape
+    if (lse is not None and (not lse.is_cuda or lse.dtype != torch.float32
+                             or lse.shape != (B, H, N) or not lse.is_contiguous())):
+        raise ValueError("lse must be a contiguous fp32 device tensor [B, H, N]")
+    need = int(lib.attn_bwd_workspace_bytes(ctypes.byref(desc)))
+    if workspace.numel() * workspace.element_size() < need or not workspace.is_cuda:
+        raise ValueError(f"workspace must be a device tensor of >= {need} bytes")
+
+
+def attn_bwd_preprocess(o, dout, workspace, scale=None, causal=False, window=0):
+    """Stage 1 of the backward: workspace <- D = rowsum(dO * O)."""
+    _check_like(o, torch.bfloat16, o=o, dout=dout)
+    desc = _bwd_desc(o, scale, causal, window)
+    _check_lse_ws(o, None, workspace, desc)
+    _check(lib.attn_bwd_preprocess(ctypes.byref(desc), _ptr(o), _ptr(dout),
+                                   _ptr(workspace),
+                                   workspace.numel() * workspace.element_size(),
+                                   _stream()), "attn_bwd_preprocess")
+
+
+def attn_bwd_dkdv(q, k, v, dout, lse, workspace, dk, dv, scale=None, causal=False,
+                  window=0):
+    """Stage 2 of the backward: dK and dV (fp32), using D from stage 1."""
+    _check_like(q, torch.bfloat16, q=q, k=k, v=v, dout=dout)
+    _check_like(q, torch.float32, dk=dk, dv=dv)
+    desc = _bwd_desc(q, scale, causal, window)
+    _check_lse_ws(q, lse, workspace, desc)
+    _check(lib.attn_bwd_dkdv(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(dout),
+                             _ptr(lse), _ptr(workspace),
+                             workspace.numel() * workspace.element_size(), _ptr(dk),
+                             _ptr(dv), _stream()), "attn_bwd_dkdv")
+
+
+def attn_bwd_dq(q, k, v, dout, lse, workspace, dq, scale=None, causal=False,
+                window=0):
+    """Stage 3 of the backward: dQ (fp32), using D from stage 1."""
+    _check_like(q, torch.bfloat16, q=q, k=k, v=v, dout=dout)
+    _check_like(q, torch.float32, dq=dq)
+    desc = _bwd_desc(q, scale, causal, window)
+    _check_lse_ws(q, lse, workspace, desc)
+    _check(lib.attn_bwd_dq(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(dout),
+                           _ptr(lse), _ptr(workspace),
+                           workspace.numel() * workspace.element_size(), _ptr(dq),
+                           _stream()), "attn_bwd_dq")
+
+
+def attn_bwd_stages(q, k, v, o, dout, lse, scale: float | None = None,
+                    causal: bool = False, window: int = 0, workspace=None,
+                    grads=None):
+    """The same result as attn_bwd, issued as its three stages."""
+    desc = _bwd_desc(q, scale, causal, window)
+    if workspace is None:
+        nbytes = int(lib.attn_bwd_workspace_bytes(ctypes.byref(desc)))
+        workspace = torch.empty(max(nbytes, 1), device=q.device, dtype=torch.uint8)
+    if grads is None:
+        grads = tuple(torch.empty(q.shape, device=q.device, dtype=torch.float32)
+                      for _ in range(3))
+    dq, dk, dv = grads
+    kw = dict(scale=scale, causal=causal, window=window)
+    attn_bwd_preprocess(o, dout, workspace, **kw)
+    attn_bwd_dkdv(q, k, v, dout, lse, workspace, dk, dv, **kw)
+    attn_bwd_dq(q, k, v, dout, lse, workspace, dq, **kw)
     return dq, dk, dv
 
 

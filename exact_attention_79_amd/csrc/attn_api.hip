@@ -53,6 +53,30 @@ attn::FwdArgs fwd_args(const attn_desc* d, const void* q, const void* k,
   return a;
 }
 
+attn::BwdArgs bwd_args(const attn_desc* d, const void* q, const void* k,
+                      const void* v, const void* o, const void* dout,
+                      const float* lse, float* dq, float* dk, float* dv,
+                      void* workspace) {
+  attn::BwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.dout = dout;
+  a.lse = lse;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.delta = (float*)workspace;
+  a.BH = d->B * d->H;
+  a.N = d->N;
+  a.d = d->d;
+  a.scale = d->scale;
+  a.causal = d->causal;
+  a.window = d->window;
+  return a;
+}
+
 }  // namespace
 
 extern "C" {
@@ -84,24 +108,53 @@ attn_status attn_bwd(const attn_desc* desc, const void* q, const void* k,
   st = check_ptrs({q, k, v, o, dout, lse, dq, dk, dv, workspace}, {});
   if (st != ATTN_OK) return st;
   if (workspace_bytes < attn_bwd_workspace_bytes(desc)) return ATTN_EINVAL;
-  attn::BwdArgs a;
-  a.q = q;
-  a.k = k;
-  a.v = v;
-  a.o = o;
-  a.dout = dout;
-  a.lse = lse;
-  a.dq = dq;
-  a.dk = dk;
-  a.dv = dv;
-  a.delta = (float*)workspace;
-  a.BH = desc->B * desc->H;
-  a.N = desc->N;
-  a.d = desc->d;
-  a.scale = desc->scale;
-  a.causal = desc->causal;
-  a.window = desc->window;
-  return from_hip(attn::launch_bwd(a, (hipStream_t)stream));
+  return from_hip(attn::launch_bwd(
+      bwd_args(desc, q, k, v, o, dout, lse, dq, dk, dv, workspace),
+      (hipStream_t)stream));
+}
+
+attn_status attn_bwd_preprocess(const attn_desc* desc, const void* o,
+                                const void* dout, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  attn_status st = check_desc(desc);
+  if (st != ATTN_OK) return st;
+  st = check_ptrs({o, dout, workspace}, {});
+  if (st != ATTN_OK) return st;
+  if (workspace_bytes < attn_bwd_workspace_bytes(desc)) return ATTN_EINVAL;
+  return from_hip(attn::launch_bwd_preprocess(
+      bwd_args(desc, nullptr, nullptr, nullptr, o, dout, nullptr, nullptr, nullptr,
+               nullptr, workspace),
+      (hipStream_t)stream));
+}
+
+attn_status attn_bwd_dkdv(const attn_desc* desc, const void* q, const void* k,
+                          const void* v, const void* dout, const float* lse,
+                          const void* workspace, size_t workspace_bytes,
+                          float* dk, float* dv, void* stream) {
+  attn_status st = check_desc(desc);
+  if (st != ATTN_OK) return st;
+  st = check_ptrs({q, k, v, dout, lse, workspace, dk, dv}, {});
+  if (st != ATTN_OK) return st;
+  if (workspace_bytes < attn_bwd_workspace_bytes(desc)) return ATTN_EINVAL;
+  return from_hip(attn::launch_bwd_dkdv(
+      bwd_args(desc, q, k, v, nullptr, dout, lse, nullptr, dk, dv,
+               (void*)workspace),
+      (hipStream_t)stream));
+}
+
+attn_status attn_bwd_dq(const attn_desc* desc, const void* q, const void* k,
+                        const void* v, const void* dout, const float* lse,
+                        const void* workspace, size_t workspace_bytes, float* dq,
+                        void* stream) {
+  attn_status st = check_desc(desc);
+  if (st != ATTN_OK) return st;
+  st = check_ptrs({q, k, v, dout, lse, workspace, dq}, {});
+  if (st != ATTN_OK) return st;
+  if (workspace_bytes < attn_bwd_workspace_bytes(desc)) return ATTN_EINVAL;
+  return from_hip(attn::launch_bwd_dq(
+      bwd_args(desc, q, k, v, nullptr, dout, lse, dq, nullptr, nullptr,
+               (void*)workspace),
+      (hipStream_t)stream));
 }
 
 attn_status attn_fwd_fp8(const attn_desc* desc, const uint8_t* q8,

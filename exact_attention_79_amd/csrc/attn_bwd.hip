@@ -380,14 +380,7 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(BwdKParams p) {
   }
 }
 
-template <int D>
-static hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t stream) {
-  constexpr int NW = 4;
-  const int rows = a.BH * a.N;
-  constexpr int RPB = 256 / (D / 8);
-  hipLaunchKernelGGL((bwd_delta_kernel<D>), dim3((rows + RPB - 1) / RPB), dim3(256),
-                     0, stream, (const __bf16*)a.o, (const __bf16*)a.dout, a.delta,
-                     rows);
+static BwdKParams bwd_params(const BwdArgs& a, int tile_rows) {
   BwdKParams p;
   p.q = (const __bf16*)a.q;
   p.k = (const __bf16*)a.k;
@@ -402,18 +395,58 @@ static hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t stream) {
   p.scale = a.scale;
   p.causal = a.causal;
   p.window = a.window;
-  p.n_tiles = (a.N + 32 * NW - 1) / (32 * NW);
-  const unsigned grid = (unsigned)(a.BH * p.n_tiles);
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, NW, 64>), dim3(grid), dim3(NW * 64), 0,
-                     stream, p);
-  hipLaunchKernelGGL((bwd_dq_kernel<D, NW, 64>), dim3(grid), dim3(NW * 64), 0,
-                     stream, p);
+  p.n_tiles = (a.N + tile_rows - 1) / tile_rows;
+  return p;
+}
+
+constexpr int kBwdWaves = 4;
+constexpr int kBwdTile = 64;  // query rows (dK/dV kernel) or keys (dQ kernel) per step
+
+hipError_t launch_bwd_preprocess(const BwdArgs& a, hipStream_t stream) {
+  const int rows = a.BH * a.N;
+  if (a.d == 128) {
+    constexpr int RPB = 256 / 16;
+    hipLaunchKernelGGL((bwd_delta_kernel<128>), dim3((rows + RPB - 1) / RPB),
+                       dim3(256), 0, stream, (const __bf16*)a.o,
+                       (const __bf16*)a.dout, a.delta, rows);
+  } else {
+    constexpr int RPB = 256 / 8;
+    hipLaunchKernelGGL((bwd_delta_kernel<64>), dim3((rows + RPB - 1) / RPB),
+                       dim3(256), 0, stream, (const __bf16*)a.o,
+                       (const __bf16*)a.dout, a.delta, rows);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream) {
+  const BwdKParams p = bwd_params(a, 32 * kBwdWaves);
+  const dim3 grid((unsigned)(a.BH * p.n_tiles)), block(64 * kBwdWaves);
+  if (a.d == 128)
+    hipLaunchKernelGGL((bwd_dkdv_kernel<128, kBwdWaves, kBwdTile>), grid, block, 0,
+                       stream, p);
+  else
+    hipLaunchKernelGGL((bwd_dkdv_kernel<64, kBwdWaves, kBwdTile>), grid, block, 0,
+                       stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream) {
+  const BwdKParams p = bwd_params(a, 32 * kBwdWaves);
+  const dim3 grid((unsigned)(a.BH * p.n_tiles)), block(64 * kBwdWaves);
+  if (a.d == 128)
+    hipLaunchKernelGGL((bwd_dq_kernel<128, kBwdWaves, kBwdTile>), grid, block, 0,
+                       stream, p);
+  else
+    hipLaunchKernelGGL((bwd_dq_kernel<64, kBwdWaves, kBwdTile>), grid, block, 0,
+                       stream, p);
   return hipGetLastError();
 }
 
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
-  if (a.d == 128) return launch_bwd_d<128>(a, stream);
-  return launch_bwd_d<64>(a, stream);
+  hipError_t e = launch_bwd_preprocess(a, stream);
+  if (e == hipSuccess) e = launch_bwd_dkdv(a, stream);
+  if (e == hipSuccess) e = launch_bwd_dq(a, stream);
+  return e;
 }
 
 }  // namespace attn

@@ -38,6 +38,10 @@ struct BwdArgs {
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_fwd_fp8(const FwdArgs& a, hipStream_t stream);
+// The three backward stages; launch_bwd = preprocess, dkdv, dq in order.
+hipError_t launch_bwd_preprocess(const BwdArgs& a, hipStream_t stream);
+hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream);
+hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream);
 
 }  // namespace attn

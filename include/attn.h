@@ -102,6 +102,28 @@ attn_status attn_bwd(const attn_desc* desc, const void* q, const void* k,
                      const float* lse, float* dq, float* dk, float* dv,
                      void* workspace, size_t workspace_bytes, void* stream);
 
+/* The backward as three separately launchable stages.  attn_bwd enqueues
+ * exactly these three, in this order, on one stream; a caller may issue them
+ * itself (for example to time or overlap them).  Argument rules as attn_bwd.
+ *   attn_bwd_preprocess: workspace <- D_i = sum_k dO_ik O_ik   (fp32 [B,H,N])
+ *   attn_bwd_dkdv:       dK = s dS^T Q and dV = P^T dO, one pass per K/V block
+ *                        over the query blocks that see it (the FLASH-ATTN
+ *                        page's column-block partition of the backward)
+ *   attn_bwd_dq:         dQ = s dS K, one pass per query block over the K/V
+ *                        blocks it sees (S and dP are recomputed there)
+ * dkdv and dq read D from the workspace written by the preprocess. */
+attn_status attn_bwd_preprocess(const attn_desc* desc, const void* o,
+                                const void* dout, void* workspace,
+                                size_t workspace_bytes, void* stream);
+attn_status attn_bwd_dkdv(const attn_desc* desc, const void* q, const void* k,
+                          const void* v, const void* dout, const float* lse,
+                          const void* workspace, size_t workspace_bytes,
+                          float* dk, float* dv, void* stream);
+attn_status attn_bwd_dq(const attn_desc* desc, const void* q, const void* k,
+                        const void* v, const void* dout, const float* lse,
+                        const void* workspace, size_t workspace_bytes, float* dq,
+                        void* stream);
+
 /* Forward with fp8 inputs (FLASH-ATTN page, FlashAttention-3 summary,
  * "Low-precision with FP8": both products on the fp8 matrix cores, one scale
  * per tensor).  q8, k8, v8 are E4M3 codes [B,H,N,d]; the real inputs are

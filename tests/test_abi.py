@@ -26,8 +26,8 @@ def ea():
 
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted(
-        ["attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_fwd_fp8",
-         "attn_status_str"])
+        ["attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_bwd_preprocess",
+         "attn_bwd_dkdv", "attn_bwd_dq", "attn_fwd_fp8", "attn_status_str"])
 
 
 def test_library_exports_every_declared_symbol(ea):
@@ -86,6 +86,20 @@ def test_bwd_workspace_and_rejections(ea):
     assert ea.lib.attn_bwd(ctypes.byref(desc), *args, ws, None) == ea.ATTN_EINVAL
     assert ea.lib.attn_bwd(ctypes.byref(bad), *([vp(FAKE)] * 10), ws, None) == \
         ea.ATTN_EUNSUPPORTED
+
+
+def test_bwd_stages_reject_bad_arguments(ea):
+    desc = ea.make_desc(1, 2, 64, 64, 0.1, False, 0)
+    ws = ea.lib.attn_bwd_workspace_bytes(ctypes.byref(desc))
+    vp = ctypes.c_void_p
+    f = vp(FAKE)
+    assert ea.lib.attn_bwd_preprocess(ctypes.byref(desc), f, None, f, ws, None) == 1
+    assert ea.lib.attn_bwd_preprocess(ctypes.byref(desc), f, f, f, ws - 1, None) == 1
+    assert ea.lib.attn_bwd_dkdv(ctypes.byref(desc), f, f, f, f, f, f, ws, f, vp(FAKE + 4),
+                                None) == 1
+    assert ea.lib.attn_bwd_dq(ctypes.byref(desc), f, f, None, f, f, f, ws, f, None) == 1
+    bad = ea.make_desc(1, 2, 64, 64, -0.1, False, 0)
+    assert ea.lib.attn_bwd_dq(ctypes.byref(bad), f, f, f, f, f, f, ws, f, None) == 1
 
 
 def test_fp8_rejects_bad_descales(ea):
