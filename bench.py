@@ -32,7 +32,7 @@ PEAK_BF16_TFLOPS = 2516.6
 PEAK_FP8_TFLOPS = 5033.2
 HBM_GBPS = 8000.0
 # The fp8 forward joins the step once its kernel is built into the library.
-INCLUDE_FP8 = False
+INCLUDE_FP8 = True
 
 
 def visible_pairs(N: int, causal: bool, window: int) -> int:

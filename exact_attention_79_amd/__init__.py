@@ -233,14 +233,21 @@ def attn_bwd_stages(q, k, v, o, dout, lse, scale: float | None = None,
 
 def attn_fwd_fp8(q8, k8, v8, q_descale: float, k_descale: float, v_descale: float,
                  scale: float | None = None, causal: bool = False, window: int = 0,
-                 out_dtype=torch.bfloat16, return_lse: bool = True):
-    """O (and LSE) for e4m3 codes q8, k8, v8 (uint8 or float8_e4m3fn) [B, H, N, d]."""
+                 out_dtype=torch.bfloat16, return_lse: bool = True, out=None, lse=None):
+    """O (and LSE) for e4m3 codes q8, k8, v8 (uint8 or float8_e4m3fn) [B, H, N, d];
+    the inputs are code * descale."""
     _check_qkv(q8, k8, v8, (torch.uint8, torch.float8_e4m3fn))
     B, H, N, d = q8.shape
     scale = 1.0 / math.sqrt(d) if scale is None else scale
-    o = torch.empty(q8.shape, device=q8.device, dtype=out_dtype)
-    lse = (torch.empty((B, H, N), device=q8.device, dtype=torch.float32)
-           if return_lse else None)
+    if out_dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("out_dtype must be torch.bfloat16 or torch.float32")
+    o = torch.empty(q8.shape, device=q8.device, dtype=out_dtype) if out is None else out
+    _check_like(q8, out_dtype, out=o)
+    if return_lse and lse is None:
+        lse = torch.empty((B, H, N), device=q8.device, dtype=torch.float32)
+    if lse is not None and (not lse.is_cuda or lse.dtype != torch.float32
+                            or lse.shape != (B, H, N) or not lse.is_contiguous()):
+        raise ValueError("lse must be a contiguous fp32 device tensor [B, H, N]")
     desc = make_desc(B, H, N, d, scale, causal, window)
     od = ATTN_OUT_F32 if out_dtype == torch.float32 else ATTN_OUT_BF16
     _check(lib.attn_fwd_fp8(ctypes.byref(desc), _ptr(q8), _ptr(k8), _ptr(v8),

@@ -1,5 +1,348 @@
-// attn_fwd_fp8.hip -- fp8 forward kernel (not yet implemented).
+// attn_fwd_fp8.hip -- fp8 (OCP e4m3) forward kernel for gfx950.
+//
+// Method: the same tiled online-softmax forward as attn_fwd.hip (FLASH-ATTN
+// page, FlashAttention-2 section), with both products on the fp8 matrix
+// cores as in the "Low-precision with FP8" part of the page's
+// FlashAttention-3 summary: Q, K, V arrive as e4m3 codes with one descale
+// per tensor; the score scale becomes s * dq * dk, and dv multiplies the
+// output once in the epilogue.
+//
+// Probabilities are requantised to e4m3 for the P V product with a scale per
+// (query row, 64-key block): the row's largest probability in the block sets
+// a power-of-two scale 2^e that brings it into [128, 256), so every entry
+// keeps the full 3-bit mantissa of e4m3's normal range.  One e4m3 term
+// leaves a relative weight error of up to 2^-4, which on inputs with outlier
+// channels exceeds the accuracy asked of this path; P is therefore carried
+// as two e4m3 terms, x = P 2^-e = hi + 2^-4 lo with lo = e4m3(16 (x - hi)),
+// giving a relative error of about 2^-8 for one extra fp8 product.  The
+// scales are not applied on the VALU: v_mfma_scale_f32_32x32x64_f8f6f4 takes
+// a per-lane E8M0 block scale for its B operand, and lane l's block is
+// exactly the 32 probabilities of one query that it holds, so the matrix
+// core multiplies by 2^e (hi) and 2^(e-4) (lo) itself.
+//
+// Layout (mirrors the bf16 kernel): each wave owns 32 queries and computes
+// S^T = K Q^T (keys on M); the C layout gives one query per lane; the fp32
+// probabilities, rounded to e4m3 and packed four per register, are the B
+// operand of O^T += V^T P^T.  For that operand a lane holds 32 keys of its
+// query (16 from each of the two 32-key halves of the block).  V is stored
+// in LDS with its rows permuted inside each 64-key block so that the 32 keys
+// of each wave half are 32 consecutive rows, which ds_read_b64_tr_b8 reads
+// as 8-key columns straight into the A-operand layout.
+#include "attn_device.hpp"
 #include "attn_kernels.hpp"
+
 namespace attn {
-hipError_t launch_fwd_fp8(const FwdArgs&, hipStream_t) { return hipErrorNotSupported; }
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+
+// fp8 tiles: rows of D bytes in 16-byte chunks, chunk c of row r at c ^ swz8(r).
+// d = 128 (8 chunks, 2 rows per 256-byte bank span): the 16 rows of a row
+// read land on 16 different slots, and the 8 rows x 2 chunks of a
+// transposing read land on 16 different slots.  d = 64 likewise with 4 rows
+// per span.
+template <int D>
+__device__ __forceinline__ int swz8(int r);
+template <>
+__device__ __forceinline__ int swz8<128>(int r) {
+  return (((r >> 1) & 3) << 1) | ((r >> 3) & 1);
+}
+template <>
+__device__ __forceinline__ int swz8<64>(int r) {
+  return (((r >> 2) & 1) << 1) | ((r >> 3) & 1);
+}
+template <int D>
+__device__ __forceinline__ int off8(int r, int ch) {
+  return r * D + ((ch ^ swz8<D>(r)) << 4);
+}
+
+// Row of V key `key` inside its LDS tile: within each 64-key block, keys
+// 8a + 4b + c (b in {0,1}) go to row 32b + 4a + c, so wave half b finds its
+// keys {8a + 4b + c} in 32 consecutive rows.
+__device__ __forceinline__ int vrow(int key) {
+  return (key & ~63) | (((key >> 2) & 1) << 5) | (((key >> 3) & 7) << 2) | (key & 3);
+}
+
+template <int D, int ROWS, int NT, bool PERMUTE>
+struct TileStage8 {
+  static constexpr int CH = D / 16;
+  static constexpr int N16 = ROWS * CH / NT;
+  static_assert((ROWS * CH) % NT == 0, "tile must split evenly over threads");
+  u32x4 r[N16];
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, int row0, int tid) {
+#pragma unroll
+    for (int i = 0; i < N16; ++i) {
+      const int c = tid + i * NT, row = c / CH, ch = c % CH;
+      r[i] = buf_load16(rs, (uint32_t)((row0 + row) * D + ch * 16));
+    }
+  }
+  __device__ __forceinline__ void store(uint8_t* t, int tid) const {
+#pragma unroll
+    for (int i = 0; i < N16; ++i) {
+      const int c = tid + i * NT, row = c / CH, ch = c % CH;
+      *(u32x4*)&t[off8<D>(PERMUTE ? vrow(row) : row, ch)] = r[i];
+    }
+  }
+};
+
+__device__ __forceinline__ f32x16 mfma_fp8(i32x8 a, i32x8 b, f32x16 c, int scale_b) {
+  // Formats: A and B e4m3 (0); A block scale 2^0 (127); B block scale per lane.
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0,
+                                                        scale_b);
+}
+
+struct FwdFp8Params {
+  const uint8_t* q;
+  const uint8_t* k;
+  const uint8_t* v;
+  void* o;
+  float* lse;
+  int N;
+  int n_qtiles;
+  float scale;      // softmax scale s
+  float qk_descale; // dq * dk
+  float v_descale;
+  int causal, window, out_f32;
+};
+
+template <int D, int NW>
+__global__ __launch_bounds__(NW * 64, 2) void fwd_fp8_kernel(FwdFp8Params p) {
+  constexpr int BC = 64;  // keys per tile = one 64-deep fp8 MFMA step
+  constexpr int BR = 32 * NW;
+  constexpr int NT = NW * 64;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2][2][BC * D];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int h = lane >> 5, n = lane & 31;
+  const int logical = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = logical / p.n_qtiles;
+  int qt = logical % p.n_qtiles;
+  if (p.causal) qt = p.n_qtiles - 1 - qt;
+  const int N = p.N;
+  const int q0 = qt * BR;
+  const int wq0 = q0 + 32 * w;
+  const int my_q = wq0 + n;
+  const size_t head = (size_t)bh * N * D;
+  const uint32_t head_bytes = (uint32_t)N * D;
+  const auto rq = make_rsrc(p.q + head, head_bytes);
+  const auto rk = make_rsrc(p.k + head, head_bytes);
+  const auto rv = make_rsrc(p.v + head, head_bytes);
+
+  // Q^T as the B operand of S^T = K Q^T: in K-step ks a lane holds the 32
+  // bytes d = 64 ks + 32 h .. +31 of its query; K rows are read the same way.
+  i32x8 qop[D / 64];
+#pragma unroll
+  for (int ks = 0; ks < D / 64; ++ks) {
+    const uint32_t off = (uint32_t)(my_q * D + 64 * ks + 32 * h);
+    const u32x4 a = buf_load16(rq, off), b = buf_load16(rq, off + 16);
+    qop[ks] = (i32x8){(int)a[0], (int)a[1], (int)a[2], (int)a[3],
+                      (int)b[0], (int)b[1], (int)b[2], (int)b[3]};
+  }
+
+  const int q_last = min(q0 + BR, N) - 1;
+  int kv_lo = 0, kv_hi = N;
+  if (p.causal) kv_hi = min(kv_hi, q_last + 1);
+  if (p.window > 0) {
+    kv_lo = max(0, q0 - p.window + 1);
+    if (!p.causal) kv_hi = min(kv_hi, q_last + p.window);
+  }
+  const int t_lo = kv_lo / BC, t_hi = (kv_hi + BC - 1) / BC;
+
+  TileStage8<D, BC, NT, false> stK;
+  TileStage8<D, BC, NT, true> stV;
+  auto load_tile = [&](int t) {
+    stK.load(rk, t * BC, tid);
+    stV.load(rv, t * BC, tid);
+  };
+  auto store_tile = [&](int b) {
+    stK.store(smem[b][0], tid);
+    stV.store(smem[b][1], tid);
+  };
+
+  f32x16 oacc[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) oacc[dt] = (f32x16){};
+  float m_run = kMaxInit, l_run = 0.f;
+  const float s2 = p.scale * p.qk_descale * kLog2e;
+  const float tau = 8.0f / s2;
+
+  if (t_lo < t_hi) {
+    load_tile(t_lo);
+    store_tile(0);
+  }
+  __syncthreads();
+
+  // Transposing-read coordinates: lane j of a 16-lane group reads row
+  // (j >> 1) of an 8-row slab, 8 bytes at column 8 (j & 1) of a 16-byte chunk;
+  // it receives column (lane & 15) of the slab.
+  const int trj = lane & 15, trg = lane >> 4;
+  const int tr_row = 32 * (trg >> 1) + (trj >> 1);       // + 8t
+  const int tr_col = 16 * (trg & 1) + 8 * (trj & 1);     // + 32 dt
+
+  int buf = 0;
+  for (int t = t_lo; t < t_hi; ++t) {
+    const bool has_next = t + 1 < t_hi;
+    if (has_next) load_tile(t + 1);
+    const uint8_t* Ks = smem[buf][0];
+    const uint8_t* Vs = smem[buf][1];
+    const int kv0 = t * BC;
+
+    f32x16 sacc[2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      sacc[mt] = (f32x16){};
+      const int r = 32 * mt + n;
+#pragma unroll
+      for (int ks = 0; ks < D / 64; ++ks) {
+        const u32x4 a = *(const u32x4*)&Ks[off8<D>(r, 4 * ks + 2 * h)];
+        const u32x4 b = *(const u32x4*)&Ks[off8<D>(r, 4 * ks + 2 * h + 1)];
+        const i32x8 ka = {(int)a[0], (int)a[1], (int)a[2], (int)a[3],
+                          (int)b[0], (int)b[1], (int)b[2], (int)b[3]};
+        sacc[mt] = mfma_fp8(ka, qop[ks], sacc[mt], 127);
+      }
+    }
+
+    bool need_mask = kv0 + BC > N;
+    if (p.causal) need_mask |= kv0 + BC - 1 > wq0;
+    if (p.window > 0) {
+      need_mask |= wq0 + 31 - kv0 >= p.window;
+      if (!p.causal) need_mask |= kv0 + BC - 1 - wq0 >= p.window;
+    }
+    if (need_mask) {
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = kv0 + 32 * mt + 8 * (r >> 2) + 4 * h + (r & 3);
+          if (!visible(my_q, key, N, p.causal, p.window))
+            sacc[mt][r] = -__builtin_inff();
+        }
+    }
+
+    float mx = -__builtin_inff();
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[mt][r]);
+    mx = halves_max(mx);
+    const float m_new = (mx > m_run + tau) ? mx : m_run;
+    const float alpha = fast_exp2((m_run - m_new) * s2);
+    m_run = m_new;
+    if (__ballot(alpha != 1.f)) {
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) oacc[dt] *= alpha;
+    }
+    const float mb = m_run * s2;
+    float pmax = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        sacc[mt][r] = fast_exp2(fmaf(sacc[mt][r], s2, -mb));
+        pmax = fmaxf(pmax, sacc[mt][r]);
+      }
+    pmax = halves_max(pmax);
+    // 2^e with pmax * 2^-e in [128, 256); e kept where e - 4 is a valid E8M0.
+    int e = (int)((__builtin_bit_cast(uint32_t, pmax) >> 23) & 0xff) - 127 - 7;
+    e = max(-123, min(127, e));
+    // Pack: byte j of the B operand = block key slot j = C[j / 16][j % 16].
+    i32x8 phi, plo;
+    float lsum = 0.f;
+#pragma unroll
+    for (int wd = 0; wd < 8; ++wd) {
+      const int mt = wd >> 2, r0 = 4 * (wd & 3);
+      float x[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        lsum += sacc[mt][r0 + i];
+        x[i] = __builtin_ldexpf(sacc[mt][r0 + i], -e);
+      }
+      int hw = 0;
+      hw = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], hw, false);
+      hw = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], hw, true);
+      const auto h01 = __builtin_amdgcn_cvt_pk_f32_fp8(hw, false);
+      const auto h23 = __builtin_amdgcn_cvt_pk_f32_fp8(hw, true);
+      int lw = 0;
+      lw = __builtin_amdgcn_cvt_pk_fp8_f32(16.f * (x[0] - h01[0]), 16.f * (x[1] - h01[1]),
+                                           lw, false);
+      lw = __builtin_amdgcn_cvt_pk_fp8_f32(16.f * (x[2] - h23[0]), 16.f * (x[3] - h23[1]),
+                                           lw, true);
+      phi[wd] = hw;
+      plo[wd] = lw;
+    }
+    l_run += lsum;
+
+    // O^T += V^T (2^e hi + 2^(e-4) lo)^T, the scales applied by the MFMA.
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) {
+      i32x8 va;
+#pragma unroll
+      for (int t8 = 0; t8 < 4; ++t8) {
+        const int row = tr_row + 8 * t8, col = 32 * dt + tr_col;
+        const i32x2 x = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+            (LDS_AS i32x2*)&Vs[off8<D>(row, col >> 4) + (col & 15)]);
+        va[2 * t8] = x[0];
+        va[2 * t8 + 1] = x[1];
+      }
+      oacc[dt] = mfma_fp8(va, phi, oacc[dt], e + 127);
+      oacc[dt] = mfma_fp8(va, plo, oacc[dt], e - 4 + 127);
+    }
+
+    if (has_next) store_tile(buf ^ 1);
+    __syncthreads();
+    buf ^= 1;
+  }
+
+  const float l_tot = halves_sum(l_run);
+  if (my_q < N) {
+    const float inv = p.v_descale / l_tot;
+    const size_t row = head + (size_t)my_q * D;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = 32 * dt + 8 * g + 4 * h;
+        const float x0 = oacc[dt][4 * g + 0] * inv, x1 = oacc[dt][4 * g + 1] * inv;
+        const float x2 = oacc[dt][4 * g + 2] * inv, x3 = oacc[dt][4 * g + 3] * inv;
+        if (p.out_f32) {
+          *(f32x4*)((float*)p.o + row + d0) = (f32x4){x0, x1, x2, x3};
+        } else {
+          *(bf16x4*)((__bf16*)p.o + row + d0) =
+              (bf16x4){(__bf16)x0, (__bf16)x1, (__bf16)x2, (__bf16)x3};
+        }
+      }
+    if (h == 0 && p.lse)
+      p.lse[(size_t)bh * N + my_q] =
+          (m_run * s2 + __builtin_amdgcn_logf(l_tot)) * kLn2;
+  }
+}
+
+template <int D>
+static hipError_t launch_fp8_d(const FwdArgs& a, hipStream_t stream) {
+  constexpr int NW = 4;
+  FwdFp8Params p;
+  p.q = (const uint8_t*)a.q;
+  p.k = (const uint8_t*)a.k;
+  p.v = (const uint8_t*)a.v;
+  p.o = a.o;
+  p.lse = a.lse;
+  p.N = a.N;
+  p.n_qtiles = (a.N + 32 * NW - 1) / (32 * NW);
+  p.scale = a.scale;
+  p.qk_descale = a.q_descale * a.k_descale;
+  p.v_descale = a.v_descale;
+  p.causal = a.causal;
+  p.window = a.window;
+  p.out_f32 = a.out_f32;
+  const unsigned grid = (unsigned)(a.BH * p.n_qtiles);
+  hipLaunchKernelGGL((fwd_fp8_kernel<D, NW>), dim3(grid), dim3(NW * 64), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd_fp8(const FwdArgs& a, hipStream_t stream) {
+  if (a.d == 128) return launch_fp8_d<128>(a, stream);
+  return launch_fp8_d<64>(a, stream);
+}
+
 }  // namespace attn
