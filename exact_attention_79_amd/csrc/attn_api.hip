@@ -4,7 +4,7 @@
 #include <math.h>
 #include <stdint.h>
 
-#include "../../include/attn.h"
+#include "attn.h"
 #include "attn_kernels.hpp"
 
 namespace {

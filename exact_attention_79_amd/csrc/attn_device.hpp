@@ -161,6 +161,27 @@ __device__ __forceinline__ bf16x8 tile_a_tr(const __bf16* t, const TrCoord& c,
   return cat4(tile_tr4<D>(t, r, col), tile_tr4<D>(t, r + 8, col));
 }
 
+// Global -> LDS copy of a ROWS x D bf16 tile without passing through VGPRs
+// (buffer_load_dwordx4 ... lds): each wave instruction writes 64 consecutive
+// 16-byte LDS chunks (lane L -> chunk base + L), so each lane fetches the
+// global chunk that the swizzle places there.  Rows past the end of the
+// buffer resource land as zeros.  Completion is tracked by vmcnt.
+template <int D, int ROWS, int NW>
+__device__ __forceinline__ void tile_load_lds(__amdgpu_buffer_rsrc_t rs, int row0,
+                                              __bf16* t, int w, int lane) {
+  constexpr int CH = D / 8;
+  constexpr int ROUNDS = ROWS * CH / (64 * NW);
+  static_assert((ROWS * CH) % (64 * NW) == 0, "tile must split evenly over waves");
+#pragma unroll
+  for (int i = 0; i < ROUNDS; ++i) {
+    const int base = (i * NW + w) * 64;  // first physical chunk of this instruction
+    const int pc = base + lane, row = pc / CH, ch = (pc % CH) ^ swz<D>(row);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rs, (LDS_AS void*)(t + base * 8), 16,
+        (int)((uint32_t)((row0 + row) * D + ch * 8) * 2u), 0, 0, 0);
+  }
+}
+
 // Global -> register -> LDS staging of a ROWS x D bf16 tile by NT threads:
 // thread tid moves chunks tid, tid + NT, ... (16 threads per 256-byte row,
 // so every global access is a full coalesced row segment).  Rows past the

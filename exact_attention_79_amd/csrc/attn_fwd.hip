@@ -53,10 +53,18 @@ struct FwdKParams {
 
 template <int D, int NW, int BC>
 __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdKParams p) {
-  constexpr int BR = 32 * NW;          // queries per workgroup
-  constexpr int NT = NW * 64;          // threads per workgroup
-  static_assert(BC % 32 == 0, "key tile is a multiple of 32");
-  __shared__ __attribute__((aligned(16))) __bf16 smem[2][2][BC * D];
+  constexpr int BR = 32 * NW;  // queries per workgroup
+  static_assert(BC == 32 || BC == 64, "the pipeline is written for 32- or 64-key tiles");
+  // Three LDS slots each for K and V, as separate arrays so that the
+  // compiler can tell the tiles being filled from the tiles being read.
+  // Tile u (counted from the first visible tile) lives in slot u % 3; tiles
+  // are fetched two iterations before they are first read.
+  __shared__ __attribute__((aligned(16))) __bf16 sK0[BC * D];
+  __shared__ __attribute__((aligned(16))) __bf16 sK1[BC * D];
+  __shared__ __attribute__((aligned(16))) __bf16 sK2[BC * D];
+  __shared__ __attribute__((aligned(16))) __bf16 sV0[BC * D];
+  __shared__ __attribute__((aligned(16))) __bf16 sV1[BC * D];
+  __shared__ __attribute__((aligned(16))) __bf16 sV2[BC * D];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int h = lane >> 5, n = lane & 31;
@@ -92,41 +100,16 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdKParams p) {
   }
   const int t_lo = kv_lo / BC, t_hi = (kv_hi + BC - 1) / BC;
 
-  TileStage<D, BC, NT> stK, stV;
-  auto load_tile = [&](int t) {
-    stK.load(rk, t * BC, tid);
-    stV.load(rv, t * BC, tid);
-  };
-  auto store_tile = [&](int b) {
-    stK.store(smem[b][0], tid);
-    stV.store(smem[b][1], tid);
-  };
-
   f32x16 oacc[D / 32];
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) oacc[dt] = (f32x16){};
   float m_run = kMaxInit, l_run = 0.f;
   const float s2 = p.scale * kLog2e;
   const float tau = 8.0f / s2;
-
-  if (t_lo < t_hi) {
-    load_tile(t_lo);
-    store_tile(0);
-  }
-  __syncthreads();
-
   const TrCoord trc(lane);  // transposing-read coordinates of this lane
 
-  int buf = 0;
-  for (int t = t_lo; t < t_hi; ++t) {
-    const bool has_next = t + 1 < t_hi;
-    if (has_next) load_tile(t + 1);
-    const __bf16* Ks = smem[buf][0];
-    const __bf16* Vs = smem[buf][1];
-    const int kv0 = t * BC;
-
-    // ---- S^T = K_j Q_i^T (raw scores, fp32) ----
-    f32x16 sacc[BC / 32];
+  // S^T = K_j Q_i^T (raw scores, fp32), keys on M, this wave's queries on N.
+  auto scores = [&](const __bf16* Ks, f32x16* sacc) {
 #pragma unroll
     for (int mt = 0; mt < BC / 32; ++mt) {
       sacc[mt] = (f32x16){};
@@ -135,8 +118,42 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdKParams p) {
       for (int ks = 0; ks < D / 16; ++ks)
         sacc[mt] = mfma32(tile_row8<D>(Ks, r, 2 * ks + h), qop[ks], sacc[mt]);
     }
+  };
 
-    // ---- mask only on tiles that straddle a boundary (wave-uniform test) ----
+  // Keys this lane may see: lo_key <= key <= hi_key.
+  int hi_key = N - 1, lo_key = 0;
+  if (p.causal) hi_key = min(hi_key, my_q);
+  if (p.window > 0) {
+    lo_key = my_q - p.window + 1;
+    if (!p.causal) hi_key = min(hi_key, my_q + p.window - 1);
+  }
+
+  // Prologue: K_0..K_2 and V_0, V_1 in flight (u = tile - t_lo), then S
+  // for the first tile.  Tiles past the last visible one may be loaded and
+  // scored: rows past N read as zeros and their scores are never used.
+  tile_load_lds<D, BC, NW>(rk, t_lo * BC, sK0, w, lane);
+  tile_load_lds<D, BC, NW>(rv, t_lo * BC, sV0, w, lane);
+  tile_load_lds<D, BC, NW>(rk, (t_lo + 1) * BC, sK1, w, lane);
+  tile_load_lds<D, BC, NW>(rv, (t_lo + 1) * BC, sV1, w, lane);
+  tile_load_lds<D, BC, NW>(rk, (t_lo + 2) * BC, sK2, w, lane);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  f32x16 scur[BC / 32];
+  scores(sK0, scur);
+
+  // vmcnt <= the loads issued by one iteration (lgkmcnt and expcnt free).
+  constexpr int kLoadsPerIter = 2 * (BC * D / 8) / (64 * NW);
+  constexpr int kWaitOlderLoads = (kLoadsPerIter & 0xF) | (0x7 << 4) | (0xF << 8) |
+                                  ((kLoadsPerIter >> 4) << 14);
+
+  // One iteration for tile t: it reads K_{t+1} from Kr and V_t from Vr, and
+  // refills Kf (K_t's slot) with K_{t+3} and Vf (V_{t-1}'s slot) with V_{t+2}.
+  auto iteration = [&](int t, const __bf16* Kr, const __bf16* Vr, __bf16* Kf,
+                       __bf16* Vf) {
+    tile_load_lds<D, BC, NW>(rk, (t + 3) * BC, Kf, w, lane);
+    tile_load_lds<D, BC, NW>(rv, (t + 2) * BC, Vf, w, lane);
+    // Mask only tiles that straddle a boundary of this wave (uniform test).
+    const int kv0 = t * BC;
     bool need_mask = kv0 + BC > N;
     if (p.causal) need_mask |= kv0 + BC - 1 > wq0;
     if (p.window > 0) {
@@ -149,17 +166,15 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdKParams p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = kv0 + 32 * mt + 8 * (r >> 2) + 4 * h + (r & 3);
-          if (!visible(my_q, key, N, p.causal, p.window))
-            sacc[mt][r] = -__builtin_inff();
+          scur[mt][r] = (key > hi_key || key < lo_key) ? -__builtin_inff() : scur[mt][r];
         }
     }
-
-    // ---- online softmax, one query per lane ----
+    // Running max; the (rare) rescale is done before the main block.
     float mx = -__builtin_inff();
 #pragma unroll
     for (int mt = 0; mt < BC / 32; ++mt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[mt][r]);
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, scur[mt][r]);
     mx = halves_max(mx);
     const float m_new = (mx > m_run + tau) ? mx : m_run;
     const float alpha = fast_exp2((m_run - m_new) * s2);
@@ -170,29 +185,70 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdKParams p) {
       for (int dt = 0; dt < D / 32; ++dt) oacc[dt] *= alpha;
     }
     const float mb = m_run * s2;
-    bf16x8 pop[BC / 16];
+
+    // Main block, scheduled by hand in bundles that the compiler may not
+    // reorder across (sched_barrier): each bundle issues one MFMA, the LDS
+    // read for the MFMA four bundles later, and a slice of the softmax, so
+    // LDS latency is covered and the VALU work sits between MFMAs.
+    // Bundles 0..NS-1: the next tile's score MFMAs + this tile's exps;
+    // bundles NS..NS+NP-1: this tile's P V MFMAs.
+    constexpr int KS = D / 16;                 // K-steps per score tile
+    constexpr int NS = (BC / 32) * KS;         // score MFMAs
+    constexpr int NP = (BC / 16) * (D / 32);   // P V MFMAs
+    constexpr int EPB = BC / 2 / NS;           // exps per lane per bundle
+    constexpr int AHEAD = 4;
+    const __bf16* Kn = Kr;
+    const __bf16* Vs = Vr;
+    auto kread = [&](int i) {
+      return tile_row8<D>(Kn, 32 * (i / KS) + n, 2 * (i % KS) + h);
+    };
+    auto vread = [&](int j) { return tile_a_tr<D>(Vs, trc, j / (D / 32), j % (D / 32)); };
+    f32x16 snext[BC / 32];
+#pragma unroll
+    for (int mt = 0; mt < BC / 32; ++mt) snext[mt] = (f32x16){};
+    bf16x8 ka[NS], va[NP], pop[BC / 16];
     float lsum = 0.f;
 #pragma unroll
-    for (int mt = 0; mt < BC / 32; ++mt)
+    for (int i = 0; i < AHEAD; ++i) ka[i] = kread(i);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float e = fast_exp2(fmaf(sacc[mt][r], s2, -mb));
-        lsum += e;
-        pop[2 * mt + (r >> 3)][r & 7] = (__bf16)e;
+    for (int i = 0; i < NS; ++i) {
+      if (i + AHEAD < NS) ka[i + AHEAD] = kread(i + AHEAD);
+      if (i >= NS - AHEAD) va[i - (NS - AHEAD)] = vread(i - (NS - AHEAD));
+      snext[i / KS] = mfma32(ka[i], qop[i % KS], snext[i / KS]);
+#pragma unroll
+      for (int u = 0; u < EPB; ++u) {
+        const int e = EPB * i + u, mt = e >> 4, r = e & 15;
+        const float x = fast_exp2(fmaf(scur[mt][r], s2, -mb));
+        lsum += x;
+        pop[e >> 3][e & 7] = (__bf16)x;
       }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int j = 0; j < NP; ++j) {
+      if (j + AHEAD < NP) va[j + AHEAD] = vread(j + AHEAD);
+      oacc[j % (D / 32)] = mfma32(va[j], pop[j / (D / 32)], oacc[j % (D / 32)]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     l_run += lsum;
 
-    // ---- O^T += V_j^T P^T ----
+    // The loads issued one iteration ago (K_{t+2}, V_{t+1}) have landed for
+    // this wave; after the barrier they have for every wave, and the slots
+    // read in this iteration may be refilled.  This iteration's loads stay
+    // in flight.
+    __builtin_amdgcn_s_waitcnt(kWaitOlderLoads);
+    __builtin_amdgcn_s_barrier();
 #pragma unroll
-    for (int kk = 0; kk < BC / 16; ++kk)
-#pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt)
-        oacc[dt] = mfma32(tile_a_tr<D>(Vs, trc, kk, dt), pop[kk], oacc[dt]);
+    for (int mt = 0; mt < BC / 32; ++mt) scur[mt] = snext[mt];
+  };
 
-    if (has_next) store_tile(buf ^ 1);
-    __syncthreads();
-    buf ^= 1;
+  for (int t = t_lo; t < t_hi; t += 3) {
+    iteration(t, sK1, sV0, sK0, sV2);
+    if (t + 1 < t_hi) iteration(t + 1, sK2, sV1, sK1, sV0);
+    if (t + 2 < t_hi) iteration(t + 2, sK0, sV2, sK2, sV1);
   }
+  __builtin_amdgcn_s_waitcnt(0);
 
   // ---- epilogue: O = O~ / l, L = ln 2 * (m s2 + log2 l) ----
   const float l_tot = halves_sum(l_run);
@@ -240,7 +296,7 @@ static hipError_t launch_fwd_cfg(const FwdArgs& a, hipStream_t stream) {
 }
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream) {
-  if (a.d == 128) return launch_fwd_cfg<128, 4, 64>(a, stream);
+  if (a.d == 128) return launch_fwd_cfg<128, 4, 32>(a, stream);
   return launch_fwd_cfg<64, 4, 64>(a, stream);
 }
 
