@@ -29,6 +29,8 @@
 // K Q^T with one query per lane, and dQ^T += K^T dS^T with K^T read
 // transposed from LDS.  Q/dO (dK/dV kernel) and K/V (dQ kernel) tiles are
 // double-buffered in LDS with the same swizzle as the forward.
+#include <limits.h>
+
 #include "attn_device.hpp"
 #include "attn_kernels.hpp"
 
@@ -80,15 +82,25 @@ struct BwdKParams {
 };
 
 // ---------------------------------------------------------------- dK, dV
+// One workgroup per block of 32*NW keys; wave w owns keys kw0 .. kw0+31 (one
+// per lane on the MFMA N side).  Query tiles of BQ rows stream through
+// three LDS slots (Q, dO and their L, D) fetched one tile ahead by direct
+// global->LDS loads.  Iteration i computes S and dP for tile i+1 on the
+// matrix cores while the VALU forms P and dS for tile i, then accumulates
+// dV += P^T dO and dK += dS^T Q for tile i.
 template <int D, int NW, int BQ>
 __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(BwdKParams p) {
-  constexpr int BKV = 32 * NW;  // keys per workgroup
-  constexpr int NT = NW * 64;
-  static_assert(BQ % 32 == 0 && BQ <= NT, "query tile");
-  __shared__ __attribute__((aligned(16))) __bf16 sQ[2][BQ * D];
-  __shared__ __attribute__((aligned(16))) __bf16 sdO[2][BQ * D];
-  __shared__ __attribute__((aligned(16))) float sL[2][BQ];
-  __shared__ __attribute__((aligned(16))) float sD[2][BQ];
+  constexpr int BKV = 32 * NW;
+  constexpr int KS = D / 16;
+  static_assert(BQ == 64, "one dword per lane stages L and D");
+  __shared__ __attribute__((aligned(16))) __bf16 sQ0[BQ * D];
+  __shared__ __attribute__((aligned(16))) __bf16 sQ1[BQ * D];
+  __shared__ __attribute__((aligned(16))) __bf16 sQ2[BQ * D];
+  __shared__ __attribute__((aligned(16))) __bf16 sO0[BQ * D];
+  __shared__ __attribute__((aligned(16))) __bf16 sO1[BQ * D];
+  __shared__ __attribute__((aligned(16))) __bf16 sO2[BQ * D];
+  __shared__ __attribute__((aligned(16))) float sL0[BQ], sL1[BQ], sL2[BQ];
+  __shared__ __attribute__((aligned(16))) float sD0[BQ], sD1[BQ], sD2[BQ];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int h = lane >> 5, n = lane & 31;
@@ -105,13 +117,13 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(BwdKParams p) {
   const auto rk = make_rsrc(p.k + head, head_bytes);
   const auto rv = make_rsrc(p.v + head, head_bytes);
   const auto rdo = make_rsrc(p.dout + head, head_bytes);
-  const float* lse = p.lse + (size_t)bh * N;
-  const float* delta = p.delta + (size_t)bh * N;
+  const auto rl = make_rsrc(p.lse + (size_t)bh * N, (uint32_t)N * 4);
+  const auto rdl = make_rsrc(p.delta + (size_t)bh * N, (uint32_t)N * 4);
 
   // K^T and V^T as B operands (lane = key, 8 consecutive d per K-step).
-  bf16x8 kop[D / 16], vop[D / 16];
+  bf16x8 kop[KS], vop[KS];
 #pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) {
+  for (int ks = 0; ks < KS; ++ks) {
     const uint32_t off = (uint32_t)(my_k * D + 16 * ks + 8 * h) * 2u;
     kop[ks] = __builtin_bit_cast(bf16x8, buf_load16(rk, off));
     vop[ks] = __builtin_bit_cast(bf16x8, buf_load16(rv, off));
@@ -120,111 +132,153 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(BwdKParams p) {
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) dkacc[dt] = dvacc[dt] = (f32x16){};
 
-  // Queries that can see any key of this block.
+  // Queries that can see any key of this block, and those that see my_k.
   const int k_last = min(k0 + BKV, N) - 1;
   int q_lo = p.causal ? k0 : 0, q_hi = N;
+  int qmin = p.causal ? my_k : INT_MIN, qmax = INT_MAX;
   if (W > 0) {
     q_lo = max(q_lo, k0 - W + 1);
     q_hi = min(q_hi, k_last + W);
+    if (!p.causal) qmin = my_k - W + 1;
+    qmax = my_k + W - 1;
   }
   const int t_lo = q_lo / BQ, t_hi = (q_hi + BQ - 1) / BQ;
 
-  TileStage<D, BQ, NT> stQ, stO;
-  float stL = 0.f, stD = 0.f;
-  auto load_tile = [&](int t) {
-    stQ.load(rq, t * BQ, tid);
-    stO.load(rdo, t * BQ, tid);
-    if (tid < BQ) {
-      const int i = t * BQ + tid;
-      stL = i < N ? lse[i] * kLog2e : 0.f;
-      stD = i < N ? delta[i] : 0.f;
-    }
-  };
-  auto store_tile = [&](int b) {
-    stQ.store(sQ[b], tid);
-    stO.store(sdO[b], tid);
-    if (tid < BQ) {
-      sL[b][tid] = stL;
-      sD[b][tid] = stD;
-    }
-  };
-
   const float s2 = p.scale * kLog2e;
   const TrCoord trc(lane);
-  if (t_lo < t_hi) {
-    load_tile(t_lo);
-    store_tile(0);
-  }
-  __syncthreads();
 
-  int buf = 0;
-  for (int t = t_lo; t < t_hi; ++t) {
-    const bool has_next = t + 1 < t_hi;
-    if (has_next) load_tile(t + 1);
-    const int i0 = t * BQ;
-    // Does any (query of this tile, key of this wave) pair survive the mask?
-    bool active = kw0 < N;
-    if (p.causal) active &= i0 + BQ - 1 >= kw0;
-    if (W > 0) {
-      active &= i0 - (kw0 + 31) < W;
-      if (!p.causal) active &= kw0 - (i0 + BQ - 1) < W;
+  auto load_tile = [&](int t, __bf16* Qf, __bf16* Of, float* Lf, float* Df) {
+    tile_load_lds<D, BQ, NW>(rq, t * BQ, Qf, w, lane);
+    tile_load_lds<D, BQ, NW>(rdo, t * BQ, Of, w, lane);
+    if (w == 0) {
+      vec_load_lds<BQ>(rl, t * BQ, Lf, lane);
+      vec_load_lds<BQ>(rdl, t * BQ, Df, lane);
     }
-    if (active) {
-      const __bf16* Qs = sQ[buf];
-      const __bf16* Os = sdO[buf];
-      // S = Q K^T and dP = dO V^T (queries on M, this wave's keys on N).
-      f32x16 sacc[BQ / 32], dpacc[BQ / 32];
+  };
+  // S = Q K^T and dP = dO V^T for one tile (queries on M, this wave's keys on N).
+  auto sdp = [&](const __bf16* Qs, const __bf16* Os, f32x16* sacc, f32x16* dpacc) {
 #pragma unroll
-      for (int mt = 0; mt < BQ / 32; ++mt) {
-        sacc[mt] = dpacc[mt] = (f32x16){};
-        const int r = 32 * mt + n;
+    for (int mt = 0; mt < BQ / 32; ++mt) {
+      sacc[mt] = dpacc[mt] = (f32x16){};
 #pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks) {
-          sacc[mt] = mfma32(tile_row8<D>(Qs, r, 2 * ks + h), kop[ks], sacc[mt]);
-          dpacc[mt] = mfma32(tile_row8<D>(Os, r, 2 * ks + h), vop[ks], dpacc[mt]);
-        }
+      for (int ks = 0; ks < KS; ++ks) {
+        sacc[mt] = mfma32(tile_row8<D>(Qs, 32 * mt + n, 2 * ks + h), kop[ks], sacc[mt]);
+        dpacc[mt] = mfma32(tile_row8<D>(Os, 32 * mt + n, 2 * ks + h), vop[ks], dpacc[mt]);
       }
-      bool need_mask = (i0 + BQ > N) || (kw0 + 32 > N);
-      if (p.causal) need_mask |= i0 < kw0 + 31;
-      if (W > 0) {
-        need_mask |= (i0 + BQ - 1) - kw0 >= W;
-        if (!p.causal) need_mask |= (kw0 + 31) - i0 >= W;
-      }
-      // P = exp(s S - L), dS = P (dP - D); rows are queries 32mt + 8g + 4h + 0..3.
-      bf16x8 pop[BQ / 16], dsop[BQ / 16];
+    }
+  };
+
+  // Prologue: tiles t_lo and t_lo+1; S, dP of the first tile.  Tiles past
+  // the last visible one read as zeros (rows >= N) or are never used.
+  load_tile(t_lo, sQ0, sO0, sL0, sD0);
+  load_tile(t_lo + 1, sQ1, sO1, sL1, sD1);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  f32x16 scur[BQ / 32], dpcur[BQ / 32];
+  sdp(sQ0, sO0, scur, dpcur);
+
+  // Iteration for query tile t: P, dS of tile t (slot c: Qc, Oc, Lc, Dc)
+  // while S, dP of tile t+1 (slot n: Qn, On) run on the matrix cores; tile
+  // t+2 is fetched into slot f (tile t-1's, fully consumed).
+  auto iteration = [&](int t, const __bf16* Qc, const __bf16* Oc, const float* Lc,
+                       const float* Dc, const __bf16* Qn, const __bf16* On, __bf16* Qf,
+                       __bf16* Of, float* Lf, float* Df) {
+    load_tile(t + 2, Qf, Of, Lf, Df);
+    const int i0 = t * BQ;
+    bool need_mask = false;
+    if (p.causal) need_mask |= i0 < kw0 + 31;
+    if (W > 0) {
+      need_mask |= (i0 + BQ - 1) - kw0 >= W;
+      if (!p.causal) need_mask |= (kw0 + 31) - i0 >= W;
+    }
+    if (need_mask) {
 #pragma unroll
       for (int mt = 0; mt < BQ / 32; ++mt)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int qi = 32 * mt + 8 * g + 4 * h;
-          const f32x4 Lb = *(const f32x4*)&sL[buf][qi];
-          const f32x4 Dl = *(const f32x4*)&sD[buf][qi];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 4 * g + e;
-            float sv = sacc[mt][r];
-            if (need_mask) {
-              const int qq = i0 + qi + e;
-              if (!(qq < N && visible(qq, my_k, N, p.causal, W))) sv = -__builtin_inff();
-            }
-            const float pv = fast_exp2(fmaf(sv, s2, -Lb[e]));
-            const float ds = pv * (dpacc[mt][r] - Dl[e]);
-            pop[2 * mt + (r >> 3)][r & 7] = (__bf16)pv;
-            dsop[2 * mt + (r >> 3)][r & 7] = (__bf16)ds;
-          }
-        }
-      // dV^T += dO^T P, dK^T += Q^T dS (d on M, keys on N, queries contracted).
-#pragma unroll
-      for (int kk = 0; kk < BQ / 16; ++kk)
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt) {
-          dvacc[dt] = mfma32(tile_a_tr<D>(Os, trc, kk, dt), pop[kk], dvacc[dt]);
-          dkacc[dt] = mfma32(tile_a_tr<D>(Qs, trc, kk, dt), dsop[kk], dkacc[dt]);
+        for (int r = 0; r < 16; ++r) {
+          const int q = i0 + 32 * mt + 8 * (r >> 2) + 4 * h + (r & 3);
+          scur[mt][r] = (q < qmin || q > qmax) ? -__builtin_inff() : scur[mt][r];
         }
     }
-    if (has_next) store_tile(buf ^ 1);
-    __syncthreads();
-    buf ^= 1;
+    // L and D of the query rows this lane holds, four rows (one group g) at
+    // a time: group g covers rows 32 (g / 4) + 8 (g % 4) + 4h + 0..3.
+    auto lrow = [&](int g) { return *(const f32x4*)&Lc[32 * (g >> 2) + 8 * (g & 3) + 4 * h]; };
+    auto drow = [&](int g) { return *(const f32x4*)&Dc[32 * (g >> 2) + 8 * (g & 3) + 4 * h]; };
+    f32x4 lb[BQ / 8], dl[BQ / 8];
+
+    constexpr int NS = 2 * (BQ / 32) * KS;     // S and dP MFMAs of the next tile
+    constexpr int NP = 2 * (BQ / 16) * (D / 32);  // dV and dK MFMAs of this tile
+    constexpr int EPB = (BQ / 2) / NS;        // P/dS elements per lane per bundle
+    constexpr int AHEAD = 3;
+    static_assert(EPB >= 1 && (BQ / 2) % NS == 0, "bundle split");
+    // Score bundle i: MFMA (i even: S, odd: dP) of M-tile mt, K-step ks.
+    auto arow = [&](int i) {
+      const int j = i >> 1, mt = j / KS, ks = j % KS;
+      return tile_row8<D>((i & 1) ? On : Qn, 32 * mt + n, 2 * ks + h);
+    };
+    // Product bundle j: (j even: dV from dO^T, odd: dK from Q^T) of K-step
+    // kk, d-tile dt.
+    auto atr = [&](int j) {
+      const int jj = j >> 1;
+      return tile_a_tr<D>((j & 1) ? Qc : Oc, trc, jj / (D / 32), jj % (D / 32));
+    };
+    f32x16 snext[BQ / 32], dpnext[BQ / 32];
+#pragma unroll
+    for (int mt = 0; mt < BQ / 32; ++mt) snext[mt] = dpnext[mt] = (f32x16){};
+    bf16x8 aop[NS], top[NP], pop[BQ / 16], dsop[BQ / 16];
+    constexpr int GB = 4 / EPB;  // bundles per 4-row group
+#pragma unroll
+    for (int i = 0; i < AHEAD; ++i) aop[i] = arow(i);
+    lb[0] = lrow(0) * kLog2e;
+    dl[0] = drow(0);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      if (i + AHEAD < NS) aop[i + AHEAD] = arow(i + AHEAD);
+      if (i >= NS - AHEAD) top[i - (NS - AHEAD)] = atr(i - (NS - AHEAD));
+      if (i % GB == 0 && i / GB + 1 < BQ / 8) {  // next group's L, D one group ahead
+        lb[i / GB + 1] = lrow(i / GB + 1) * kLog2e;
+        dl[i / GB + 1] = drow(i / GB + 1);
+      }
+      const int j = i >> 1, mt = j / KS, ks = j % KS;
+      if (i & 1)
+        dpnext[mt] = mfma32(aop[i], vop[ks], dpnext[mt]);
+      else
+        snext[mt] = mfma32(aop[i], kop[ks], snext[mt]);
+#pragma unroll
+      for (int u = 0; u < EPB; ++u) {
+        const int e = EPB * i + u, mt2 = e >> 4, r = e & 15, g = 4 * mt2 + (r >> 2);
+        const float pv = fast_exp2(fmaf(scur[mt2][r], s2, -lb[g][r & 3]));
+        const float ds = pv * (dpcur[mt2][r] - dl[g][r & 3]);
+        pop[e >> 3][e & 7] = (__bf16)pv;
+        dsop[e >> 3][e & 7] = (__bf16)ds;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int j = 0; j < NP; ++j) {
+      if (j + AHEAD < NP) top[j + AHEAD] = atr(j + AHEAD);
+      const int jj = j >> 1, kk = jj / (D / 32), dt = jj % (D / 32);
+      if (j & 1)
+        dkacc[dt] = mfma32(top[j], dsop[kk], dkacc[dt]);
+      else
+        dvacc[dt] = mfma32(top[j], pop[kk], dvacc[dt]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // Tile t+2 has landed for every wave; slot c may be refilled next time.
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_s_barrier();
+#pragma unroll
+    for (int mt = 0; mt < BQ / 32; ++mt) {
+      scur[mt] = snext[mt];
+      dpcur[mt] = dpnext[mt];
+    }
+  };
+
+  for (int t = t_lo; t < t_hi; t += 3) {
+    iteration(t, sQ0, sO0, sL0, sD0, sQ1, sO1, sQ2, sO2, sL2, sD2);
+    if (t + 1 < t_hi) iteration(t + 1, sQ1, sO1, sL1, sD1, sQ2, sO2, sQ0, sO0, sL0, sD0);
+    if (t + 2 < t_hi) iteration(t + 2, sQ2, sO2, sL2, sD2, sQ0, sO0, sQ1, sO1, sL1, sD1);
   }
 
   if (my_k < N) {
@@ -244,11 +298,20 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(BwdKParams p) {
 }
 
 // ---------------------------------------------------------------- dQ
+// One workgroup per block of 32*NW queries (one query per lane on the MFMA N
+// side); K/V tiles of BC keys stream through three LDS slots fetched one
+// tile ahead.  Iteration t computes S^T and dP^T of tile t+1 on the matrix
+// cores while the VALU forms P and dS^T of tile t, then dQ^T += K_t^T dS_t^T.
 template <int D, int NW, int BC>
-__global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(BwdKParams p) {
+__global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdKParams p) {
   constexpr int BR = 32 * NW;
-  constexpr int NT = NW * 64;
-  __shared__ __attribute__((aligned(16))) __bf16 smem[2][2][BC * D];
+  constexpr int KS = D / 16;
+  __shared__ __attribute__((aligned(16))) __bf16 sK0[BC * D];
+  __shared__ __attribute__((aligned(16))) __bf16 sK1[BC * D];
+  __shared__ __attribute__((aligned(16))) __bf16 sK2[BC * D];
+  __shared__ __attribute__((aligned(16))) __bf16 sV0[BC * D];
+  __shared__ __attribute__((aligned(16))) __bf16 sV1[BC * D];
+  __shared__ __attribute__((aligned(16))) __bf16 sV2[BC * D];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int h = lane >> 5, n = lane & 31;
@@ -268,9 +331,9 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(BwdKParams p) {
   const auto rdo = make_rsrc(p.dout + head, head_bytes);
 
   // Q^T and dO^T as B operands (lane = query), L and D per lane.
-  bf16x8 qop[D / 16], doop[D / 16];
+  bf16x8 qop[KS], doop[KS];
 #pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) {
+  for (int ks = 0; ks < KS; ++ks) {
     const uint32_t off = (uint32_t)(my_q * D + 16 * ks + 8 * h) * 2u;
     qop[ks] = __builtin_bit_cast(bf16x8, buf_load16(rq, off));
     doop[ks] = __builtin_bit_cast(bf16x8, buf_load16(rdo, off));
@@ -287,83 +350,116 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(BwdKParams p) {
     if (!p.causal) kv_hi = min(kv_hi, q_last + W);
   }
   const int t_lo = kv_lo / BC, t_hi = (kv_hi + BC - 1) / BC;
-
-  TileStage<D, BC, NT> stK, stV;
-  auto load_tile = [&](int t) {
-    stK.load(rk, t * BC, tid);
-    stV.load(rv, t * BC, tid);
-  };
-  auto store_tile = [&](int b) {
-    stK.store(smem[b][0], tid);
-    stV.store(smem[b][1], tid);
-  };
+  int hi_key = N - 1, lo_key = 0;
+  if (p.causal) hi_key = min(hi_key, my_q);
+  if (W > 0) {
+    lo_key = my_q - W + 1;
+    if (!p.causal) hi_key = min(hi_key, my_q + W - 1);
+  }
 
   f32x16 dqacc[D / 32];
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) dqacc[dt] = (f32x16){};
   const float s2 = p.scale * kLog2e;
   const TrCoord trc(lane);
-  if (t_lo < t_hi) {
-    load_tile(t_lo);
-    store_tile(0);
-  }
-  __syncthreads();
 
-  int buf = 0;
-  for (int t = t_lo; t < t_hi; ++t) {
-    const bool has_next = t + 1 < t_hi;
-    if (has_next) load_tile(t + 1);
-    const __bf16* Ks = smem[buf][0];
-    const __bf16* Vs = smem[buf][1];
-    const int kv0 = t * BC;
-    bool active = wq0 < N;
-    if (p.causal) active &= kv0 <= wq0 + 31;
-    if (W > 0) {
-      active &= wq0 - (kv0 + BC - 1) < W;
-      if (!p.causal) active &= kv0 - (wq0 + 31) < W;
+  auto sdp = [&](const __bf16* Ks, const __bf16* Vs, f32x16* sacc, f32x16* dpacc) {
+#pragma unroll
+    for (int mt = 0; mt < BC / 32; ++mt) {
+      sacc[mt] = dpacc[mt] = (f32x16){};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        sacc[mt] = mfma32(tile_row8<D>(Ks, 32 * mt + n, 2 * ks + h), qop[ks], sacc[mt]);
+        dpacc[mt] = mfma32(tile_row8<D>(Vs, 32 * mt + n, 2 * ks + h), doop[ks], dpacc[mt]);
+      }
     }
-    if (active) {
-      // S^T = K Q^T and dP^T = V dO^T (keys on M, this wave's queries on N).
-      f32x16 sacc[BC / 32], dpacc[BC / 32];
-#pragma unroll
-      for (int mt = 0; mt < BC / 32; ++mt) {
-        sacc[mt] = dpacc[mt] = (f32x16){};
-        const int r = 32 * mt + n;
-#pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks) {
-          sacc[mt] = mfma32(tile_row8<D>(Ks, r, 2 * ks + h), qop[ks], sacc[mt]);
-          dpacc[mt] = mfma32(tile_row8<D>(Vs, r, 2 * ks + h), doop[ks], dpacc[mt]);
-        }
-      }
-      bool need_mask = (kv0 + BC > N) || (wq0 + 32 > N);
-      if (p.causal) need_mask |= kv0 + BC - 1 > wq0;
-      if (W > 0) {
-        need_mask |= wq0 + 31 - kv0 >= W;
-        if (!p.causal) need_mask |= kv0 + BC - 1 - wq0 >= W;
-      }
-      bf16x8 dsop[BC / 16];
+  };
+
+  tile_load_lds<D, BC, NW>(rk, t_lo * BC, sK0, w, lane);
+  tile_load_lds<D, BC, NW>(rv, t_lo * BC, sV0, w, lane);
+  tile_load_lds<D, BC, NW>(rk, (t_lo + 1) * BC, sK1, w, lane);
+  tile_load_lds<D, BC, NW>(rv, (t_lo + 1) * BC, sV1, w, lane);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  f32x16 scur[BC / 32], dpcur[BC / 32];
+  sdp(sK0, sV0, scur, dpcur);
+
+  // Iteration for key tile t: P, dS^T of tile t and dQ^T += K_t^T dS_t^T
+  // (K_t in slot c), S^T, dP^T of tile t+1 (slot n); tile t+2 -> slot f.
+  auto iteration = [&](int t, const __bf16* Kc, const __bf16* Kn, const __bf16* Vn,
+                       __bf16* Kf, __bf16* Vf) {
+    tile_load_lds<D, BC, NW>(rk, (t + 2) * BC, Kf, w, lane);
+    tile_load_lds<D, BC, NW>(rv, (t + 2) * BC, Vf, w, lane);
+    const int kv0 = t * BC;
+    bool need_mask = (kv0 + BC > N) || (wq0 + 32 > N);
+    if (p.causal) need_mask |= kv0 + BC - 1 > wq0;
+    if (W > 0) {
+      need_mask |= wq0 + 31 - kv0 >= W;
+      if (!p.causal) need_mask |= kv0 + BC - 1 - wq0 >= W;
+    }
+    if (need_mask) {
 #pragma unroll
       for (int mt = 0; mt < BC / 32; ++mt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          float sv = sacc[mt][r];
-          if (need_mask) {
-            const int key = kv0 + 32 * mt + 8 * (r >> 2) + 4 * h + (r & 3);
-            if (!(q_ok && visible(my_q, key, N, p.causal, W))) sv = -__builtin_inff();
-          }
-          const float pv = fast_exp2(fmaf(sv, s2, -Lb));
-          dsop[2 * mt + (r >> 3)][r & 7] = (__bf16)(pv * (dpacc[mt][r] - Dl));
+          const int key = kv0 + 32 * mt + 8 * (r >> 2) + 4 * h + (r & 3);
+          scur[mt][r] = (key > hi_key || key < lo_key || !q_ok) ? -__builtin_inff()
+                                                                  : scur[mt][r];
         }
-      // dQ^T += K^T dS^T (d on M, queries on N, keys contracted).
-#pragma unroll
-      for (int kk = 0; kk < BC / 16; ++kk)
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt)
-          dqacc[dt] = mfma32(tile_a_tr<D>(Ks, trc, kk, dt), dsop[kk], dqacc[dt]);
     }
-    if (has_next) store_tile(buf ^ 1);
-    __syncthreads();
-    buf ^= 1;
+    constexpr int NS = 2 * (BC / 32) * KS;
+    constexpr int NP = (BC / 16) * (D / 32);
+    constexpr int EPB = (BC / 2) / NS;
+    constexpr int AHEAD = 4;
+    static_assert(EPB >= 1 && (BC / 2) % NS == 0, "bundle split");
+    auto arow = [&](int i) {
+      const int j = i >> 1, mt = j / KS, ks = j % KS;
+      return tile_row8<D>((i & 1) ? Vn : Kn, 32 * mt + n, 2 * ks + h);
+    };
+    auto atr = [&](int j) { return tile_a_tr<D>(Kc, trc, j / (D / 32), j % (D / 32)); };
+    f32x16 snext[BC / 32], dpnext[BC / 32];
+#pragma unroll
+    for (int mt = 0; mt < BC / 32; ++mt) snext[mt] = dpnext[mt] = (f32x16){};
+    bf16x8 aop[NS], top[NP], dsop[BC / 16];
+#pragma unroll
+    for (int i = 0; i < AHEAD; ++i) aop[i] = arow(i);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      if (i + AHEAD < NS) aop[i + AHEAD] = arow(i + AHEAD);
+      if (i >= NS - AHEAD) top[i - (NS - AHEAD)] = atr(i - (NS - AHEAD));
+      const int j = i >> 1, mt = j / KS, ks = j % KS;
+      if (i & 1)
+        dpnext[mt] = mfma32(aop[i], doop[ks], dpnext[mt]);
+      else
+        snext[mt] = mfma32(aop[i], qop[ks], snext[mt]);
+#pragma unroll
+      for (int u = 0; u < EPB; ++u) {
+        const int e = EPB * i + u, mt2 = e >> 4, r = e & 15;
+        const float pv = fast_exp2(fmaf(scur[mt2][r], s2, -Lb));
+        dsop[e >> 3][e & 7] = (__bf16)(pv * (dpcur[mt2][r] - Dl));
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int j = 0; j < NP; ++j) {
+      if (j + AHEAD < NP) top[j + AHEAD] = atr(j + AHEAD);
+      dqacc[j % (D / 32)] = mfma32(top[j], dsop[j / (D / 32)], dqacc[j % (D / 32)]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_s_barrier();
+#pragma unroll
+    for (int mt = 0; mt < BC / 32; ++mt) {
+      scur[mt] = snext[mt];
+      dpcur[mt] = dpnext[mt];
+    }
+  };
+
+  for (int t = t_lo; t < t_hi; t += 3) {
+    iteration(t, sK0, sK1, sV1, sK2, sV2);
+    if (t + 1 < t_hi) iteration(t + 1, sK1, sK2, sV2, sK0, sV0);
+    if (t + 2 < t_hi) iteration(t + 2, sK2, sK0, sV0, sK1, sV1);
   }
 
   if (q_ok) {
@@ -400,7 +496,7 @@ static BwdKParams bwd_params(const BwdArgs& a, int tile_rows) {
 }
 
 constexpr int kBwdWaves = 4;
-constexpr int kBwdTile = 64;  // query rows (dK/dV kernel) or keys (dQ kernel) per step
+constexpr int kBwdQTile = 64;  // query rows per step of the dK/dV kernel
 
 hipError_t launch_bwd_preprocess(const BwdArgs& a, hipStream_t stream) {
   const int rows = a.BH * a.N;
@@ -422,10 +518,10 @@ hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream) {
   const BwdKParams p = bwd_params(a, 32 * kBwdWaves);
   const dim3 grid((unsigned)(a.BH * p.n_tiles)), block(64 * kBwdWaves);
   if (a.d == 128)
-    hipLaunchKernelGGL((bwd_dkdv_kernel<128, kBwdWaves, kBwdTile>), grid, block, 0,
+    hipLaunchKernelGGL((bwd_dkdv_kernel<128, kBwdWaves, kBwdQTile>), grid, block, 0,
                        stream, p);
   else
-    hipLaunchKernelGGL((bwd_dkdv_kernel<64, kBwdWaves, kBwdTile>), grid, block, 0,
+    hipLaunchKernelGGL((bwd_dkdv_kernel<64, kBwdWaves, kBwdQTile>), grid, block, 0,
                        stream, p);
   return hipGetLastError();
 }
@@ -434,11 +530,9 @@ hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream) {
   const BwdKParams p = bwd_params(a, 32 * kBwdWaves);
   const dim3 grid((unsigned)(a.BH * p.n_tiles)), block(64 * kBwdWaves);
   if (a.d == 128)
-    hipLaunchKernelGGL((bwd_dq_kernel<128, kBwdWaves, kBwdTile>), grid, block, 0,
-                       stream, p);
+    hipLaunchKernelGGL((bwd_dq_kernel<128, kBwdWaves, 32>), grid, block, 0, stream, p);
   else
-    hipLaunchKernelGGL((bwd_dq_kernel<64, kBwdWaves, kBwdTile>), grid, block, 0,
-                       stream, p);
+    hipLaunchKernelGGL((bwd_dq_kernel<64, kBwdWaves, 64>), grid, block, 0, stream, p);
   return hipGetLastError();
 }
 

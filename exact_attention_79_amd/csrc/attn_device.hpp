@@ -182,6 +182,23 @@ __device__ __forceinline__ void tile_load_lds(__amdgpu_buffer_rsrc_t rs, int row
   }
 }
 
+// Global -> LDS copy of ROWS consecutive fp32 values (ROWS <= 64) by one
+// wave: lane L fetches element row0 + L into LDS word L.
+template <int ROWS>
+__device__ __forceinline__ void vec_load_lds(__amdgpu_buffer_rsrc_t rs, int row0,
+                                             float* t, int lane) {
+  static_assert(ROWS == 64, "one dword per lane of one wave");
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS_AS void*)t, 4,
+                                           (int)((uint32_t)(row0 + lane) * 4u), 0, 0,
+                                           0);
+}
+
+// s_waitcnt immediate that waits until at most `n` vector-memory operations
+// of this wave are outstanding (LDS and export counters not waited on).
+__host__ __device__ constexpr int waitcnt_vm(int n) {
+  return (n & 0xF) | (0x7 << 4) | (0xF << 8) | ((n >> 4) << 14);
+}
+
 // Global -> register -> LDS staging of a ROWS x D bf16 tile by NT threads:
 // thread tid moves chunks tid, tid + NT, ... (16 threads per 256-byte row,
 // so every global access is a full coalesced row segment).  Rows past the
