@@ -92,15 +92,16 @@ template <int D, int NW, int BQ>
 __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(BwdKParams p) {
   constexpr int BKV = 32 * NW;
   constexpr int KS = D / 16;
-  static_assert(BQ == 64, "one dword per lane stages L and D");
+  static_assert(BQ == 32 || BQ == 64, "query tile");
+  constexpr int LDROWS = 64;  // L and D are staged one dword per lane of a wave
   __shared__ __attribute__((aligned(16))) __bf16 sQ0[BQ * D];
   __shared__ __attribute__((aligned(16))) __bf16 sQ1[BQ * D];
   __shared__ __attribute__((aligned(16))) __bf16 sQ2[BQ * D];
   __shared__ __attribute__((aligned(16))) __bf16 sO0[BQ * D];
   __shared__ __attribute__((aligned(16))) __bf16 sO1[BQ * D];
   __shared__ __attribute__((aligned(16))) __bf16 sO2[BQ * D];
-  __shared__ __attribute__((aligned(16))) float sL0[BQ], sL1[BQ], sL2[BQ];
-  __shared__ __attribute__((aligned(16))) float sD0[BQ], sD1[BQ], sD2[BQ];
+  __shared__ __attribute__((aligned(16))) float sL0[LDROWS], sL1[LDROWS], sL2[LDROWS];
+  __shared__ __attribute__((aligned(16))) float sD0[LDROWS], sD1[LDROWS], sD2[LDROWS];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int h = lane >> 5, n = lane & 31;
@@ -151,8 +152,8 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(BwdKParams p) {
     tile_load_lds<D, BQ, NW>(rq, t * BQ, Qf, w, lane);
     tile_load_lds<D, BQ, NW>(rdo, t * BQ, Of, w, lane);
     if (w == 0) {
-      vec_load_lds<BQ>(rl, t * BQ, Lf, lane);
-      vec_load_lds<BQ>(rdl, t * BQ, Df, lane);
+      vec_load_lds<LDROWS>(rl, t * BQ, Lf, lane);
+      vec_load_lds<LDROWS>(rdl, t * BQ, Df, lane);
     }
   };
   // S = Q K^T and dP = dO V^T for one tile (queries on M, this wave's keys on N).
@@ -410,7 +411,7 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdKParams p) {
     constexpr int NS = 2 * (BC / 32) * KS;
     constexpr int NP = (BC / 16) * (D / 32);
     constexpr int EPB = (BC / 2) / NS;
-    constexpr int AHEAD = 4;
+    constexpr int AHEAD = 2;
     static_assert(EPB >= 1 && (BC / 2) % NS == 0, "bundle split");
     auto arow = [&](int i) {
       const int j = i >> 1, mt = j / KS, ks = j % KS;
