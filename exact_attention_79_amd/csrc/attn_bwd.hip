@@ -105,9 +105,10 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(BwdKParams p) {
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int h = lane >> 5, n = lane & 31;
-  const int logical = xcd_remap(blockIdx.x, gridDim.x);
-  const int bh = logical / p.n_tiles;
-  const int kt = logical % p.n_tiles;  // low key blocks see the most queries
+  // Low key blocks see the most queries under the causal mask: rank = block.
+  const TileId id = tile_order(blockIdx.x, gridDim.x / p.n_tiles, p.n_tiles, p.causal);
+  const int bh = id.bh;
+  const int kt = id.rank;
   const int N = p.N, W = p.window;
   const int k0 = kt * BKV;
   const int kw0 = k0 + 32 * w;
@@ -316,10 +317,9 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdKParams p) {
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int h = lane >> 5, n = lane & 31;
-  const int logical = xcd_remap(blockIdx.x, gridDim.x);
-  const int bh = logical / p.n_tiles;
-  int qt = logical % p.n_tiles;
-  if (p.causal) qt = p.n_tiles - 1 - qt;  // longest blocks first
+  const TileId id = tile_order(blockIdx.x, gridDim.x / p.n_tiles, p.n_tiles, p.causal);
+  const int bh = id.bh;
+  const int qt = p.causal ? p.n_tiles - 1 - id.rank : id.rank;  // longest first
   const int N = p.N, W = p.window;
   const int q0 = qt * BR;
   const int wq0 = q0 + 32 * w;

@@ -102,6 +102,25 @@ __device__ __forceinline__ int xcd_remap(int wg, int total) {
   return (xcd < r) ? xcd * (q + 1) + local : r * (q + 1) + (xcd - r) * q + local;
 }
 
+// Which (batch*head, tile rank) workgroup wg of a grid of BH * n_tiles
+// works on.  Whole heads stay on one XCD.  With rank_major (uneven work:
+// rank 0 is the heaviest tile of a head) each XCD walks its heads rank by
+// rank, so the longest workgroups of all its heads are dispatched before
+// any short one; otherwise it walks them head by head.  Rank-major needs
+// BH to be a multiple of 8; other grids fall back to head-major order.
+struct TileId {
+  int bh, rank;
+};
+__device__ __forceinline__ TileId tile_order(int wg, int BH, int n_tiles, bool rank_major) {
+  constexpr int kXcd = 8;
+  if (rank_major && BH % kXcd == 0) {
+    const int hpx = BH / kXcd, xcd = wg % kXcd, j = wg / kXcd;
+    return {xcd * hpx + j % hpx, j / hpx};
+  }
+  const int logical = xcd_remap(wg, BH * n_tiles);
+  return {logical / n_tiles, logical % n_tiles};
+}
+
 // ---- LDS tiles of bf16 rows (d elements each), swizzled in 16-byte chunks ----
 //
 // Two read patterns hit every tile:

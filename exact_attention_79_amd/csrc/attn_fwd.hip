@@ -68,10 +68,10 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdKParams p) {
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int h = lane >> 5, n = lane & 31;
-  const int logical = xcd_remap(blockIdx.x, gridDim.x);
-  const int bh = logical / p.n_qtiles;
-  int qt = logical % p.n_qtiles;
-  if (p.causal) qt = p.n_qtiles - 1 - qt;  // longest blocks first
+  // With the causal mask the last query blocks are the longest: run them first.
+  const TileId id = tile_order(blockIdx.x, gridDim.x / p.n_qtiles, p.n_qtiles, p.causal);
+  const int bh = id.bh;
+  const int qt = p.causal ? p.n_qtiles - 1 - id.rank : id.rank;
   const int N = p.N;
   const int q0 = qt * BR;
   const int wq0 = q0 + 32 * w;             // first query of this wave
@@ -128,53 +128,40 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdKParams p) {
     if (!p.causal) hi_key = min(hi_key, my_q + p.window - 1);
   }
 
-  // Prologue: K_0..K_2 and V_0, V_1 in flight (u = tile - t_lo), then S
-  // for the first tile.  Tiles past the last visible one may be loaded and
-  // scored: rows past N read as zeros and their scores are never used.
-  tile_load_lds<D, BC, NW>(rk, t_lo * BC, sK0, w, lane);
-  tile_load_lds<D, BC, NW>(rv, t_lo * BC, sV0, w, lane);
-  tile_load_lds<D, BC, NW>(rk, (t_lo + 1) * BC, sK1, w, lane);
-  tile_load_lds<D, BC, NW>(rv, (t_lo + 1) * BC, sV1, w, lane);
-  tile_load_lds<D, BC, NW>(rk, (t_lo + 2) * BC, sK2, w, lane);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  f32x16 scur[BC / 32];
-  scores(sK0, scur);
-
-  // vmcnt <= the loads issued by one iteration (lgkmcnt and expcnt free).
-  constexpr int kLoadsPerIter = 2 * (BC * D / 8) / (64 * NW);
-  constexpr int kWaitOlderLoads = (kLoadsPerIter & 0xF) | (0x7 << 4) | (0xF << 8) |
-                                  ((kLoadsPerIter >> 4) << 14);
-
-  // One iteration for tile t: it reads K_{t+1} from Kr and V_t from Vr, and
-  // refills Kf (K_t's slot) with K_{t+3} and Vf (V_{t-1}'s slot) with V_{t+2}.
-  auto iteration = [&](int t, const __bf16* Kr, const __bf16* Vr, __bf16* Kf,
-                       __bf16* Vf) {
-    tile_load_lds<D, BC, NW>(rk, (t + 3) * BC, Kf, w, lane);
-    tile_load_lds<D, BC, NW>(rv, (t + 2) * BC, Vf, w, lane);
-    // Mask only tiles that straddle a boundary of this wave (uniform test).
+  // Masks the scores of tile t element by element, but only when the tile
+  // straddles a boundary of this wave (a uniform test); returns whether it
+  // did.  Register r of M-tile mt holds key t*BC + 32mt + 8(r/4) + 4h + r%4.
+  auto mask_tile = [&](int t, f32x16* sacc) -> bool {
     const int kv0 = t * BC;
-    bool need_mask = kv0 + BC > N;
-    if (p.causal) need_mask |= kv0 + BC - 1 > wq0;
+    bool need = kv0 + BC > N;
+    if (p.causal) need |= kv0 + BC - 1 > wq0;
     if (p.window > 0) {
-      need_mask |= wq0 + 31 - kv0 >= p.window;
-      if (!p.causal) need_mask |= kv0 + BC - 1 - wq0 >= p.window;
+      need |= wq0 + 31 - kv0 >= p.window;
+      if (!p.causal) need |= kv0 + BC - 1 - wq0 >= p.window;
     }
-    if (need_mask) {
-#pragma unroll
-      for (int mt = 0; mt < BC / 32; ++mt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kv0 + 32 * mt + 8 * (r >> 2) + 4 * h + (r & 3);
-          scur[mt][r] = (key > hi_key || key < lo_key) ? -__builtin_inff() : scur[mt][r];
-        }
-    }
-    // Running max; the (rare) rescale is done before the main block.
-    float mx = -__builtin_inff();
+    if (!need) return false;
+    const int lim_hi = hi_key - kv0 - 4 * h, lim_lo = lo_key - kv0 - 4 * h;
 #pragma unroll
     for (int mt = 0; mt < BC / 32; ++mt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, scur[mt][r]);
+      for (int r = 0; r < 16; ++r) {
+        const int c = 32 * mt + 8 * (r >> 2) + (r & 3);
+        sacc[mt][r] = (c > lim_hi || c < lim_lo) ? -__builtin_inff() : sacc[mt][r];
+      }
+    return true;
+  };
+  auto tile_max = [&](const f32x16* sacc) {
+    float mx = sacc[0][0];
+#pragma unroll
+    for (int mt = 0; mt < BC / 32; ++mt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[mt][r]);
+    return mx;
+  };
+
+  // Moves the running max to cover a new tile whose in-lane max is mx (the
+  // max only moves when it grows by more than tau), rescaling O~ and l.
+  auto update_max = [&](float mx) {
     mx = halves_max(mx);
     const float m_new = (mx > m_run + tau) ? mx : m_run;
     const float alpha = fast_exp2((m_run - m_new) * s2);
@@ -184,19 +171,56 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdKParams p) {
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) oacc[dt] *= alpha;
     }
+  };
+
+  // Prologue: K_0..K_2 and V_0, V_1 in flight (u = tile - t_lo), then S
+  // and the running max for the first tile.  Tiles past the last visible
+  // one may be loaded and scored: rows past N read as zeros and their
+  // scores are never used.
+  tile_load_lds<D, BC, NW>(rk, t_lo * BC, sK0, w, lane);
+  tile_load_lds<D, BC, NW>(rv, t_lo * BC, sV0, w, lane);
+  tile_load_lds<D, BC, NW>(rk, (t_lo + 1) * BC, sK1, w, lane);
+  tile_load_lds<D, BC, NW>(rv, (t_lo + 1) * BC, sV1, w, lane);
+  tile_load_lds<D, BC, NW>(rk, (t_lo + 2) * BC, sK2, w, lane);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  f32x16 scur[BC / 32];
+  scores(sK0, scur);
+  mask_tile(t_lo, scur);
+  update_max(tile_max(scur));
+
+  // vmcnt <= the loads issued by one iteration (lgkmcnt and expcnt free).
+  constexpr int kLoadsPerIter = 2 * (BC * D / 8) / (64 * NW);
+  constexpr int kWaitOlderLoads = (kLoadsPerIter & 0xF) | (0x7 << 4) | (0xF << 8) |
+                                  ((kLoadsPerIter >> 4) << 14);
+
+  // One iteration for tile t, whose scores (masked) are in scur and whose
+  // running max is already in m_run: it reads K_{t+1} from Kr and V_t from
+  // Vr, and refills Kf (K_t's slot) with K_{t+3} and Vf (V_{t-1}'s slot)
+  // with V_{t+2}.  It leaves S_{t+1} (masked) in scur and its max in m_run.
+  auto iteration = [&](int t, const __bf16* Kr, const __bf16* Vr, __bf16* Kf,
+                       __bf16* Vf) {
+    tile_load_lds<D, BC, NW>(rk, (t + 3) * BC, Kf, w, lane);
+    tile_load_lds<D, BC, NW>(rv, (t + 2) * BC, Vf, w, lane);
     const float mb = m_run * s2;
 
     // Main block, scheduled by hand in bundles that the compiler may not
-    // reorder across (sched_barrier): each bundle issues one MFMA, the LDS
-    // read for the MFMA four bundles later, and a slice of the softmax, so
-    // LDS latency is covered and the VALU work sits between MFMAs.
+    // reorder across (sched_barrier): each bundle issues one MFMA and the
+    // LDS read for the MFMA AHEAD bundles later.
     // Bundles 0..NS-1: the next tile's score MFMAs + this tile's exps;
-    // bundles NS..NS+NP-1: this tile's P V MFMAs.
+    // bundles NS..NS+NP-1: this tile's P V MFMAs + slices of the next
+    // tile's row max (once its score MFMAs have drained).  A tile that
+    // needs the mask has its max taken again after masking (rare).
     constexpr int KS = D / 16;                 // K-steps per score tile
     constexpr int NS = (BC / 32) * KS;         // score MFMAs
     constexpr int NP = (BC / 16) * (D / 32);   // P V MFMAs
     constexpr int EPB = BC / 2 / NS;           // exps per lane per bundle
     constexpr int AHEAD = 4;
+    constexpr int NV = BC / 2;                 // scores per lane per tile
+    constexpr int J0 = 2;                      // first PV bundle with max work
+    constexpr int NCH = NP - J0;               // max slices
+    constexpr int CH = (NV + NCH - 1) / NCH;   // scores per slice
+    static_assert(NCH >= 1 && CH * NCH >= NV, "max slices");
     const __bf16* Kn = Kr;
     const __bf16* Vs = Vr;
     auto kread = [&](int i) {
@@ -225,13 +249,34 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdKParams p) {
       }
       __builtin_amdgcn_sched_barrier(0);
     }
+    float part[NCH];
 #pragma unroll
     for (int j = 0; j < NP; ++j) {
       if (j + AHEAD < NP) va[j + AHEAD] = vread(j + AHEAD);
       oacc[j % (D / 32)] = mfma32(va[j], pop[j / (D / 32)], oacc[j % (D / 32)]);
+      if (j >= J0) {
+        const int c = j - J0;
+        float mx = snext[(c * CH) >> 4][(c * CH) & 15];
+#pragma unroll
+        for (int u = 1; u < CH; ++u) {
+          const int e = c * CH + u;
+          if (e < NV) mx = fmaxf(mx, snext[e >> 4][e & 15]);
+        }
+        // Pin the slice here: it is only read after the loop, and the
+        // compiler would otherwise sink it there, out of the bundles.
+        asm volatile("" ::"v"(mx));
+        part[c] = mx;
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
     l_run += lsum;
+    if (t + 1 < t_hi) {
+      float mx = part[0];
+#pragma unroll
+      for (int c = 1; c < NCH; ++c) mx = fmaxf(mx, part[c]);
+      if (mask_tile(t + 1, snext)) mx = tile_max(snext);
+      update_max(mx);
+    }
 
     // The loads issued one iteration ago (K_{t+2}, V_{t+1}) have landed for
     // this wave; after the barrier they have for every wave, and the slots

@@ -114,10 +114,9 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8_kernel(FwdFp8Params p) {
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int h = lane >> 5, n = lane & 31;
-  const int logical = xcd_remap(blockIdx.x, gridDim.x);
-  const int bh = logical / p.n_qtiles;
-  int qt = logical % p.n_qtiles;
-  if (p.causal) qt = p.n_qtiles - 1 - qt;
+  const TileId id = tile_order(blockIdx.x, gridDim.x / p.n_qtiles, p.n_qtiles, p.causal);
+  const int bh = id.bh;
+  const int qt = p.causal ? p.n_qtiles - 1 - id.rank : id.rank;  // longest first
   const int N = p.N;
   const int q0 = qt * BR;
   const int wq0 = q0 + 32 * w;
