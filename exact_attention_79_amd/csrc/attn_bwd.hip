@@ -203,7 +203,9 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(BwdKParams p) {
         }
     }
     // L and D of the query rows this lane holds, four rows (one group g) at
-    // a time: group g covers rows 32 (g / 4) + 8 (g % 4) + 4h + 0..3.
+    // a time: group g covers rows 32 (g / 4) + 8 (g % 4) + 4h + 0..3.  They
+    // are read two groups before use and scaled only where used, so that
+    // waiting for them never drains the operand reads queued behind them.
     auto lrow = [&](int g) { return *(const f32x4*)&Lc[32 * (g >> 2) + 8 * (g & 3) + 4 * h]; };
     auto drow = [&](int g) { return *(const f32x4*)&Dc[32 * (g >> 2) + 8 * (g & 3) + 4 * h]; };
     f32x4 lb[BQ / 8], dl[BQ / 8];
@@ -229,18 +231,22 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(BwdKParams p) {
     for (int mt = 0; mt < BQ / 32; ++mt) snext[mt] = dpnext[mt] = (f32x16){};
     bf16x8 aop[NS], top[NP], pop[BQ / 16], dsop[BQ / 16];
     constexpr int GB = 4 / EPB;  // bundles per 4-row group
+    constexpr int LDA = 2;  // groups of L, D in flight ahead of their use
+#pragma unroll
+    for (int g = 0; g < LDA && g < BQ / 8; ++g) {
+      lb[g] = lrow(g);
+      dl[g] = drow(g);
+    }
 #pragma unroll
     for (int i = 0; i < AHEAD; ++i) aop[i] = arow(i);
-    lb[0] = lrow(0) * kLog2e;
-    dl[0] = drow(0);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
       if (i + AHEAD < NS) aop[i + AHEAD] = arow(i + AHEAD);
       if (i >= NS - AHEAD) top[i - (NS - AHEAD)] = atr(i - (NS - AHEAD));
-      if (i % GB == 0 && i / GB + 1 < BQ / 8) {  // next group's L, D one group ahead
-        lb[i / GB + 1] = lrow(i / GB + 1) * kLog2e;
-        dl[i / GB + 1] = drow(i / GB + 1);
+      if (i % GB == 0 && i / GB + LDA < BQ / 8) {
+        lb[i / GB + LDA] = lrow(i / GB + LDA);
+        dl[i / GB + LDA] = drow(i / GB + LDA);
       }
       const int j = i >> 1, mt = j / KS, ks = j % KS;
       if (i & 1)
@@ -250,7 +256,7 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(BwdKParams p) {
 #pragma unroll
       for (int u = 0; u < EPB; ++u) {
         const int e = EPB * i + u, mt2 = e >> 4, r = e & 15, g = 4 * mt2 + (r >> 2);
-        const float pv = fast_exp2(fmaf(scur[mt2][r], s2, -lb[g][r & 3]));
+        const float pv = fast_exp2(fmaf(scur[mt2][r], s2, -lb[g][r & 3] * kLog2e));
         const float ds = pv * (dpcur[mt2][r] - dl[g][r & 3]);
         pop[e >> 3][e & 7] = (__bf16)pv;
         dsop[e >> 3][e & 7] = (__bf16)ds;
