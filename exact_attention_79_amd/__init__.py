@@ -53,12 +53,12 @@ def _load():
     L.attn_bwd_workspace_bytes.restype = sz
     L.attn_bwd.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.attn_bwd.restype = ctypes.c_int
-    L.attn_bwd_preprocess.argtypes = [dp, vp, vp, vp, sz, vp]
+    L.attn_bwd_preprocess.argtypes = [dp, vp, vp, vp, vp, sz, vp]
     L.attn_bwd_preprocess.restype = ctypes.c_int
-    L.attn_bwd_dkdv.argtypes = [dp, vp, vp, vp, vp, vp, vp, sz, vp, vp, vp]
-    L.attn_bwd_dkdv.restype = ctypes.c_int
-    L.attn_bwd_dq.argtypes = [dp, vp, vp, vp, vp, vp, vp, sz, vp, vp]
+    L.attn_bwd_dq.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp]
     L.attn_bwd_dq.restype = ctypes.c_int
+    L.attn_bwd_dkdv.argtypes = [dp, vp, vp, vp, vp, vp, sz, vp, vp, vp]
+    L.attn_bwd_dkdv.restype = ctypes.c_int
     L.attn_fwd_fp8.argtypes = [dp, vp, vp, vp, f32, f32, f32, vp, i32, vp, vp]
     L.attn_fwd_fp8.restype = ctypes.c_int
     L.attn_status_str.argtypes = [ctypes.c_int]
@@ -175,47 +175,52 @@ def _check_lse_ws(q, lse, workspace, desc):
         raise ValueError(f"workspace must be a device tensor of >= {need} bytes")
 
 
-def attn_bwd_preprocess(o, dout, workspace, scale=None, causal=False, window=0):
-    """Stage 1 of the backward: workspace <- D = rowsum(dO * O)."""
+def _ws_bytes(workspace):
+    return workspace.numel() * workspace.element_size()
+
+
+def attn_bwd_preprocess(o, dout, lse, workspace, scale=None, causal=False, window=0):
+    """Fills the workspace only: D = rowsum(dO * O) and L log2(e)."""
     _check_like(o, torch.bfloat16, o=o, dout=dout)
     desc = _bwd_desc(o, scale, causal, window)
-    _check_lse_ws(o, None, workspace, desc)
-    _check(lib.attn_bwd_preprocess(ctypes.byref(desc), _ptr(o), _ptr(dout),
-                                   _ptr(workspace),
-                                   workspace.numel() * workspace.element_size(),
-                                   _stream()), "attn_bwd_preprocess")
+    _check_lse_ws(o, lse, workspace, desc)
+    _check(lib.attn_bwd_preprocess(ctypes.byref(desc), _ptr(o), _ptr(dout), _ptr(lse),
+                                   _ptr(workspace), _ws_bytes(workspace), _stream()),
+           "attn_bwd_preprocess")
 
 
-def attn_bwd_dkdv(q, k, v, dout, lse, workspace, dk, dv, scale=None, causal=False,
-                  window=0):
-    """Stage 2 of the backward: dK and dV (fp32), using D from stage 1."""
-    _check_like(q, torch.bfloat16, q=q, k=k, v=v, dout=dout)
-    _check_like(q, torch.float32, dk=dk, dv=dv)
-    desc = _bwd_desc(q, scale, causal, window)
-    _check_lse_ws(q, lse, workspace, desc)
-    _check(lib.attn_bwd_dkdv(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(dout),
-                             _ptr(lse), _ptr(workspace),
-                             workspace.numel() * workspace.element_size(), _ptr(dk),
-                             _ptr(dv), _stream()), "attn_bwd_dkdv")
-
-
-def attn_bwd_dq(q, k, v, dout, lse, workspace, dq, scale=None, causal=False,
+def attn_bwd_dq(q, k, v, o, dout, lse, workspace, dq, scale=None, causal=False,
                 window=0):
-    """Stage 3 of the backward: dQ (fp32), using D from stage 1."""
-    _check_like(q, torch.bfloat16, q=q, k=k, v=v, dout=dout)
+    """First backward stage: dQ (fp32); also fills the workspace (D, L log2(e))."""
+    _check_like(q, torch.bfloat16, q=q, k=k, v=v, o=o, dout=dout)
     _check_like(q, torch.float32, dq=dq)
     desc = _bwd_desc(q, scale, causal, window)
     _check_lse_ws(q, lse, workspace, desc)
-    _check(lib.attn_bwd_dq(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(dout),
-                           _ptr(lse), _ptr(workspace),
-                           workspace.numel() * workspace.element_size(), _ptr(dq),
-                           _stream()), "attn_bwd_dq")
+    _check(lib.attn_bwd_dq(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
+                           _ptr(dout), _ptr(lse), _ptr(workspace), _ws_bytes(workspace),
+                           _ptr(dq), _stream()), "attn_bwd_dq")
+
+
+def attn_bwd_dkdv(q, k, v, dout, workspace, dk, dv, scale=None, causal=False,
+                  window=0):
+    """Second backward stage: dK and dV (fp32), from the workspace that
+    attn_bwd_dq (or attn_bwd_preprocess) filled."""
+    _check_like(q, torch.bfloat16, q=q, k=k, v=v, dout=dout)
+    _check_like(q, torch.float32, dk=dk, dv=dv)
+    desc = _bwd_desc(q, scale, causal, window)
+    _check_lse_ws(q, None, workspace, desc)
+    _check(lib.attn_bwd_dkdv(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(dout),
+                             _ptr(workspace), _ws_bytes(workspace), _ptr(dk), _ptr(dv),
+                             _stream()), "attn_bwd_dkdv")
 
 
 def attn_bwd_stages(q, k, v, o, dout, lse, scale: float | None = None,
                     causal: bool = False, window: int = 0, workspace=None,
-                    grads=None):
-    """The same result as attn_bwd, issued as its three stages."""
+                    grads=None, preprocess: bool = False):
+    """The result of attn_bwd, issued stage by stage: attn_bwd_dq, then
+    attn_bwd_dkdv (exactly what attn_bwd enqueues).  With preprocess=True:
+    attn_bwd_preprocess, attn_bwd_dkdv, then attn_bwd_dq, so that dK and dV
+    come from the workspace the preprocess filled."""
     desc = _bwd_desc(q, scale, causal, window)
     if workspace is None:
         nbytes = int(lib.attn_bwd_workspace_bytes(ctypes.byref(desc)))
@@ -225,9 +230,13 @@ def attn_bwd_stages(q, k, v, o, dout, lse, scale: float | None = None,
                       for _ in range(3))
     dq, dk, dv = grads
     kw = dict(scale=scale, causal=causal, window=window)
-    attn_bwd_preprocess(o, dout, workspace, **kw)
-    attn_bwd_dkdv(q, k, v, dout, lse, workspace, dk, dv, **kw)
-    attn_bwd_dq(q, k, v, dout, lse, workspace, dq, **kw)
+    if preprocess:
+        attn_bwd_preprocess(o, dout, lse, workspace, **kw)
+        attn_bwd_dkdv(q, k, v, dout, workspace, dk, dv, **kw)
+        attn_bwd_dq(q, k, v, o, dout, lse, workspace, dq, **kw)
+    else:
+        attn_bwd_dq(q, k, v, o, dout, lse, workspace, dq, **kw)
+        attn_bwd_dkdv(q, k, v, dout, workspace, dk, dv, **kw)
     return dq, dk, dv
 
 

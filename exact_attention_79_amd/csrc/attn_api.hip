@@ -53,6 +53,12 @@ attn::FwdArgs fwd_args(const attn_desc* d, const void* q, const void* k,
   return a;
 }
 
+// One fp32 [B,H,N] array of the workspace, padded to 256 bytes.
+size_t ws_array_bytes(const attn_desc* d) {
+  const size_t rows = (size_t)d->B * d->H * d->N;
+  return (rows * sizeof(float) + 255) & ~(size_t)255;
+}
+
 attn::BwdArgs bwd_args(const attn_desc* d, const void* q, const void* k,
                       const void* v, const void* o, const void* dout,
                       const float* lse, float* dq, float* dk, float* dv,
@@ -68,6 +74,7 @@ attn::BwdArgs bwd_args(const attn_desc* d, const void* q, const void* k,
   a.dk = dk;
   a.dv = dv;
   a.delta = (float*)workspace;
+  a.lse2 = (float*)((char*)workspace + ws_array_bytes(d));
   a.BH = d->B * d->H;
   a.N = d->N;
   a.d = d->d;
@@ -95,8 +102,7 @@ attn_status attn_fwd(const attn_desc* desc, const void* q, const void* k,
 
 size_t attn_bwd_workspace_bytes(const attn_desc* desc) {
   if (check_desc(desc) != ATTN_OK) return 0;
-  const size_t rows = (size_t)desc->B * desc->H * desc->N;
-  return (rows * sizeof(float) + 255) & ~(size_t)255;
+  return 2 * ws_array_bytes(desc);  // D, then L log2(e)
 }
 
 attn_status attn_bwd(const attn_desc* desc, const void* q, const void* k,
@@ -114,45 +120,43 @@ attn_status attn_bwd(const attn_desc* desc, const void* q, const void* k,
 }
 
 attn_status attn_bwd_preprocess(const attn_desc* desc, const void* o,
-                                const void* dout, void* workspace,
+                                const void* dout, const float* lse, void* workspace,
                                 size_t workspace_bytes, void* stream) {
   attn_status st = check_desc(desc);
   if (st != ATTN_OK) return st;
-  st = check_ptrs({o, dout, workspace}, {});
+  st = check_ptrs({o, dout, lse, workspace}, {});
   if (st != ATTN_OK) return st;
   if (workspace_bytes < attn_bwd_workspace_bytes(desc)) return ATTN_EINVAL;
   return from_hip(attn::launch_bwd_preprocess(
-      bwd_args(desc, nullptr, nullptr, nullptr, o, dout, nullptr, nullptr, nullptr,
+      bwd_args(desc, nullptr, nullptr, nullptr, o, dout, lse, nullptr, nullptr,
                nullptr, workspace),
       (hipStream_t)stream));
 }
 
-attn_status attn_bwd_dkdv(const attn_desc* desc, const void* q, const void* k,
-                          const void* v, const void* dout, const float* lse,
-                          const void* workspace, size_t workspace_bytes,
-                          float* dk, float* dv, void* stream) {
-  attn_status st = check_desc(desc);
-  if (st != ATTN_OK) return st;
-  st = check_ptrs({q, k, v, dout, lse, workspace, dk, dv}, {});
-  if (st != ATTN_OK) return st;
-  if (workspace_bytes < attn_bwd_workspace_bytes(desc)) return ATTN_EINVAL;
-  return from_hip(attn::launch_bwd_dkdv(
-      bwd_args(desc, q, k, v, nullptr, dout, lse, nullptr, dk, dv,
-               (void*)workspace),
-      (hipStream_t)stream));
-}
-
 attn_status attn_bwd_dq(const attn_desc* desc, const void* q, const void* k,
-                        const void* v, const void* dout, const float* lse,
-                        const void* workspace, size_t workspace_bytes, float* dq,
-                        void* stream) {
+                        const void* v, const void* o, const void* dout,
+                        const float* lse, void* workspace, size_t workspace_bytes,
+                        float* dq, void* stream) {
   attn_status st = check_desc(desc);
   if (st != ATTN_OK) return st;
-  st = check_ptrs({q, k, v, dout, lse, workspace, dq}, {});
+  st = check_ptrs({q, k, v, o, dout, lse, workspace, dq}, {});
   if (st != ATTN_OK) return st;
   if (workspace_bytes < attn_bwd_workspace_bytes(desc)) return ATTN_EINVAL;
   return from_hip(attn::launch_bwd_dq(
-      bwd_args(desc, q, k, v, nullptr, dout, lse, dq, nullptr, nullptr,
+      bwd_args(desc, q, k, v, o, dout, lse, dq, nullptr, nullptr, workspace),
+      (hipStream_t)stream));
+}
+
+attn_status attn_bwd_dkdv(const attn_desc* desc, const void* q, const void* k,
+                          const void* v, const void* dout, const void* workspace,
+                          size_t workspace_bytes, float* dk, float* dv, void* stream) {
+  attn_status st = check_desc(desc);
+  if (st != ATTN_OK) return st;
+  st = check_ptrs({q, k, v, dout, workspace, dk, dv}, {});
+  if (st != ATTN_OK) return st;
+  if (workspace_bytes < attn_bwd_workspace_bytes(desc)) return ATTN_EINVAL;
+  return from_hip(attn::launch_bwd_dkdv(
+      bwd_args(desc, q, k, v, nullptr, dout, nullptr, nullptr, dk, dv,
                (void*)workspace),
       (hipStream_t)stream));
 }

@@ -8,15 +8,18 @@
 // dS_ij = P_ij (dP_ij - D_i) with D_i = sum_k dO_ik O_ik, and the scale s of
 // S = s Q K^T gives dQ = s dS K and dK = s dS^T Q.
 //
-// Three launches on the caller's stream:
-//  1. bwd_delta_kernel: D = rowsum(dO * O) (memory-bound, one pass);
+// Two launches on the caller's stream:
+//  1. bwd_dq_kernel: one workgroup per query block, Q_i, dO_i, L_i, D_i
+//     resident, looping over the K/V blocks it sees; dQ_i accumulates in
+//     VGPRs and is written once.  Each lane owns one query row, so it forms
+//     D_i = rowsum(dO_i * O_i) itself (one read of O_i) and also leaves D_i
+//     and L_i log2(e) in the workspace for the second launch;
 //  2. bwd_dkdv_kernel: one workgroup per K/V block (the page's column-block
 //     partition of the backward), K_j and V_j resident in VGPRs, looping over
 //     the query blocks that can see them; dK_j and dV_j accumulate in VGPRs
-//     and are written once;
-//  3. bwd_dq_kernel: one workgroup per query block, Q_i, dO_i, L_i, D_i
-//     resident, looping over the K/V blocks it sees; dQ_i accumulates in
-//     VGPRs and is written once.
+//     and are written once.
+// bwd_delta_kernel writes the same two workspace arrays on its own (for
+// callers that run the dK/dV pass without the dQ pass).
 // Splitting dQ into its own pass recomputes S and dP there (two extra
 // products per visible tile) but needs no atomics and no zeroed buffer, and
 // the result is deterministic.
@@ -43,11 +46,13 @@ __device__ __forceinline__ float bf16_hi(uint32_t x) {
   return __builtin_bit_cast(float, x & 0xffff0000u);
 }
 
-// D_i = sum_k dO_ik O_ik over rows of d elements; D/8 threads per row.
+// D_i = sum_k dO_ik O_ik over rows of d elements (D/8 threads per row), and
+// L_i log2(e), the base-2 form of the log-sum-exp the other kernels use.
 template <int D>
 __global__ __launch_bounds__(256) void bwd_delta_kernel(const __bf16* o,
                                                         const __bf16* dout,
-                                                        float* delta, int rows) {
+                                                        const float* lse, float* delta,
+                                                        float* lse2, int rows) {
   constexpr int TPR = D / 8;
   const int tid = threadIdx.x;
   const int r = blockIdx.x * (256 / TPR) + tid / TPR;
@@ -62,16 +67,21 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(const __bf16* o,
   }
 #pragma unroll
   for (int off = TPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
-  if (r < rows && c == 0) delta[r] = acc;
+  if (r < rows && c == 0) {
+    delta[r] = acc;
+    lse2[r] = lse[r] * kLog2e;
+  }
 }
 
 struct BwdKParams {
   const __bf16* q;
   const __bf16* k;
   const __bf16* v;
+  const __bf16* o;
   const __bf16* dout;
-  const float* lse;
-  const float* delta;
+  const float* lse;  // natural-log L from the forward (dQ kernel)
+  float* delta;      // workspace: D_i
+  float* lse2;       // workspace: L_i log2(e)
   float* dq;
   float* dk;
   float* dv;
@@ -119,7 +129,7 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(BwdKParams p) {
   const auto rk = make_rsrc(p.k + head, head_bytes);
   const auto rv = make_rsrc(p.v + head, head_bytes);
   const auto rdo = make_rsrc(p.dout + head, head_bytes);
-  const auto rl = make_rsrc(p.lse + (size_t)bh * N, (uint32_t)N * 4);
+  const auto rl = make_rsrc(p.lse2 + (size_t)bh * N, (uint32_t)N * 4);
   const auto rdl = make_rsrc(p.delta + (size_t)bh * N, (uint32_t)N * 4);
 
   // K^T and V^T as B operands (lane = key, 8 consecutive d per K-step).
@@ -202,10 +212,10 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(BwdKParams p) {
           scur[mt][r] = (q < qmin || q > qmax) ? -__builtin_inff() : scur[mt][r];
         }
     }
-    // L and D of the query rows this lane holds, four rows (one group g) at
-    // a time: group g covers rows 32 (g / 4) + 8 (g % 4) + 4h + 0..3.  They
-    // are read two groups before use and scaled only where used, so that
-    // waiting for them never drains the operand reads queued behind them.
+    // L log2(e) and D of the query rows this lane holds, four rows (one
+    // group g) at a time: group g covers rows 32 (g / 4) + 8 (g % 4) + 4h +
+    // 0..3.  They are read two groups before use, so that waiting for them
+    // never drains the operand reads queued behind them.
     auto lrow = [&](int g) { return *(const f32x4*)&Lc[32 * (g >> 2) + 8 * (g & 3) + 4 * h]; };
     auto drow = [&](int g) { return *(const f32x4*)&Dc[32 * (g >> 2) + 8 * (g & 3) + 4 * h]; };
     f32x4 lb[BQ / 8], dl[BQ / 8];
@@ -256,7 +266,7 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(BwdKParams p) {
 #pragma unroll
       for (int u = 0; u < EPB; ++u) {
         const int e = EPB * i + u, mt2 = e >> 4, r = e & 15, g = 4 * mt2 + (r >> 2);
-        const float pv = fast_exp2(fmaf(scur[mt2][r], s2, -lb[g][r & 3] * kLog2e));
+        const float pv = fast_exp2(fmaf(scur[mt2][r], s2, -lb[g][r & 3]));
         const float ds = pv * (dpcur[mt2][r] - dl[g][r & 3]);
         pop[e >> 3][e & 7] = (__bf16)pv;
         dsop[e >> 3][e & 7] = (__bf16)ds;
@@ -336,18 +346,30 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdKParams p) {
   const auto rk = make_rsrc(p.k + head, head_bytes);
   const auto rv = make_rsrc(p.v + head, head_bytes);
   const auto rdo = make_rsrc(p.dout + head, head_bytes);
+  const auto ro = make_rsrc(p.o + head, head_bytes);
 
-  // Q^T and dO^T as B operands (lane = query), L and D per lane.
+  // Q^T and dO^T as B operands (lane = query): this lane holds d = 16ks +
+  // 8h .. +7 of its query for every K-step ks, and the same slice of O_i
+  // for its half of D_i = sum_k dO_ik O_ik.
   bf16x8 qop[KS], doop[KS];
+  float dpart = 0.f;
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
     const uint32_t off = (uint32_t)(my_q * D + 16 * ks + 8 * h) * 2u;
     qop[ks] = __builtin_bit_cast(bf16x8, buf_load16(rq, off));
     doop[ks] = __builtin_bit_cast(bf16x8, buf_load16(rdo, off));
+    const bf16x8 ov = __builtin_bit_cast(bf16x8, buf_load16(ro, off));
+#pragma unroll
+    for (int e = 0; e < 8; ++e) dpart = fmaf((float)doop[ks][e], (float)ov[e], dpart);
   }
   const bool q_ok = my_q < N;
   const float Lb = q_ok ? p.lse[(size_t)bh * N + my_q] * kLog2e : 0.f;
-  const float Dl = q_ok ? p.delta[(size_t)bh * N + my_q] : 0.f;
+  const float Dl = halves_sum(dpart);
+  // Leave D_i and L_i log2(e) for the dK/dV pass.
+  if (q_ok && h == 0) {
+    p.delta[(size_t)bh * N + my_q] = Dl;
+    p.lse2[(size_t)bh * N + my_q] = Lb;
+  }
 
   const int q_last = min(q0 + BR, N) - 1;
   int kv_lo = 0, kv_hi = N;
@@ -488,9 +510,11 @@ static BwdKParams bwd_params(const BwdArgs& a, int tile_rows) {
   p.q = (const __bf16*)a.q;
   p.k = (const __bf16*)a.k;
   p.v = (const __bf16*)a.v;
+  p.o = (const __bf16*)a.o;
   p.dout = (const __bf16*)a.dout;
   p.lse = a.lse;
   p.delta = a.delta;
+  p.lse2 = a.lse2;
   p.dq = a.dq;
   p.dk = a.dk;
   p.dv = a.dv;
@@ -511,12 +535,12 @@ hipError_t launch_bwd_preprocess(const BwdArgs& a, hipStream_t stream) {
     constexpr int RPB = 256 / 16;
     hipLaunchKernelGGL((bwd_delta_kernel<128>), dim3((rows + RPB - 1) / RPB),
                        dim3(256), 0, stream, (const __bf16*)a.o,
-                       (const __bf16*)a.dout, a.delta, rows);
+                       (const __bf16*)a.dout, a.lse, a.delta, a.lse2, rows);
   } else {
     constexpr int RPB = 256 / 8;
     hipLaunchKernelGGL((bwd_delta_kernel<64>), dim3((rows + RPB - 1) / RPB),
                        dim3(256), 0, stream, (const __bf16*)a.o,
-                       (const __bf16*)a.dout, a.delta, rows);
+                       (const __bf16*)a.dout, a.lse, a.delta, a.lse2, rows);
   }
   return hipGetLastError();
 }
@@ -544,9 +568,8 @@ hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream) {
 }
 
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
-  hipError_t e = launch_bwd_preprocess(a, stream);
+  hipError_t e = launch_bwd_dq(a, stream);
   if (e == hipSuccess) e = launch_bwd_dkdv(a, stream);
-  if (e == hipSuccess) e = launch_bwd_dq(a, stream);
   return e;
 }
 

@@ -31,6 +31,7 @@ struct BwdArgs {
   float* dk;
   float* dv;
   float* delta;        // fp32 [BH][N] workspace: D_i = sum_k dO_ik O_ik
+  float* lse2;         // fp32 [BH][N] workspace: L_i log2(e)
   int BH, N, d;
   float scale;
   int causal, window;
@@ -38,7 +39,8 @@ struct BwdArgs {
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_fwd_fp8(const FwdArgs& a, hipStream_t stream);
-// The three backward stages; launch_bwd = preprocess, dkdv, dq in order.
+// The backward stages; launch_bwd = dq (which also fills the workspace),
+// then dkdv.  preprocess fills the workspace on its own.
 hipError_t launch_bwd_preprocess(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream);

@@ -84,8 +84,9 @@ attn_status attn_fwd(const attn_desc* desc, const void* q, const void* k,
                      const void* v, void* o, int32_t o_dtype, float* lse,
                      void* stream);
 
-/* Bytes of device workspace attn_bwd needs for `desc` (D = rowsum(dO * O),
- * fp32 [B,H,N], rounded up to 256 bytes). */
+/* Bytes of device workspace the backward needs for `desc`: two fp32 [B,H,N]
+ * arrays, D_i = sum_k dO_ik O_ik and L_i log2(e), each padded to a multiple
+ * of 256 bytes.  0 if `desc` is invalid. */
 size_t attn_bwd_workspace_bytes(const attn_desc* desc);
 
 /* Backward (FLASH-ATTN page, FlashAttention-2 summary "Background": dV = P^T dO,
@@ -102,27 +103,31 @@ attn_status attn_bwd(const attn_desc* desc, const void* q, const void* k,
                      const float* lse, float* dq, float* dk, float* dv,
                      void* workspace, size_t workspace_bytes, void* stream);
 
-/* The backward as three separately launchable stages.  attn_bwd enqueues
- * exactly these three, in this order, on one stream; a caller may issue them
- * itself (for example to time or overlap them).  Argument rules as attn_bwd.
- *   attn_bwd_preprocess: workspace <- D_i = sum_k dO_ik O_ik   (fp32 [B,H,N])
+/* The backward as separately launchable stages.  attn_bwd enqueues
+ * attn_bwd_dq and then attn_bwd_dkdv on one stream; a caller may issue them
+ * itself (for example to time them).  Argument rules as attn_bwd.
+ *   attn_bwd_dq:         dQ = s dS K, one pass per query block over the K/V
+ *                        blocks it sees (S and dP are recomputed there).  It
+ *                        forms D_i = sum_k dO_ik O_ik of its own rows and
+ *                        also writes D and L log2(e) to the workspace.
  *   attn_bwd_dkdv:       dK = s dS^T Q and dV = P^T dO, one pass per K/V block
  *                        over the query blocks that see it (the FLASH-ATTN
- *                        page's column-block partition of the backward)
- *   attn_bwd_dq:         dQ = s dS K, one pass per query block over the K/V
- *                        blocks it sees (S and dP are recomputed there)
- * dkdv and dq read D from the workspace written by the preprocess. */
-attn_status attn_bwd_preprocess(const attn_desc* desc, const void* o,
-                                const void* dout, void* workspace,
-                                size_t workspace_bytes, void* stream);
-attn_status attn_bwd_dkdv(const attn_desc* desc, const void* q, const void* k,
-                          const void* v, const void* dout, const float* lse,
-                          const void* workspace, size_t workspace_bytes,
-                          float* dk, float* dv, void* stream);
+ *                        page's column-block partition of the backward).  It
+ *                        reads D and L log2(e) from the workspace, which
+ *                        attn_bwd_dq or attn_bwd_preprocess must have filled
+ *                        from the same o, dout and lse earlier on the stream.
+ *   attn_bwd_preprocess: only fills the workspace (D and L log2(e)), for a
+ *                        caller that runs attn_bwd_dkdv without attn_bwd_dq. */
 attn_status attn_bwd_dq(const attn_desc* desc, const void* q, const void* k,
-                        const void* v, const void* dout, const float* lse,
-                        const void* workspace, size_t workspace_bytes, float* dq,
-                        void* stream);
+                        const void* v, const void* o, const void* dout,
+                        const float* lse, void* workspace, size_t workspace_bytes,
+                        float* dq, void* stream);
+attn_status attn_bwd_dkdv(const attn_desc* desc, const void* q, const void* k,
+                          const void* v, const void* dout, const void* workspace,
+                          size_t workspace_bytes, float* dk, float* dv, void* stream);
+attn_status attn_bwd_preprocess(const attn_desc* desc, const void* o,
+                                const void* dout, const float* lse, void* workspace,
+                                size_t workspace_bytes, void* stream);
 
 /* Forward with fp8 inputs (FLASH-ATTN page, FlashAttention-3 summary,
  * "Low-precision with FP8": both products on the fp8 matrix cores, one scale

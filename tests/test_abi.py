@@ -76,7 +76,7 @@ def test_fwd_rejects_bad_pointers_and_dtype(ea):
 def test_bwd_workspace_and_rejections(ea):
     desc = ea.make_desc(2, 3, 100, 128, 0.1, True, 0)
     ws = ea.lib.attn_bwd_workspace_bytes(ctypes.byref(desc))
-    assert ws >= 2 * 3 * 100 * 4 and ws % 256 == 0
+    assert ws >= 2 * (2 * 3 * 100 * 4) and ws % 256 == 0  # D and L log2(e)
     bad = ea.make_desc(2, 3, 100, 80, 0.1, True, 0)
     assert ea.lib.attn_bwd_workspace_bytes(ctypes.byref(bad)) == 0
     vp = ctypes.c_void_p
@@ -93,13 +93,18 @@ def test_bwd_stages_reject_bad_arguments(ea):
     ws = ea.lib.attn_bwd_workspace_bytes(ctypes.byref(desc))
     vp = ctypes.c_void_p
     f = vp(FAKE)
-    assert ea.lib.attn_bwd_preprocess(ctypes.byref(desc), f, None, f, ws, None) == 1
-    assert ea.lib.attn_bwd_preprocess(ctypes.byref(desc), f, f, f, ws - 1, None) == 1
-    assert ea.lib.attn_bwd_dkdv(ctypes.byref(desc), f, f, f, f, f, f, ws, f, vp(FAKE + 4),
+    assert ea.lib.attn_bwd_preprocess(ctypes.byref(desc), f, None, f, f, ws, None) == 1
+    assert ea.lib.attn_bwd_preprocess(ctypes.byref(desc), f, f, None, f, ws, None) == 1
+    assert ea.lib.attn_bwd_preprocess(ctypes.byref(desc), f, f, f, f, ws - 1, None) == 1
+    assert ea.lib.attn_bwd_dkdv(ctypes.byref(desc), f, f, f, f, f, ws, f, vp(FAKE + 4),
                                 None) == 1
-    assert ea.lib.attn_bwd_dq(ctypes.byref(desc), f, f, None, f, f, f, ws, f, None) == 1
+    assert ea.lib.attn_bwd_dkdv(ctypes.byref(desc), f, f, f, f, None, ws, f, f, None) == 1
+    assert ea.lib.attn_bwd_dq(ctypes.byref(desc), f, f, None, f, f, f, f, ws, f, None) == 1
+    assert ea.lib.attn_bwd_dq(ctypes.byref(desc), f, f, f, None, f, f, f, ws, f, None) == 1
+    assert ea.lib.attn_bwd_dq(ctypes.byref(desc), f, f, f, f, f, f, f, ws - 1, f,
+                              None) == 1
     bad = ea.make_desc(1, 2, 64, 64, -0.1, False, 0)
-    assert ea.lib.attn_bwd_dq(ctypes.byref(bad), f, f, f, f, f, f, ws, f, None) == 1
+    assert ea.lib.attn_bwd_dq(ctypes.byref(bad), f, f, f, f, f, f, f, ws, f, None) == 1
 
 
 def test_fp8_rejects_bad_descales(ea):

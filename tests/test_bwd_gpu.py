@@ -91,3 +91,51 @@ def test_backward_deterministic(ea):
     b = fwd_bwd(ea, dev, True, 0)
     for x, y in zip(a, b):
         assert np.array_equal(x, y)
+
+
+@pytest.mark.parametrize("d,causal", [(64, False), (128, True)])
+def test_stages_and_workspace(ea, d, causal):
+    """attn_bwd_stages (dQ pass, then dK/dV pass) is bitwise attn_bwd; the
+    preprocess-filled workspace (D, L log2 e) agrees with the one the dQ pass
+    writes, and dK, dV computed from it meet the bars against the oracle."""
+    B, H, N = 2, 2, 777
+    log(f"case: bwd stages B{B} H{H} N{N} d{d} causal={causal}")
+    dev, ref = bf16_case(700 + d, B, H, N, d, with_dout=True)
+    q, k, v, do = dev["q"], dev["k"], dev["v"], dev["do"]
+    o, lse = ea.attn_fwd(q, k, v, causal=causal)
+    whole = ea.attn_bwd(q, k, v, o, do, lse, causal=causal)
+    nbytes = ea.attn_bwd_workspace_bytes(B, H, N, d)
+    ws_dq = torch.zeros(nbytes, device="cuda", dtype=torch.uint8)
+    staged = ea.attn_bwd_stages(q, k, v, o, do, lse, causal=causal, workspace=ws_dq)
+    ws_pre = torch.zeros(nbytes, device="cuda", dtype=torch.uint8)
+    pre = ea.attn_bwd_stages(q, k, v, o, do, lse, causal=causal, workspace=ws_pre,
+                             preprocess=True)
+    # the preprocess pass alone, on a fresh workspace
+    ws_only = torch.zeros(nbytes, device="cuda", dtype=torch.uint8)
+    ea.attn_bwd_preprocess(o, do, lse, ws_only, causal=causal)
+    torch.cuda.synchronize()
+    for a, b in zip(whole, staged):
+        assert torch.equal(a, b)
+    rows = B * H * N
+    half = nbytes // 2
+    f_dq, f_only = ws_dq.view(torch.float32), ws_only.view(torch.float32)
+    # D: two fp32 summation orders of the same d products; each is within
+    # d * 2^-24 * sum_k |dO_ik O_ik| of the exact sum (Higham's bound for a
+    # recursive sum of products), so they differ by at most twice that.
+    x, y = f_dq[:rows].double(), f_only[:rows].double()
+    mag = (do.double() * o.double()).abs().sum(dim=-1).reshape(-1)
+    ratio = ((x - y).abs() / (2 * d * 2.0 ** -24 * mag + 1e-30)).max().item()
+    log(f"    workspace D: dQ pass vs preprocess, max diff / bound = {ratio:.3f}")
+    assert ratio <= 1.0
+    # L log2(e): the same single fp32 product on both paths.
+    off = half // 4
+    assert torch.equal(f_dq[off:off + rows], f_only[off:off + rows])
+    lse_np = lse.cpu().numpy().reshape(-1).astype(np.float64)
+    assert np.allclose(f_only[off:off + rows].cpu().numpy(),
+                       lse_np * math.log2(math.e), rtol=1e-6, atol=1e-6)
+    got = [t.cpu().numpy().astype(np.float64) for t in pre]
+    for b, h in ((0, 0), (B - 1, H - 1)):
+        want = oracle.bwd(ref["q"][b, h], ref["k"][b, h], ref["v"][b, h],
+                          ref["do"][b, h], 1 / math.sqrt(d), causal, 0)[:3]
+        for name, g, r in zip(("dQ", "dK", "dV"), got, want):
+            assert_close(g[b, h], r, BF16_MAX, BF16_MEAN, f"{name} head ({b},{h})")
