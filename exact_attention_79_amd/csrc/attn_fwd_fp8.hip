@@ -58,32 +58,31 @@ __device__ __forceinline__ int off8(int r, int ch) {
 
 // Row of V key `key` inside its LDS tile: within each 64-key block, keys
 // 8a + 4b + c (b in {0,1}) go to row 32b + 4a + c, so wave half b finds its
-// keys {8a + 4b + c} in 32 consecutive rows.
-__device__ __forceinline__ int vrow(int key) {
-  return (key & ~63) | (((key >> 2) & 1) << 5) | (((key >> 3) & 7) << 2) | (key & 3);
+// keys {8a + 4b + c} in 32 consecutive rows.  vkey is the inverse map.
+__device__ __forceinline__ int vkey(int row) {
+  return (row & ~63) | (((row >> 2) & 7) << 3) | (((row >> 5) & 1) << 2) | (row & 3);
 }
 
-template <int D, int ROWS, int NT, bool PERMUTE>
-struct TileStage8 {
-  static constexpr int CH = D / 16;
-  static constexpr int N16 = ROWS * CH / NT;
-  static_assert((ROWS * CH) % NT == 0, "tile must split evenly over threads");
-  u32x4 r[N16];
-  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, int row0, int tid) {
+// Direct global -> LDS load of a ROWS x D byte tile by NW waves: wave w's
+// instruction i fills LDS chunks (i*NW + w)*64 + lane, i.e. chunk ch of LDS
+// row r, which holds global chunk ch ^ swz8(r) of source row r (K) or of
+// source row vkey(r) (V, PERMUTE).  Rows past the buffer end read as zero.
+template <int D, int ROWS, int NW, bool PERMUTE>
+__device__ __forceinline__ void tile_load_lds8(__amdgpu_buffer_rsrc_t rs, int row0,
+                                               uint8_t* t, int w, int lane) {
+  constexpr int CH = D / 16;
+  constexpr int ROUNDS = ROWS * CH / (64 * NW);
+  static_assert((ROWS * CH) % (64 * NW) == 0 && ROWS % 64 == 0, "tile split");
 #pragma unroll
-    for (int i = 0; i < N16; ++i) {
-      const int c = tid + i * NT, row = c / CH, ch = c % CH;
-      r[i] = buf_load16(rs, (uint32_t)((row0 + row) * D + ch * 16));
-    }
+  for (int i = 0; i < ROUNDS; ++i) {
+    const int base = (i * NW + w) * 64;
+    const int pc = base + lane, r = pc / CH, ch = (pc % CH) ^ swz8<D>(r);
+    const int g = PERMUTE ? vkey(r) : r;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS_AS void*)(t + base * 16), 16,
+                                             (int)((uint32_t)((row0 + g) * D + ch * 16)),
+                                             0, 0, 0);
   }
-  __device__ __forceinline__ void store(uint8_t* t, int tid) const {
-#pragma unroll
-    for (int i = 0; i < N16; ++i) {
-      const int c = tid + i * NT, row = c / CH, ch = c % CH;
-      *(u32x4*)&t[off8<D>(PERMUTE ? vrow(row) : row, ch)] = r[i];
-    }
-  }
-};
+}
 
 __device__ __forceinline__ f32x16 mfma_fp8(i32x8 a, i32x8 b, f32x16 c, int scale_b) {
   // Formats: A and B e4m3 (0); A block scale 2^0 (127); B block scale per lane.
@@ -109,8 +108,16 @@ template <int D, int NW>
 __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8_kernel(FwdFp8Params p) {
   constexpr int BC = 64;  // keys per tile = one 64-deep fp8 MFMA step
   constexpr int BR = 32 * NW;
-  constexpr int NT = NW * 64;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2][2][BC * D];
+  constexpr int KS = D / 64;  // K-steps of a score tile
+  // Three LDS slots each for K and V (tile u in slot u % 3), as separate
+  // arrays so that the compiler can tell the slots being filled from the
+  // ones being read; tiles are fetched two iterations before first use.
+  __shared__ __attribute__((aligned(16))) uint8_t sK0[BC * D];
+  __shared__ __attribute__((aligned(16))) uint8_t sK1[BC * D];
+  __shared__ __attribute__((aligned(16))) uint8_t sK2[BC * D];
+  __shared__ __attribute__((aligned(16))) uint8_t sV0[BC * D];
+  __shared__ __attribute__((aligned(16))) uint8_t sV1[BC * D];
+  __shared__ __attribute__((aligned(16))) uint8_t sV2[BC * D];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int h = lane >> 5, n = lane & 31;
@@ -129,9 +136,9 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8_kernel(FwdFp8Params p) {
 
   // Q^T as the B operand of S^T = K Q^T: in K-step ks a lane holds the 32
   // bytes d = 64 ks + 32 h .. +31 of its query; K rows are read the same way.
-  i32x8 qop[D / 64];
+  i32x8 qop[KS];
 #pragma unroll
-  for (int ks = 0; ks < D / 64; ++ks) {
+  for (int ks = 0; ks < KS; ++ks) {
     const uint32_t off = (uint32_t)(my_q * D + 64 * ks + 32 * h);
     const u32x4 a = buf_load16(rq, off), b = buf_load16(rq, off + 16);
     qop[ks] = (i32x8){(int)a[0], (int)a[1], (int)a[2], (int)a[3],
@@ -147,17 +154,6 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8_kernel(FwdFp8Params p) {
   }
   const int t_lo = kv_lo / BC, t_hi = (kv_hi + BC - 1) / BC;
 
-  TileStage8<D, BC, NT, false> stK;
-  TileStage8<D, BC, NT, true> stV;
-  auto load_tile = [&](int t) {
-    stK.load(rk, t * BC, tid);
-    stV.load(rv, t * BC, tid);
-  };
-  auto store_tile = [&](int b) {
-    stK.store(smem[b][0], tid);
-    stV.store(smem[b][1], tid);
-  };
-
   f32x16 oacc[D / 32];
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) oacc[dt] = (f32x16){};
@@ -165,64 +161,81 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8_kernel(FwdFp8Params p) {
   const float s2 = p.scale * p.qk_descale * kLog2e;
   const float tau = 8.0f / s2;
 
-  if (t_lo < t_hi) {
-    load_tile(t_lo);
-    store_tile(0);
-  }
-  __syncthreads();
-
-  // Transposing-read coordinates: lane j of a 16-lane group reads row
-  // (j >> 1) of an 8-row slab, 8 bytes at column 8 (j & 1) of a 16-byte chunk;
-  // it receives column (lane & 15) of the slab.
+  // K row reads: the A operand of K-step ks for M-tile mt (32 bytes of row
+  // 32 mt + n: chunks 4 ks + 2 h and 4 ks + 2 h + 1).
+  auto kread = [&](const uint8_t* Ks, int mt, int ks) {
+    const int r = 32 * mt + n;
+    const u32x4 a = *(const u32x4*)&Ks[off8<D>(r, 4 * ks + 2 * h)];
+    const u32x4 b = *(const u32x4*)&Ks[off8<D>(r, 4 * ks + 2 * h + 1)];
+    return (i32x8){(int)a[0], (int)a[1], (int)a[2], (int)a[3],
+                   (int)b[0], (int)b[1], (int)b[2], (int)b[3]};
+  };
+  // V^T reads: lane j of a 16-lane group reads row (j >> 1) of an 8-row slab,
+  // 8 bytes at column 8 (j & 1) of a 16-byte chunk, and receives column
+  // (lane & 15) of the slab; four slabs make the A operand of d-tile dt.
   const int trj = lane & 15, trg = lane >> 4;
-  const int tr_row = 32 * (trg >> 1) + (trj >> 1);       // + 8t
-  const int tr_col = 16 * (trg & 1) + 8 * (trj & 1);     // + 32 dt
-
-  int buf = 0;
-  for (int t = t_lo; t < t_hi; ++t) {
-    const bool has_next = t + 1 < t_hi;
-    if (has_next) load_tile(t + 1);
-    const uint8_t* Ks = smem[buf][0];
-    const uint8_t* Vs = smem[buf][1];
-    const int kv0 = t * BC;
-
-    f32x16 sacc[2];
+  const int tr_row = 32 * (trg >> 1) + (trj >> 1);
+  const int tr_col = 16 * (trg & 1) + 8 * (trj & 1);
+  auto vread = [&](const uint8_t* Vs, int dt) {
+    i32x8 va;
+#pragma unroll
+    for (int t8 = 0; t8 < 4; ++t8) {
+      const int row = tr_row + 8 * t8, col = 32 * dt + tr_col;
+      const i32x2 x = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+          (LDS_AS i32x2*)&Vs[off8<D>(row, col >> 4) + (col & 15)]);
+      va[2 * t8] = x[0];
+      va[2 * t8 + 1] = x[1];
+    }
+    return va;
+  };
+  auto scores = [&](const uint8_t* Ks, f32x16* sacc) {
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
       sacc[mt] = (f32x16){};
-      const int r = 32 * mt + n;
 #pragma unroll
-      for (int ks = 0; ks < D / 64; ++ks) {
-        const u32x4 a = *(const u32x4*)&Ks[off8<D>(r, 4 * ks + 2 * h)];
-        const u32x4 b = *(const u32x4*)&Ks[off8<D>(r, 4 * ks + 2 * h + 1)];
-        const i32x8 ka = {(int)a[0], (int)a[1], (int)a[2], (int)a[3],
-                          (int)b[0], (int)b[1], (int)b[2], (int)b[3]};
-        sacc[mt] = mfma_fp8(ka, qop[ks], sacc[mt], 127);
-      }
+      for (int ks = 0; ks < KS; ++ks) sacc[mt] = mfma_fp8(kread(Ks, mt, ks), qop[ks], sacc[mt], 127);
     }
+  };
 
-    bool need_mask = kv0 + BC > N;
-    if (p.causal) need_mask |= kv0 + BC - 1 > wq0;
+  int hi_key = N - 1, lo_key = 0;
+  if (p.causal) hi_key = min(hi_key, my_q);
+  if (p.window > 0) {
+    lo_key = my_q - p.window + 1;
+    if (!p.causal) hi_key = min(hi_key, my_q + p.window - 1);
+  }
+  // Masks tile t element by element when it straddles a boundary of this
+  // wave (a uniform test); returns whether it did.  Register r of M-tile mt
+  // holds key t*BC + 32mt + 8(r/4) + 4h + r%4.
+  auto mask_tile = [&](int t, f32x16* sacc) -> bool {
+    const int kv0 = t * BC;
+    bool need = kv0 + BC > N;
+    if (p.causal) need |= kv0 + BC - 1 > wq0;
     if (p.window > 0) {
-      need_mask |= wq0 + 31 - kv0 >= p.window;
-      if (!p.causal) need_mask |= kv0 + BC - 1 - wq0 >= p.window;
+      need |= wq0 + 31 - kv0 >= p.window;
+      if (!p.causal) need |= kv0 + BC - 1 - wq0 >= p.window;
     }
-    if (need_mask) {
+    if (!need) return false;
+    const int lim_hi = hi_key - kv0 - 4 * h, lim_lo = lo_key - kv0 - 4 * h;
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
+    for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kv0 + 32 * mt + 8 * (r >> 2) + 4 * h + (r & 3);
-          if (!visible(my_q, key, N, p.causal, p.window))
-            sacc[mt][r] = -__builtin_inff();
-        }
-    }
-
-    float mx = -__builtin_inff();
+      for (int r = 0; r < 16; ++r) {
+        const int c = 32 * mt + 8 * (r >> 2) + (r & 3);
+        sacc[mt][r] = (c > lim_hi || c < lim_lo) ? -__builtin_inff() : sacc[mt][r];
+      }
+    return true;
+  };
+  auto tile_max = [&](const f32x16* sacc) {
+    float mx = sacc[0][0];
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[mt][r]);
+    return mx;
+  };
+  // Running max update for a tile whose in-lane max is mx; returns the
+  // tile's row max (both wave halves).
+  auto update_max = [&](float mx) {
     mx = halves_max(mx);
     const float m_new = (mx > m_run + tau) ? mx : m_run;
     const float alpha = fast_exp2((m_run - m_new) * s2);
@@ -232,66 +245,127 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8_kernel(FwdFp8Params p) {
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) oacc[dt] *= alpha;
     }
+    return mx;
+  };
+
+  tile_load_lds8<D, BC, NW, false>(rk, t_lo * BC, sK0, w, lane);
+  tile_load_lds8<D, BC, NW, true>(rv, t_lo * BC, sV0, w, lane);
+  tile_load_lds8<D, BC, NW, false>(rk, (t_lo + 1) * BC, sK1, w, lane);
+  tile_load_lds8<D, BC, NW, true>(rv, (t_lo + 1) * BC, sV1, w, lane);
+  tile_load_lds8<D, BC, NW, false>(rk, (t_lo + 2) * BC, sK2, w, lane);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  f32x16 scur[2];
+  scores(sK0, scur);
+  mask_tile(t_lo, scur);
+  float tmx = update_max(tile_max(scur));
+
+  constexpr int kLoadsPerIter = 2 * (BC * D / 16) / (64 * NW);
+  constexpr int kWaitOlderLoads = waitcnt_vm(kLoadsPerIter);
+
+  // One iteration for tile t (scores masked in scur, row max tmx, running
+  // max already in m_run): reads K_{t+1} from Kr and V_t from Vr, refills
+  // Kf (K_t's slot) with K_{t+3} and Vf (V_{t-1}'s slot) with V_{t+2}.
+  auto iteration = [&](int t, const uint8_t* Kr, const uint8_t* Vr, uint8_t* Kf,
+                       uint8_t* Vf) {
+    tile_load_lds8<D, BC, NW, false>(rk, (t + 3) * BC, Kf, w, lane);
+    tile_load_lds8<D, BC, NW, true>(rv, (t + 2) * BC, Vf, w, lane);
+    // Block scale of this tile's probabilities: the row's largest weight
+    // 2^y (y = s2 tmx - s2 m_run <= 8) is brought into [128, 256) by 2^-e,
+    // e = floor(y) - 7, folded into the exponent of every weight.
     const float mb = m_run * s2;
-    float pmax = 0.f;
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        sacc[mt][r] = fast_exp2(fmaf(sacc[mt][r], s2, -mb));
-        pmax = fmaxf(pmax, sacc[mt][r]);
-      }
-    pmax = halves_max(pmax);
-    // 2^e with pmax * 2^-e in [128, 256); e kept where e - 4 is a valid E8M0.
-    int e = (int)((__builtin_bit_cast(uint32_t, pmax) >> 23) & 0xff) - 127 - 7;
-    e = max(-123, min(127, e));
-    // Pack: byte j of the B operand = block key slot j = C[j / 16][j % 16].
-    i32x8 phi, plo;
-    float lsum = 0.f;
-#pragma unroll
-    for (int wd = 0; wd < 8; ++wd) {
-      const int mt = wd >> 2, r0 = 4 * (wd & 3);
-      float x[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        lsum += sacc[mt][r0 + i];
-        x[i] = __builtin_ldexpf(sacc[mt][r0 + i], -e);
-      }
-      int hw = 0;
-      hw = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], hw, false);
-      hw = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], hw, true);
-      const auto h01 = __builtin_amdgcn_cvt_pk_f32_fp8(hw, false);
-      const auto h23 = __builtin_amdgcn_cvt_pk_f32_fp8(hw, true);
-      int lw = 0;
-      lw = __builtin_amdgcn_cvt_pk_fp8_f32(16.f * (x[0] - h01[0]), 16.f * (x[1] - h01[1]),
-                                           lw, false);
-      lw = __builtin_amdgcn_cvt_pk_fp8_f32(16.f * (x[2] - h23[0]), 16.f * (x[3] - h23[1]),
-                                           lw, true);
-      phi[wd] = hw;
-      plo[wd] = lw;
-    }
-    l_run += lsum;
+    const float y = fmaxf(tmx * s2 - mb, -200.f);
+    const int e = max(-123, min(127, (int)floorf(y) - 7));
+    const float mbe = mb + (float)e;
 
-    // O^T += V^T (2^e hi + 2^(e-4) lo)^T, the scales applied by the MFMA.
+    // Bundles 0..NS-1: the next tile's score MFMAs, each with a slice of
+    // this tile's weights (exp2, then e4m3 hi and 16x residual lo terms);
+    // bundles NS..NS+NP-1: this tile's P V MFMAs (hi and lo per d-tile),
+    // each with a slice of the next tile's row max.
+    constexpr int NS = 2 * KS;
+    constexpr int NP = 2 * (D / 32);
+    constexpr int WPB = 8 / NS;  // packed words (4 weights) per score bundle
+    constexpr int NCH = NP - 2, CH = (32 + NCH - 1) / NCH;
+    static_assert(WPB >= 1 && 8 % NS == 0, "bundle split");
+    f32x16 snext[2];
+    snext[0] = snext[1] = (f32x16){};
+    i32x8 ka[NS], va[D / 32], phi, plo;
+    float lsum = 0.f, part[NCH];
+    ka[0] = kread(Kr, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt) {
-      i32x8 va;
+    for (int i = 0; i < NS; ++i) {
+      if (i + 1 < NS) ka[i + 1] = kread(Kr, (i + 1) / KS, (i + 1) % KS);
+      if (i == NS - 1) va[0] = vread(Vr, 0);
+      snext[i / KS] = mfma_fp8(ka[i], qop[i % KS], snext[i / KS], 127);
 #pragma unroll
-      for (int t8 = 0; t8 < 4; ++t8) {
-        const int row = tr_row + 8 * t8, col = 32 * dt + tr_col;
-        const i32x2 x = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-            (LDS_AS i32x2*)&Vs[off8<D>(row, col >> 4) + (col & 15)]);
-        va[2 * t8] = x[0];
-        va[2 * t8 + 1] = x[1];
+      for (int u = 0; u < WPB; ++u) {
+        const int wd = WPB * i + u, mt = wd >> 2, r0 = 4 * (wd & 3);
+        float x[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          x[j] = fast_exp2(fmaf(scur[mt][r0 + j], s2, -mbe));
+          lsum += x[j];
+        }
+        int hw = 0;
+        hw = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], hw, false);
+        hw = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], hw, true);
+        const auto h01 = __builtin_amdgcn_cvt_pk_f32_fp8(hw, false);
+        const auto h23 = __builtin_amdgcn_cvt_pk_f32_fp8(hw, true);
+        int lw = 0;
+        lw = __builtin_amdgcn_cvt_pk_fp8_f32(16.f * (x[0] - h01[0]), 16.f * (x[1] - h01[1]),
+                                             lw, false);
+        lw = __builtin_amdgcn_cvt_pk_fp8_f32(16.f * (x[2] - h23[0]), 16.f * (x[3] - h23[1]),
+                                             lw, true);
+        phi[wd] = hw;
+        plo[wd] = lw;
       }
-      oacc[dt] = mfma_fp8(va, phi, oacc[dt], e + 127);
-      oacc[dt] = mfma_fp8(va, plo, oacc[dt], e - 4 + 127);
+      __builtin_amdgcn_sched_barrier(0);
     }
+#pragma unroll
+    for (int j = 0; j < NP; ++j) {
+      const int dt = j >> 1;
+      if ((j & 1) && dt + 1 < D / 32) va[dt + 1] = vread(Vr, dt + 1);
+      oacc[dt] = mfma_fp8(va[dt], (j & 1) ? plo : phi, oacc[dt],
+                          (j & 1) ? e - 4 + 127 : e + 127);
+      if (j >= 2) {
+        const int c = j - 2;
+        float mx = snext[(c * CH) >> 4][(c * CH) & 15];
+#pragma unroll
+        for (int u = 1; u < CH; ++u) {
+          const int el = c * CH + u;
+          if (el < 32) mx = fmaxf(mx, snext[el >> 4][el & 15]);
+        }
+        // Pinned here: it is only read after the loop, and the compiler
+        // would otherwise sink it there, out of the bundles.
+        asm volatile("" ::"v"(mx));
+        part[c] = mx;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    l_run += __builtin_ldexpf(lsum, e);
+    if (t + 1 < t_hi) {
+      float mx = part[0];
+#pragma unroll
+      for (int c = 1; c < NCH; ++c) mx = fmaxf(mx, part[c]);
+      if (mask_tile(t + 1, snext)) mx = tile_max(snext);
+      tmx = update_max(mx);
+    }
+    // The loads issued one iteration ago (K_{t+2}, V_{t+1}) have landed for
+    // this wave; after the barrier they have for every wave, and the slots
+    // read in this iteration may be refilled.
+    __builtin_amdgcn_s_waitcnt(kWaitOlderLoads);
+    __builtin_amdgcn_s_barrier();
+    scur[0] = snext[0];
+    scur[1] = snext[1];
+  };
 
-    if (has_next) store_tile(buf ^ 1);
-    __syncthreads();
-    buf ^= 1;
+  for (int t = t_lo; t < t_hi; t += 3) {
+    iteration(t, sK1, sV0, sK0, sV2);
+    if (t + 1 < t_hi) iteration(t + 1, sK2, sV1, sK1, sV0);
+    if (t + 2 < t_hi) iteration(t + 2, sK0, sV2, sK2, sV1);
   }
+  __builtin_amdgcn_s_waitcnt(0);
 
   const float l_tot = halves_sum(l_run);
   if (my_q < N) {
