@@ -35,6 +35,7 @@ namespace attn {
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef short v2i16 __attribute__((ext_vector_type(2)));
 
 // fp8 tiles: rows of D bytes in 16-byte chunks, chunk c of row r at c ^ swz8(r).
 // d = 128 (8 chunks, 2 rows per 256-byte bank span): the 16 rows of a row
@@ -307,18 +308,22 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8_kernel(FwdFp8Params p) {
           x[j] = fast_exp2(fmaf(scur[mt][r0 + j], s2, -mbe));
           lsum += x[j];
         }
-        int hw = 0;
+        // (The first convert of each pair writes the low word and keeps the
+        // high one, which the second convert then fills: any old value will
+        // do, so an existing register is passed instead of a zeroed one.)
+        int hw = __builtin_bit_cast(int, x[3]);
         hw = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], hw, false);
         hw = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], hw, true);
         const auto h01 = __builtin_amdgcn_cvt_pk_f32_fp8(hw, false);
         const auto h23 = __builtin_amdgcn_cvt_pk_f32_fp8(hw, true);
-        int lw = 0;
-        lw = __builtin_amdgcn_cvt_pk_fp8_f32(16.f * (x[0] - h01[0]), 16.f * (x[1] - h01[1]),
-                                             lw, false);
-        lw = __builtin_amdgcn_cvt_pk_fp8_f32(16.f * (x[2] - h23[0]), 16.f * (x[3] - h23[1]),
-                                             lw, true);
+        // lo = e4m3(16 (x - hi)): the scaled convert divides by 2^-4 itself.
+        v2i16 lw = __builtin_bit_cast(v2i16, x[3]);
+        lw = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lw, x[0] - h01[0], x[1] - h01[1],
+                                                      0.0625f, false);
+        lw = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lw, x[2] - h23[0], x[3] - h23[1],
+                                                      0.0625f, true);
         phi[wd] = hw;
-        plo[wd] = lw;
+        plo[wd] = __builtin_bit_cast(int, lw);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
