@@ -132,10 +132,12 @@ attn_status attn_bwd_preprocess(const attn_desc* desc, const void* o,
 /* Forward with fp8 inputs (FLASH-ATTN page, FlashAttention-3 summary,
  * "Low-precision with FP8": both products on the fp8 matrix cores, one scale
  * per tensor).  q8, k8, v8 are E4M3 codes [B,H,N,d]; the real inputs are
- * code * descale.  Within each K/V tile the probabilities of every query row
- * are rescaled so that the row's largest entry maps to 448 before they are
- * rounded to E4M3 for the P V product; that scale is divided out again in
- * the fp32 accumulator.  o and lse as in attn_fwd. */
+ * code * descale.  Within each 64-key tile the probabilities of every query
+ * row are scaled by the power of two that brings the row's largest one into
+ * [128, 256) and are carried as two E4M3 terms, hi + 2^-4 lo, through the
+ * P V product; the matrix core's per-lane block scale removes the power of
+ * two again, so the fp32 accumulator holds the unscaled product.  o and lse
+ * as in attn_fwd. */
 attn_status attn_fwd_fp8(const attn_desc* desc, const uint8_t* q8,
                          const uint8_t* k8, const uint8_t* v8, float q_descale,
                          float k_descale, float v_descale, void* o,
