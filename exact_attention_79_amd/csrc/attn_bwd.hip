@@ -30,8 +30,9 @@
 // dK^T += Q^T dS; dO^T and Q^T are read from LDS with transposing reads in
 // the C layout's row permutation.  The dQ kernel is the mirror image: S^T =
 // K Q^T with one query per lane, and dQ^T += K^T dS^T with K^T read
-// transposed from LDS.  Q/dO (dK/dV kernel) and K/V (dQ kernel) tiles are
-// double-buffered in LDS with the same swizzle as the forward.
+// transposed from LDS.  Q/dO (dK/dV kernel) and K/V (dQ kernel) tiles stream
+// through three-slot LDS rings (direct global -> LDS loads) with the same
+// swizzle as the forward.
 #include <limits.h>
 
 #include "attn_device.hpp"

@@ -218,30 +218,4 @@ __host__ __device__ constexpr int waitcnt_vm(int n) {
   return (n & 0xF) | (0x7 << 4) | (0xF << 8) | ((n >> 4) << 14);
 }
 
-// Global -> register -> LDS staging of a ROWS x D bf16 tile by NT threads:
-// thread tid moves chunks tid, tid + NT, ... (16 threads per 256-byte row,
-// so every global access is a full coalesced row segment).  Rows past the
-// end of the buffer resource read as zero.
-template <int D, int ROWS, int NT>
-struct TileStage {
-  static constexpr int CH = D / 8;
-  static constexpr int N16 = ROWS * CH / NT;
-  static_assert((ROWS * CH) % NT == 0, "tile must split evenly over threads");
-  u32x4 r[N16];
-  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, int row0, int tid) {
-#pragma unroll
-    for (int i = 0; i < N16; ++i) {
-      const int c = tid + i * NT, row = c / CH, ch = c % CH;
-      r[i] = buf_load16(rs, (uint32_t)((row0 + row) * D + ch * 8) * 2u);
-    }
-  }
-  __device__ __forceinline__ void store(__bf16* t, int tid) const {
-#pragma unroll
-    for (int i = 0; i < N16; ++i) {
-      const int c = tid + i * NT, row = c / CH, ch = c % CH;
-      *(u32x4*)&t[tile_off<D>(row, ch)] = r[i];
-    }
-  }
-};
-
 }  // namespace attn

@@ -14,15 +14,15 @@
 //  * Each wave owns 32 queries and computes S^T = K_j Q_i^T on
 //    v_mfma_f32_32x32x16_bf16 (keys on the M side, queries on N), so the C
 //    layout gives every lane ONE query: the row max and row sum are in-lane
-//    reductions plus one permlane32 swap, and the rescale factor is a
-//    per-lane scalar.
+//    reductions plus one exchange between the two wave halves, and the
+//    rescale factor is a per-lane scalar.
 //  * The probabilities P^T, converted to bf16 in place, are directly the B
 //    operand of O^T += V_j^T P^T (d on the M side).  V_j^T is read from LDS
 //    with ds_read_b64_tr_b16 using the key permutation of the C layout
 //    (see attn_device.hpp), so nothing moves between lanes.
-//  * Q_i^T stays in VGPRs for the whole K/V loop; K_j and V_j are
-//    double-buffered in LDS: the next tile's global loads are issued before
-//    the current tile's math and written to the other buffer after it.
+//  * Q_i^T stays in VGPRs for the whole K/V loop; K_j and V_j stream
+//    through a ring of three LDS slots, filled by direct global -> LDS loads
+//    issued two to three tiles ahead of use, with one barrier per tile.
 //  * Scores stay in raw units; exp2 takes fma(S, s*log2e, -m*s*log2e).  The
 //    running max is only moved when a new score exceeds it by more than
 //    8 / (s*log2e) (i.e. 2^8 in probability units): every exponent stays
