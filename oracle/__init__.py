@@ -60,6 +60,9 @@ def lib():
         L.oracle_bwd.argtypes = [i, i, i, d, i, lg, dp, dp, dp, dp, dp, dp, dp, dp, i]
         L.oracle_online_fwd.argtypes = [i, i, d, i, lg, dp, dp, dp,
                                         ctypes.POINTER(lg), i, i, dp, dp]
+        L.oracle_fwd_gqa.argtypes = [i, i, i, i, i, d, i, lg, dp, dp, dp, dp, dp, i]
+        L.oracle_bwd_gqa.argtypes = [i, i, i, i, i, d, i, lg, dp, dp, dp, dp, dp, dp,
+                                     dp, dp, i]
         _lib = L
     return _lib
 
@@ -162,3 +165,39 @@ def online_fwd(q, k, v, bounds, form: int, scale: float, causal: bool = False,
                             b.ctypes.data_as(ctypes.POINTER(ctypes.c_long)),
                             b.size - 1, int(form), _p(o), _p(lse))
     return o, lse
+
+
+def _gqa_shapes(q, k):
+    assert q.ndim == 4 and k.ndim == 4
+    B, H, N, d = q.shape
+    Hkv = k.shape[1]
+    assert k.shape == (B, Hkv, N, d) and Hkv >= 1 and H % Hkv == 0
+    return B, H, Hkv, N, d
+
+
+def fwd_gqa(q, k, v, scale: float, causal: bool = False, window: int = 0,
+            nthreads: int = 0):
+    """O and L for q [B, H, N, d] and shared k, v [B, Hkv, N, d]."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, H, Hkv, N, d = _gqa_shapes(q, k)
+    assert v.shape == k.shape
+    o = np.empty_like(q)
+    lse = np.empty(q.shape[:-1], np.float64)
+    lib().oracle_fwd_gqa(B, H, Hkv, N, d, float(scale), int(causal), int(window),
+                         _p(q), _p(k), _p(v), _p(o), _p(lse), int(nthreads))
+    return o, lse
+
+
+def bwd_gqa(q, k, v, dout, scale: float, causal: bool = False, window: int = 0,
+            nthreads: int = 0):
+    """dQ [B, H, N, d], dK, dV [B, Hkv, N, d] (summed over each group) and D."""
+    q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+    B, H, Hkv, N, d = _gqa_shapes(q, k)
+    assert v.shape == k.shape and dout.shape == q.shape
+    dq = np.empty_like(q)
+    dk, dv = np.empty_like(k), np.empty_like(k)
+    D = np.empty(q.shape[:-1], np.float64)
+    lib().oracle_bwd_gqa(B, H, Hkv, N, d, float(scale), int(causal), int(window),
+                         _p(q), _p(k), _p(v), _p(dout), _p(dq), _p(dk), _p(dv), _p(D),
+                         int(nthreads))
+    return dq, dk, dv, D

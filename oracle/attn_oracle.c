@@ -173,6 +173,37 @@ void oracle_probs_row(int N, int d, double scale, int causal, long window,
   free(o_row);
 }
 
+/* Multi-query and grouped-query attention (FLASH-ATTN page, FlashAttention-2
+ * section, the paragraph on MQA and GQA): H query heads share Hkv key/value
+ * heads, H a multiple of Hkv.  Query head h of batch element b reads key and
+ * value head b*Hkv + h/(H/Hkv) through its index; nothing is copied.  (The
+ * page does not say which query heads share a head; consecutive ones do
+ * here.)  Layouts: q, o [B][H][N][d]; k, v [B][Hkv][N][d]; lse [B][H][N]. */
+static long kv_head_of(long bh, int H, int Hkv) {
+  return (bh / H) * Hkv + (bh % H) / (H / Hkv);
+}
+
+void oracle_fwd_gqa(int B, int H, int Hkv, int N, int d, double scale, int causal,
+                    long window, const double* q, const double* k, const double* v,
+                    double* o, double* lse, int nthreads) {
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+  long total = (long)B * H * N;
+#pragma omp parallel
+  {
+    double* srow = (double*)malloc(sizeof(double) * (size_t)N);
+    double* prow = (double*)malloc(sizeof(double) * (size_t)N);
+#pragma omp for schedule(dynamic, 16)
+    for (long r = 0; r < total; ++r) {
+      long bh = r / N, i = r % N;
+      long qoff = bh * (long)N * d, kvoff = kv_head_of(bh, H, Hkv) * (long)N * d;
+      fwd_row(N, d, scale, causal, window, q + qoff, k + kvoff, v + kvoff, i, srow,
+              prow, o + r * d, lse ? lse + r : NULL);
+    }
+    free(srow);
+    free(prow);
+  }
+}
+
 /* Backward over BH heads.  Inputs q,k,v,dout: [BH][N][d].  Outputs dq,dk,dv:
  * [BH][N][d]; Dvec: [BH][N] receives D_i = sum_j P_ij dP_ij (may be NULL).
  * Per head: pass 1 builds the explicit rows of P and dS (and dQ) one query
@@ -307,4 +338,31 @@ void oracle_online_fwd(int N, int d, double scale, int causal, long window,
     if (lse) lse[i] = m + log(l);
   }
   free(sblk);
+}
+
+/* Backward of the grouped-query forward above (same passage): every query
+ * head's gradients are those of one ordinary head reading its key/value
+ * head (oracle_bwd), and the dK, dV of a shared head are the sums of the dK,
+ * dV its query heads produce, added in increasing query-head order.
+ * q, dout, dq [B][H][N][d]; k, v, dk, dv [B][Hkv][N][d]; Dvec [B][H][N]. */
+void oracle_bwd_gqa(int B, int H, int Hkv, int N, int d, double scale, int causal,
+                    long window, const double* q, const double* k, const double* v,
+                    const double* dout, double* dq, double* dk, double* dv,
+                    double* Dvec, int nthreads) {
+  const long hs = (long)N * d;
+  double* dk1 = (double*)malloc(sizeof(double) * (size_t)hs);
+  double* dv1 = (double*)malloc(sizeof(double) * (size_t)hs);
+  for (long x = 0; x < (long)B * Hkv * hs; ++x) dk[x] = dv[x] = 0.0;
+  for (long bh = 0; bh < (long)B * H; ++bh) {
+    const long kv = kv_head_of(bh, H, Hkv);
+    oracle_bwd(1, N, d, scale, causal, window, q + bh * hs, k + kv * hs, v + kv * hs,
+               dout + bh * hs, dq + bh * hs, dk1, dv1, Dvec ? Dvec + bh * N : NULL,
+               nthreads);
+    for (long x = 0; x < hs; ++x) {
+      dk[kv * hs + x] += dk1[x];
+      dv[kv * hs + x] += dv1[x];
+    }
+  }
+  free(dk1);
+  free(dv1);
 }

@@ -325,3 +325,60 @@ def test_backward_invariants(causal, window):
     np.testing.assert_allclose(D, (o * do).sum(-1), rtol=0, atol=1e-13)
     # dV columns: sum_j dV_j = sum_i dO_i (each P row sums to 1)
     np.testing.assert_allclose(dv.sum(axis=0), do.sum(axis=0), rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------- MQA / GQA
+GQA_SHAPES = [(2, 4, 2, 9, 8), (1, 3, 1, 17, 4), (1, 6, 3, 12, 16), (2, 2, 2, 10, 4)]
+
+
+@pytest.mark.parametrize("B,H,Hkv,N,d", GQA_SHAPES)
+@pytest.mark.parametrize("causal,window", [(False, 0), (True, 0), (True, 4), (False, 3)])
+def test_gqa_equals_attention_on_repeated_heads(B, H, Hkv, N, d, causal, window):
+    """Grouped-query attention is ordinary attention with each key/value head
+    repeated for its consecutive query heads (torch fp64 SDPA on the repeated
+    tensors), and torch's autograd through the repetition sums the gradients
+    of the copies, which is the page's dK, dV accumulation over the group."""
+    q, do = rnd(900, B, H, N, d), rnd(901, B, H, N, d)
+    k, v = rnd(902, B, Hkv, N, d), rnd(903, B, Hkv, N, d)
+    s = 1.0 / math.sqrt(d)
+    o, lse = oracle.fwd_gqa(q, k, v, s, causal, window)
+    dq, dk, dv, D = oracle.bwd_gqa(q, k, v, do, s, causal, window)
+    tq, tk, tv = (torch.from_numpy(x).requires_grad_() for x in (q, k, v))
+    g = H // Hkv
+    kr, vr = tk.repeat_interleave(g, dim=1), tv.repeat_interleave(g, dim=1)
+    to = torch.nn.functional.scaled_dot_product_attention(
+        tq, kr, vr, attn_mask=torch_mask(N, causal, window), scale=s)
+    (to * torch.from_numpy(do)).sum().backward()
+    _, tlse = torch_attention(q, kr.detach().numpy(), vr.detach().numpy(), s, causal,
+                              window)
+    np.testing.assert_allclose(o, to.detach().numpy(), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, tlse, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dq, tq.grad.numpy(), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dk, tk.grad.numpy(), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dv, tv.grad.numpy(), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(D, (o * do).sum(-1), rtol=0, atol=1e-12)
+
+
+def test_gqa_with_one_query_head_per_group_is_ordinary_attention():
+    B, H, N, d = 2, 3, 11, 8
+    q, k, v, do = (rnd(910 + t, B, H, N, d) for t in range(4))
+    s = 0.3
+    o1, l1 = oracle.fwd_gqa(q, k, v, s, True, 0)
+    o2, l2 = oracle.fwd(q, k, v, s, True, 0)
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(l1, l2)
+    for a, b in zip(oracle.bwd_gqa(q, k, v, do, s, True, 0),
+                    oracle.bwd(q, k, v, do, s, True, 0)):
+        np.testing.assert_array_equal(a, b)
+
+
+def test_mqa_shared_head_gradient_is_sum_over_query_heads():
+    """With H identical query heads (same q and dO) sharing one key/value
+    head, dK and dV are exactly H times those of a single head."""
+    N, d, H = 13, 4, 4
+    q1, k, v, do1 = (rnd(920 + t, 1, 1, N, d) for t in range(4))
+    q, do = np.repeat(q1, H, axis=1), np.repeat(do1, H, axis=1)
+    _, dk, dv, _ = oracle.bwd_gqa(q, k, v, do, 0.5, False, 0)
+    _, dk1, dv1, _ = oracle.bwd(q1, k, v, do1, 0.5, False, 0)
+    np.testing.assert_allclose(dk, H * dk1, rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(dv, H * dv1, rtol=1e-13, atol=1e-14)
