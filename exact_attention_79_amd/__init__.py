@@ -30,7 +30,7 @@ class AttnDesc(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32),
                 ("N", ctypes.c_int32), ("d", ctypes.c_int32),
                 ("scale", ctypes.c_float), ("causal", ctypes.c_int32),
-                ("window", ctypes.c_int32)]
+                ("window", ctypes.c_int32), ("H_kv", ctypes.c_int32)]
 
 
 class AttnError(RuntimeError):
@@ -74,9 +74,9 @@ def status_str(status: int) -> str:
 
 
 def make_desc(B: int, H: int, N: int, d: int, scale: float, causal: bool,
-              window: int) -> AttnDesc:
+              window: int, H_kv: int = 0) -> AttnDesc:
     return AttnDesc(int(B), int(H), int(N), int(d), float(scale), int(bool(causal)),
-                    int(window))
+                    int(window), int(H_kv))
 
 
 def _ptr(t):
@@ -93,12 +93,19 @@ def _check(status: int, where: str):
 
 
 def _check_qkv(q, k, v, dtypes):
+    """q: [B, H, N, d]; k, v: [B, H_kv, N, d] with H a multiple of H_kv
+    (shared key/value heads; H_kv = H is ordinary multi-head attention)."""
     for t in (q, k, v):
         if not t.is_cuda or t.dtype not in dtypes or not t.is_contiguous():
             raise ValueError("q, k, v must be contiguous device tensors of dtype "
                              f"{dtypes}")
-        if t.dim() != 4 or t.shape != q.shape:
-            raise ValueError("q, k, v must all have shape [B, H, N, d]")
+        if t.dim() != 4:
+            raise ValueError("q, k, v must be 4-d tensors [B, heads, N, d]")
+    B, H, N, d = q.shape
+    Hkv = k.shape[1]
+    if (k.shape != (B, Hkv, N, d) or v.shape != k.shape or Hkv < 1 or H % Hkv):
+        raise ValueError("q must be [B, H, N, d] and k, v [B, H_kv, N, d] with H a "
+                         "multiple of H_kv")
 
 
 def attn_fwd(q, k, v, scale: float | None = None, causal: bool = False,
@@ -117,7 +124,7 @@ def attn_fwd(q, k, v, scale: float | None = None, causal: bool = False,
     if lse is not None and (not lse.is_cuda or lse.dtype != torch.float32
                             or lse.shape != (B, H, N) or not lse.is_contiguous()):
         raise ValueError("lse must be a contiguous fp32 device tensor [B, H, N]")
-    desc = make_desc(B, H, N, d, scale, causal, window)
+    desc = make_desc(B, H, N, d, scale, causal, window, k.shape[1])
     od = ATTN_OUT_F32 if out_dtype == torch.float32 else ATTN_OUT_BF16
     _check(lib.attn_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(o), od,
                         _ptr(lse), _stream()), "attn_fwd")
@@ -134,15 +141,15 @@ def attn_bwd(q, k, v, o, dout, lse, scale: float | None = None,
     """dQ, dK, dV (fp32) for bf16 q, k, v, o, dout and the forward's fp32 lse."""
     _check_qkv(q, k, v, (torch.bfloat16,))
     _check_like(q, torch.bfloat16, o=o, dout=dout)
-    desc = _bwd_desc(q, scale, causal, window)
+    desc = _bwd_desc(q, k, scale, causal, window)
     nbytes = int(lib.attn_bwd_workspace_bytes(ctypes.byref(desc)))
     if workspace is None:
         workspace = torch.empty(max(nbytes, 1), device=q.device, dtype=torch.uint8)
     if grads is None:
-        grads = tuple(torch.empty(q.shape, device=q.device, dtype=torch.float32)
-                      for _ in range(3))
+        grads = _new_grads(q, k)
     dq, dk, dv = grads
-    _check_like(q, torch.float32, dq=dq, dk=dk, dv=dv)
+    _check_like(q, torch.float32, dq=dq)
+    _check_like(k, torch.float32, dk=dk, dv=dv)
     _check_lse_ws(q, lse, workspace, desc)
     _check(lib.attn_bwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
                         _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
@@ -151,10 +158,17 @@ def attn_bwd(q, k, v, o, dout, lse, scale: float | None = None,
     return dq, dk, dv
 
 
-def _bwd_desc(q, scale, causal, window):
+def _bwd_desc(q, k, scale, causal, window):
+    """Descriptor from q's shape and, when given, the key/value head count of k."""
     B, H, N, d = q.shape
     scale = 1.0 / math.sqrt(d) if scale is None else scale
-    return make_desc(B, H, N, d, scale, causal, window)
+    return make_desc(B, H, N, d, scale, causal, window, 0 if k is None else k.shape[1])
+
+
+def _new_grads(q, k):
+    dq = torch.empty(q.shape, device=q.device, dtype=torch.float32)
+    dk, dv = (torch.empty(k.shape, device=q.device, dtype=torch.float32) for _ in range(2))
+    return dq, dk, dv
 
 
 def _check_like(ref, dtype, **tensors):
@@ -182,7 +196,7 @@ def _ws_bytes(workspace):
 def attn_bwd_preprocess(o, dout, lse, workspace, scale=None, causal=False, window=0):
     """Fills the workspace only: D = rowsum(dO * O) and L log2(e)."""
     _check_like(o, torch.bfloat16, o=o, dout=dout)
-    desc = _bwd_desc(o, scale, causal, window)
+    desc = _bwd_desc(o, None, scale, causal, window)
     _check_lse_ws(o, lse, workspace, desc)
     _check(lib.attn_bwd_preprocess(ctypes.byref(desc), _ptr(o), _ptr(dout), _ptr(lse),
                                    _ptr(workspace), _ws_bytes(workspace), _stream()),
@@ -192,9 +206,10 @@ def attn_bwd_preprocess(o, dout, lse, workspace, scale=None, causal=False, windo
 def attn_bwd_dq(q, k, v, o, dout, lse, workspace, dq, scale=None, causal=False,
                 window=0):
     """First backward stage: dQ (fp32); also fills the workspace (D, L log2(e))."""
-    _check_like(q, torch.bfloat16, q=q, k=k, v=v, o=o, dout=dout)
+    _check_qkv(q, k, v, (torch.bfloat16,))
+    _check_like(q, torch.bfloat16, o=o, dout=dout)
     _check_like(q, torch.float32, dq=dq)
-    desc = _bwd_desc(q, scale, causal, window)
+    desc = _bwd_desc(q, k, scale, causal, window)
     _check_lse_ws(q, lse, workspace, desc)
     _check(lib.attn_bwd_dq(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
                            _ptr(dout), _ptr(lse), _ptr(workspace), _ws_bytes(workspace),
@@ -205,9 +220,10 @@ def attn_bwd_dkdv(q, k, v, dout, workspace, dk, dv, scale=None, causal=False,
                   window=0):
     """Second backward stage: dK and dV (fp32), from the workspace that
     attn_bwd_dq (or attn_bwd_preprocess) filled."""
-    _check_like(q, torch.bfloat16, q=q, k=k, v=v, dout=dout)
-    _check_like(q, torch.float32, dk=dk, dv=dv)
-    desc = _bwd_desc(q, scale, causal, window)
+    _check_qkv(q, k, v, (torch.bfloat16,))
+    _check_like(q, torch.bfloat16, dout=dout)
+    _check_like(k, torch.float32, dk=dk, dv=dv)
+    desc = _bwd_desc(q, k, scale, causal, window)
     _check_lse_ws(q, None, workspace, desc)
     _check(lib.attn_bwd_dkdv(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(dout),
                              _ptr(workspace), _ws_bytes(workspace), _ptr(dk), _ptr(dv),
@@ -221,13 +237,12 @@ def attn_bwd_stages(q, k, v, o, dout, lse, scale: float | None = None,
     attn_bwd_dkdv (exactly what attn_bwd enqueues).  With preprocess=True:
     attn_bwd_preprocess, attn_bwd_dkdv, then attn_bwd_dq, so that dK and dV
     come from the workspace the preprocess filled."""
-    desc = _bwd_desc(q, scale, causal, window)
+    desc = _bwd_desc(q, k, scale, causal, window)
     if workspace is None:
         nbytes = int(lib.attn_bwd_workspace_bytes(ctypes.byref(desc)))
         workspace = torch.empty(max(nbytes, 1), device=q.device, dtype=torch.uint8)
     if grads is None:
-        grads = tuple(torch.empty(q.shape, device=q.device, dtype=torch.float32)
-                      for _ in range(3))
+        grads = _new_grads(q, k)
     dq, dk, dv = grads
     kw = dict(scale=scale, causal=causal, window=window)
     if preprocess:
@@ -243,8 +258,8 @@ def attn_bwd_stages(q, k, v, o, dout, lse, scale: float | None = None,
 def attn_fwd_fp8(q8, k8, v8, q_descale: float, k_descale: float, v_descale: float,
                  scale: float | None = None, causal: bool = False, window: int = 0,
                  out_dtype=torch.bfloat16, return_lse: bool = True, out=None, lse=None):
-    """O (and LSE) for e4m3 codes q8, k8, v8 (uint8 or float8_e4m3fn) [B, H, N, d];
-    the inputs are code * descale."""
+    """O (and LSE) for e4m3 codes (uint8 or float8_e4m3fn) q8 [B, H, N, d] and
+    k8, v8 [B, H_kv, N, d]; the inputs are code * descale."""
     _check_qkv(q8, k8, v8, (torch.uint8, torch.float8_e4m3fn))
     B, H, N, d = q8.shape
     scale = 1.0 / math.sqrt(d) if scale is None else scale
@@ -257,7 +272,7 @@ def attn_fwd_fp8(q8, k8, v8, q_descale: float, k_descale: float, v_descale: floa
     if lse is not None and (not lse.is_cuda or lse.dtype != torch.float32
                             or lse.shape != (B, H, N) or not lse.is_contiguous()):
         raise ValueError("lse must be a contiguous fp32 device tensor [B, H, N]")
-    desc = make_desc(B, H, N, d, scale, causal, window)
+    desc = make_desc(B, H, N, d, scale, causal, window, k8.shape[1])
     od = ATTN_OUT_F32 if out_dtype == torch.float32 else ATTN_OUT_BF16
     _check(lib.attn_fwd_fp8(ctypes.byref(desc), _ptr(q8), _ptr(k8), _ptr(v8),
                             float(q_descale), float(k_descale), float(v_descale),

@@ -11,11 +11,15 @@ namespace {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+// Key/value heads per batch element (H_kv = 0 means one per query head).
+int kv_heads(const attn_desc* d) { return d->H_kv > 0 ? d->H_kv : d->H; }
+
 attn_status check_desc(const attn_desc* d) {
   if (!d) return ATTN_EINVAL;
   if (d->B < 1 || d->H < 1 || d->N < 1) return ATTN_EINVAL;
   if (d->window < 0) return ATTN_EINVAL;
   if (d->causal != 0 && d->causal != 1) return ATTN_EINVAL;
+  if (d->H_kv < 0 || (d->H_kv > 0 && d->H % d->H_kv != 0)) return ATTN_EINVAL;
   if (!isfinite(d->scale) || !(d->scale > 0.f)) return ATTN_EINVAL;
   if (d->d != 64 && d->d != 128) return ATTN_EUNSUPPORTED;
   const int64_t elems = (int64_t)d->B * d->H * d->N * d->d;
@@ -43,6 +47,8 @@ attn::FwdArgs fwd_args(const attn_desc* d, const void* q, const void* k,
   a.o = o;
   a.lse = lse;
   a.BH = d->B * d->H;
+  a.H = d->H;
+  a.Hkv = kv_heads(d);
   a.N = d->N;
   a.d = d->d;
   a.scale = d->scale;
@@ -76,6 +82,8 @@ attn::BwdArgs bwd_args(const attn_desc* d, const void* q, const void* k,
   a.delta = (float*)workspace;
   a.lse2 = (float*)((char*)workspace + ws_array_bytes(d));
   a.BH = d->B * d->H;
+  a.H = d->H;
+  a.Hkv = kv_heads(d);
   a.N = d->N;
   a.d = d->d;
   a.scale = d->scale;

@@ -83,6 +83,7 @@ struct BwdKParams {
   const float* lse;  // natural-log L from the forward (dQ kernel)
   float* delta;      // workspace: D_i
   float* lse2;       // workspace: L_i log2(e)
+  int H, Hkv;        // query heads per batch element; key/value heads
   float* dq;
   float* dk;
   float* dv;
@@ -93,12 +94,15 @@ struct BwdKParams {
 };
 
 // ---------------------------------------------------------------- dK, dV
-// One workgroup per block of 32*NW keys; wave w owns keys kw0 .. kw0+31 (one
-// per lane on the MFMA N side).  Query tiles of BQ rows stream through
-// three LDS slots (Q, dO and their L, D) fetched one tile ahead by direct
-// global->LDS loads.  Iteration i computes S and dP for tile i+1 on the
-// matrix cores while the VALU forms P and dS for tile i, then accumulates
-// dV += P^T dO and dK += dS^T Q for tile i.
+// One workgroup per block of 32*NW keys of one key/value head; wave w owns
+// keys kw0 .. kw0+31 (one per lane on the MFMA N side).  Query tiles of BQ
+// rows stream through three LDS slots (Q, dO and their L, D) fetched one
+// tile ahead by direct global->LDS loads: the visible tiles of the first
+// query head that reads this key/value head, then those of the next one of
+// its group, and so on, so that dK and dV are summed over the group in
+// registers (the FLASH-ATTN page's MQA/GQA paragraph).  Iteration i computes
+// S and dP for tile i+1 on the matrix cores while the VALU forms P and dS
+// for tile i, then accumulates dV += P^T dO and dK += dS^T Q for tile i.
 template <int D, int NW, int BQ>
 __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(BwdKParams p) {
   constexpr int BKV = 32 * NW;
@@ -118,20 +122,18 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(BwdKParams p) {
   const int h = lane >> 5, n = lane & 31;
   // Low key blocks see the most queries under the causal mask: rank = block.
   const TileId id = tile_order(blockIdx.x, gridDim.x / p.n_tiles, p.n_tiles, p.causal);
-  const int bh = id.bh;
+  const int bkv = id.bh;  // key/value head (b * Hkv + hk)
   const int kt = id.rank;
   const int N = p.N, W = p.window;
+  const int G = p.H / p.Hkv;  // query heads reading this key/value head
+  const int bh0 = (bkv / p.Hkv) * p.H + (bkv % p.Hkv) * G;  // the first of them
   const int k0 = kt * BKV;
   const int kw0 = k0 + 32 * w;
   const int my_k = kw0 + n;
-  const size_t head = (size_t)bh * N * D;
+  const size_t head = (size_t)bkv * N * D;
   const uint32_t head_bytes = (uint32_t)N * D * 2;
-  const auto rq = make_rsrc(p.q + head, head_bytes);
   const auto rk = make_rsrc(p.k + head, head_bytes);
   const auto rv = make_rsrc(p.v + head, head_bytes);
-  const auto rdo = make_rsrc(p.dout + head, head_bytes);
-  const auto rl = make_rsrc(p.lse2 + (size_t)bh * N, (uint32_t)N * 4);
-  const auto rdl = make_rsrc(p.delta + (size_t)bh * N, (uint32_t)N * 4);
 
   // K^T and V^T as B operands (lane = key, 8 consecutive d per K-step).
   bf16x8 kop[KS], vop[KS];
@@ -160,12 +162,25 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(BwdKParams p) {
   const float s2 = p.scale * kLog2e;
   const TrCoord trc(lane);
 
-  auto load_tile = [&](int t, __bf16* Qf, __bf16* Of, float* Lf, float* Df) {
-    tile_load_lds<D, BQ, NW>(rq, t * BQ, Qf, w, lane);
-    tile_load_lds<D, BQ, NW>(rdo, t * BQ, Of, w, lane);
+  // Tiles are taken in the order (query head j of the group, tile t): the
+  // load cursor (lj, lt) runs two tiles ahead of the compute cursor ct.
+  // Past the last head it keeps reading the last head's rows (in bounds;
+  // those tiles are never used).
+  int lj = 0, lt = t_lo, ct = t_lo;
+  auto load_tile = [&](__bf16* Qf, __bf16* Of, float* Lf, float* Df) {
+    const int bhq = bh0 + min(lj, G - 1);
+    const size_t qhead = (size_t)bhq * N * D;
+    tile_load_lds<D, BQ, NW>(make_rsrc(p.q + qhead, head_bytes), lt * BQ, Qf, w, lane);
+    tile_load_lds<D, BQ, NW>(make_rsrc(p.dout + qhead, head_bytes), lt * BQ, Of, w, lane);
     if (w == 0) {
-      vec_load_lds<LDROWS>(rl, t * BQ, Lf, lane);
-      vec_load_lds<LDROWS>(rdl, t * BQ, Df, lane);
+      vec_load_lds<LDROWS>(make_rsrc(p.lse2 + (size_t)bhq * N, (uint32_t)N * 4), lt * BQ,
+                           Lf, lane);
+      vec_load_lds<LDROWS>(make_rsrc(p.delta + (size_t)bhq * N, (uint32_t)N * 4), lt * BQ,
+                           Df, lane);
+    }
+    if (++lt == t_hi) {
+      lt = t_lo;
+      ++lj;
     }
   };
   // S = Q K^T and dP = dO V^T for one tile (queries on M, this wave's keys on N).
@@ -183,21 +198,23 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(BwdKParams p) {
 
   // Prologue: tiles t_lo and t_lo+1; S, dP of the first tile.  Tiles past
   // the last visible one read as zeros (rows >= N) or are never used.
-  load_tile(t_lo, sQ0, sO0, sL0, sD0);
-  load_tile(t_lo + 1, sQ1, sO1, sL1, sD1);
+  load_tile(sQ0, sO0, sL0, sD0);
+  load_tile(sQ1, sO1, sL1, sD1);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   f32x16 scur[BQ / 32], dpcur[BQ / 32];
   sdp(sQ0, sO0, scur, dpcur);
 
-  // Iteration for query tile t: P, dS of tile t (slot c: Qc, Oc, Lc, Dc)
-  // while S, dP of tile t+1 (slot n: Qn, On) run on the matrix cores; tile
-  // t+2 is fetched into slot f (tile t-1's, fully consumed).
-  auto iteration = [&](int t, const __bf16* Qc, const __bf16* Oc, const float* Lc,
+  // Iteration for the tile u of the sequence (query tile ct): P, dS of tile
+  // u (slot c: Qc, Oc, Lc, Dc) while S, dP of tile u+1 (slot n: Qn, On) run
+  // on the matrix cores; tile u+2 is fetched into slot f (tile u-1's, fully
+  // consumed).
+  auto iteration = [&](const __bf16* Qc, const __bf16* Oc, const float* Lc,
                        const float* Dc, const __bf16* Qn, const __bf16* On, __bf16* Qf,
                        __bf16* Of, float* Lf, float* Df) {
-    load_tile(t + 2, Qf, Of, Lf, Df);
-    const int i0 = t * BQ;
+    load_tile(Qf, Of, Lf, Df);
+    const int i0 = ct * BQ;
+    if (++ct == t_hi) ct = t_lo;
     bool need_mask = false;
     if (p.causal) need_mask |= i0 < kw0 + 31;
     if (W > 0) {
@@ -294,10 +311,11 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(BwdKParams p) {
     }
   };
 
-  for (int t = t_lo; t < t_hi; t += 3) {
-    iteration(t, sQ0, sO0, sL0, sD0, sQ1, sO1, sQ2, sO2, sL2, sD2);
-    if (t + 1 < t_hi) iteration(t + 1, sQ1, sO1, sL1, sD1, sQ2, sO2, sQ0, sO0, sL0, sD0);
-    if (t + 2 < t_hi) iteration(t + 2, sQ2, sO2, sL2, sD2, sQ0, sO0, sQ1, sO1, sL1, sD1);
+  const int U = G * (t_hi - t_lo);  // tiles in the sequence
+  for (int u = 0; u < U; u += 3) {
+    iteration(sQ0, sO0, sL0, sD0, sQ1, sO1, sQ2, sO2, sL2, sD2);
+    if (u + 1 < U) iteration(sQ1, sO1, sL1, sD1, sQ2, sO2, sQ0, sO0, sL0, sD0);
+    if (u + 2 < U) iteration(sQ2, sO2, sL2, sD2, sQ0, sO0, sQ1, sO1, sL1, sD1);
   }
 
   if (my_k < N) {
@@ -342,10 +360,11 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdKParams p) {
   const int wq0 = q0 + 32 * w;
   const int my_q = wq0 + n;
   const size_t head = (size_t)bh * N * D;
+  const size_t kv_off = (size_t)kv_head(bh, p.H, p.Hkv) * N * D;
   const uint32_t head_bytes = (uint32_t)N * D * 2;
   const auto rq = make_rsrc(p.q + head, head_bytes);
-  const auto rk = make_rsrc(p.k + head, head_bytes);
-  const auto rv = make_rsrc(p.v + head, head_bytes);
+  const auto rk = make_rsrc(p.k + kv_off, head_bytes);
+  const auto rv = make_rsrc(p.v + kv_off, head_bytes);
   const auto rdo = make_rsrc(p.dout + head, head_bytes);
   const auto ro = make_rsrc(p.o + head, head_bytes);
 
@@ -516,6 +535,8 @@ static BwdKParams bwd_params(const BwdArgs& a, int tile_rows) {
   p.lse = a.lse;
   p.delta = a.delta;
   p.lse2 = a.lse2;
+  p.H = a.H;
+  p.Hkv = a.Hkv;
   p.dq = a.dq;
   p.dk = a.dk;
   p.dv = a.dv;
@@ -548,7 +569,9 @@ hipError_t launch_bwd_preprocess(const BwdArgs& a, hipStream_t stream) {
 
 hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream) {
   const BwdKParams p = bwd_params(a, 32 * kBwdWaves);
-  const dim3 grid((unsigned)(a.BH * p.n_tiles)), block(64 * kBwdWaves);
+  // One workgroup per key block of every key/value head.
+  const int BHkv = a.BH / a.H * a.Hkv;
+  const dim3 grid((unsigned)(BHkv * p.n_tiles)), block(64 * kBwdWaves);
   if (a.d == 128)
     hipLaunchKernelGGL((bwd_dkdv_kernel<128, kBwdWaves, kBwdQTile>), grid, block, 0,
                        stream, p);

@@ -102,6 +102,12 @@ __device__ __forceinline__ int xcd_remap(int wg, int total) {
   return (xcd < r) ? xcd * (q + 1) + local : r * (q + 1) + (xcd - r) * q + local;
 }
 
+// The key/value head that query head bh (= b * H + h) reads when H query
+// heads share Hkv key/value heads: consecutive query heads form a group.
+__device__ __forceinline__ int kv_head(int bh, int H, int Hkv) {
+  return (bh / H) * Hkv + (bh % H) / (H / Hkv);
+}
+
 // Which (batch*head, tile rank) workgroup wg of a grid of BH * n_tiles
 // works on.  Whole heads stay on one XCD.  With rank_major (uneven work:
 // rank 0 is the heaviest tile of a head) each XCD walks its heads rank by

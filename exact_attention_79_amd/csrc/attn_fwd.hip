@@ -45,6 +45,7 @@ struct FwdKParams {
   const __bf16* v;
   void* o;
   float* lse;
+  int H, Hkv;  // query heads per batch element; key/value heads
   int N;
   int n_qtiles;
   float scale;
@@ -77,10 +78,11 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdKParams p) {
   const int wq0 = q0 + 32 * w;             // first query of this wave
   const int my_q = wq0 + n;                // this lane's query
   const size_t head = (size_t)bh * N * D;
+  const size_t kv_off = (size_t)kv_head(bh, p.H, p.Hkv) * N * D;
   const uint32_t head_bytes = (uint32_t)N * D * 2;
   const auto rq = make_rsrc(p.q + head, head_bytes);
-  const auto rk = make_rsrc(p.k + head, head_bytes);
-  const auto rv = make_rsrc(p.v + head, head_bytes);
+  const auto rk = make_rsrc(p.k + kv_off, head_bytes);
+  const auto rv = make_rsrc(p.v + kv_off, head_bytes);
 
   // Q^T as the B operand of S^T = K Q^T: K-step ks covers d = 16ks..16ks+15,
   // lane holds d = 16ks + 8h .. +7 of its query (zero beyond N).
@@ -328,6 +330,8 @@ static hipError_t launch_fwd_cfg(const FwdArgs& a, hipStream_t stream) {
   p.v = (const __bf16*)a.v;
   p.o = a.o;
   p.lse = a.lse;
+  p.H = a.H;
+  p.Hkv = a.Hkv;
   p.N = a.N;
   p.n_qtiles = (a.N + 32 * NW - 1) / (32 * NW);
   p.scale = a.scale;

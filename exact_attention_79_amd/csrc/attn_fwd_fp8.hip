@@ -97,6 +97,7 @@ struct FwdFp8Params {
   const uint8_t* v;
   void* o;
   float* lse;
+  int H, Hkv;       // query heads per batch element; key/value heads
   int N;
   int n_qtiles;
   float scale;      // softmax scale s
@@ -130,10 +131,11 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8_kernel(FwdFp8Params p) {
   const int wq0 = q0 + 32 * w;
   const int my_q = wq0 + n;
   const size_t head = (size_t)bh * N * D;
+  const size_t kv_off = (size_t)kv_head(bh, p.H, p.Hkv) * N * D;
   const uint32_t head_bytes = (uint32_t)N * D;
   const auto rq = make_rsrc(p.q + head, head_bytes);
-  const auto rk = make_rsrc(p.k + head, head_bytes);
-  const auto rv = make_rsrc(p.v + head, head_bytes);
+  const auto rk = make_rsrc(p.k + kv_off, head_bytes);
+  const auto rv = make_rsrc(p.v + kv_off, head_bytes);
 
   // Q^T as the B operand of S^T = K Q^T: in K-step ks a lane holds the 32
   // bytes d = 64 ks + 32 h .. +31 of its query; K rows are read the same way.
@@ -405,6 +407,8 @@ static hipError_t launch_fp8_d(const FwdArgs& a, hipStream_t stream) {
   p.v = (const uint8_t*)a.v;
   p.o = a.o;
   p.lse = a.lse;
+  p.H = a.H;
+  p.Hkv = a.Hkv;
   p.N = a.N;
   p.n_qtiles = (a.N + 32 * NW - 1) / (32 * NW);
   p.scale = a.scale;

@@ -7,13 +7,15 @@
 
 namespace attn {
 
+// BH = B * H query heads; K and V (and dK, dV) have B * Hkv heads, and query
+// head h of batch b reads key/value head b * Hkv + h / (H / Hkv).
 struct FwdArgs {
   const void* q;       // bf16 [BH][N][d], or e4m3 codes for the fp8 kernel
-  const void* k;
+  const void* k;       // [B*Hkv][N][d]
   const void* v;
   void* o;             // bf16 or fp32 [BH][N][d]
   float* lse;          // fp32 [BH][N] or nullptr
-  int BH, N, d;
+  int BH, H, Hkv, N, d;
   float scale;         // softmax scale s
   int causal, window;
   int out_f32;         // 1: o is fp32, 0: bf16
@@ -22,17 +24,17 @@ struct FwdArgs {
 
 struct BwdArgs {
   const void* q;       // bf16 [BH][N][d]
-  const void* k;
+  const void* k;       // bf16 [B*Hkv][N][d]
   const void* v;
   const void* o;
   const void* dout;
   const float* lse;    // fp32 [BH][N]
   float* dq;           // fp32 [BH][N][d]
-  float* dk;
+  float* dk;           // fp32 [B*Hkv][N][d], summed over each head group
   float* dv;
   float* delta;        // fp32 [BH][N] workspace: D_i = sum_k dO_ik O_ik
   float* lse2;         // fp32 [BH][N] workspace: L_i log2(e)
-  int BH, N, d;
+  int BH, H, Hkv, N, d;
   float scale;
   int causal, window;
 };

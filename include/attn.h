@@ -26,8 +26,17 @@
  * Every query sees at least its own key when causal or windowed, so no row of
  * P is empty.
  *
- * Layouts.  Q, K, V, O, dO, dQ, dK, dV are dense [B][H][N][d] row-major (d
- * fastest, no padding); L and the backward workspace rows are [B][H][N].
+ * Shared key/value heads (multi-query and grouped-query attention, the
+ * FLASH-ATTN page's FlashAttention-2 section): with H_kv > 0, the H query
+ * heads of a batch element share H_kv key/value heads (H a multiple of
+ * H_kv); query head h reads key/value head h / (H / H_kv), i.e. consecutive
+ * query heads form a group.  Nothing is copied; the backward's dK and dV of
+ * a shared head are the sums over its group.  H_kv = 0 (or H) is ordinary
+ * multi-head attention, H_kv = 1 multi-query attention.
+ *
+ * Layouts.  Q, O, dO, dQ are dense [B][H][N][d] row-major (d fastest, no
+ * padding); K, V, dK, dV are [B][H_kv][N][d] (H_kv = H when desc->H_kv is
+ * 0); L and the backward workspace rows are [B][H][N].
  * bf16 is IEEE binary32 truncated to its upper 16 bits (round-to-nearest-even
  * when produced here).  fp8 inputs are OCP E4M3 ("fn": bias 7, max 448, no
  * infinities) with a per-tensor descale: value = code_value * descale.
@@ -41,8 +50,9 @@
  *
  * Errors.  Arguments are checked on the host before anything is launched:
  *   ATTN_EINVAL        null required pointer, B/H/N < 1, window < 0, scale not
- *                      finite or <= 0, causal not 0/1, pointer not 16-byte
- *                      aligned, output dtype unknown, workspace too small;
+ *                      finite or <= 0, causal not 0/1, H_kv < 0 or H not a
+ *                      multiple of H_kv, pointer not 16-byte aligned, output
+ *                      dtype unknown, workspace too small;
  *   ATTN_EUNSUPPORTED  d not in {64, 128}, or B*H*N*d >= 2^31;
  *   ATTN_EHIP          the HIP runtime reported an error at launch.
  * On ATTN_EINVAL / ATTN_EUNSUPPORTED nothing has been enqueued.
@@ -67,16 +77,17 @@ typedef enum {
 typedef enum { ATTN_OUT_BF16 = 0, ATTN_OUT_F32 = 1 } attn_out_dtype;
 
 typedef struct {
-  int32_t B, H, N, d; /* batch, heads, sequence length, head dim (64 or 128) */
-  float scale;        /* s in softmax(s * Q K^T); finite and > 0             */
-  int32_t causal;     /* 0 or 1                                              */
-  int32_t window;     /* 0 = no window; W > 0 as in the masking rule above   */
+  int32_t B, H, N, d; /* batch, query heads, sequence length, head dim (64/128) */
+  float scale;        /* s in softmax(s * Q K^T); finite and > 0                */
+  int32_t causal;     /* 0 or 1                                                 */
+  int32_t window;     /* 0 = no window; W > 0 as in the masking rule above      */
+  int32_t H_kv;       /* key/value heads: 0 = H; else a divisor of H (above)    */
 } attn_desc;
 
 /* Forward, bf16 inputs (FLASH-ATTN page, FlashAttention-2 section: the
  * unnormalised accumulator O~ <- diag(e^{m_old - m_new}) O~ + e^{S - m_new} V,
  * divided by l once at the end).
- *   q, k, v : bf16 [B,H,N,d]
+ *   q       : bf16 [B,H,N,d];  k, v : bf16 [B,H_kv,N,d]
  *   o       : [B,H,N,d], bf16 (o_dtype = ATTN_OUT_BF16) or fp32 (ATTN_OUT_F32)
  *   lse     : fp32 [B,H,N], natural-log LSE of the scaled, masked scores;
  *             may be NULL when the caller does not need it.               */
@@ -94,9 +105,11 @@ size_t attn_bwd_workspace_bytes(const attn_desc* desc);
  * carried through, dQ = s dS K and dK = s dS^T Q, and dsoftmax written out as
  * dS_ij = P_ij (dP_ij - D_i), D_i = sum_k dO_ik O_ik).  P is recomputed from
  * Q, K and the forward's L; it is never read from memory.
- *   q, k, v, o, dout : bf16 [B,H,N,d]  (o is the forward's bf16 output)
+ *   q, o, dout       : bf16 [B,H,N,d]  (o is the forward's bf16 output)
+ *   k, v             : bf16 [B,H_kv,N,d]
  *   lse              : fp32 [B,H,N] from attn_fwd with the same desc
- *   dq, dk, dv       : fp32 [B,H,N,d], overwritten
+ *   dq               : fp32 [B,H,N,d], overwritten
+ *   dk, dv           : fp32 [B,H_kv,N,d], overwritten (summed over groups)
  *   workspace        : device memory of at least attn_bwd_workspace_bytes */
 attn_status attn_bwd(const attn_desc* desc, const void* q, const void* k,
                      const void* v, const void* o, const void* dout,
@@ -131,7 +144,7 @@ attn_status attn_bwd_preprocess(const attn_desc* desc, const void* o,
 
 /* Forward with fp8 inputs (FLASH-ATTN page, FlashAttention-3 summary,
  * "Low-precision with FP8": both products on the fp8 matrix cores, one scale
- * per tensor).  q8, k8, v8 are E4M3 codes [B,H,N,d]; the real inputs are
+ * per tensor).  q8 [B,H,N,d] and k8, v8 [B,H_kv,N,d] are E4M3 codes; the inputs are
  * code * descale.  Within each 64-key tile the probabilities of every query
  * row are scaled by the power of two that brings the row's largest one into
  * [128, 256) and are carried as two E4M3 terms, hi + 2^-4 lo, through the

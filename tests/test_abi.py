@@ -62,6 +62,18 @@ def test_fwd_rejects_bad_descriptors(ea, field, value, expect):
     assert call_fwd(ea, desc) == expect
 
 
+@pytest.mark.parametrize("H,H_kv,expect", [(4, 3, 1), (4, -1, 1), (6, 4, 1), (4, 0, 0),
+                                            (4, 4, 0), (4, 2, 0), (4, 1, 0)])
+def test_shared_kv_head_counts(ea, H, H_kv, expect):
+    """H_kv must be 0 or a divisor of H: an invalid descriptor has no
+    workspace size (0) and is refused by every entry point."""
+    desc = ea.make_desc(1, H, 16, 64, 0.125, False, 0, H_kv)
+    ws = ea.lib.attn_bwd_workspace_bytes(ctypes.byref(desc))
+    assert (ws == 0) == (expect == 1)
+    if expect == 1:
+        assert call_fwd(ea, desc) == ea.ATTN_EINVAL
+
+
 def test_fwd_rejects_bad_pointers_and_dtype(ea):
     desc = ea.make_desc(1, 1, 16, 64, 0.125, False, 0)
     assert call_fwd(ea, desc, q=0) == ea.ATTN_EINVAL
