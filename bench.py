@@ -197,6 +197,55 @@ def run_step(launches, torch, record):
     return evs
 
 
+def measure_gqa(ea, torch, attn_synth, reps=10):
+    """Grouped-query attention at B4 H16 N2048 d128 with 4 key/value heads
+    (4 query heads per group), causal and non-causal: forward, dQ pass and
+    dK/dV pass, each timed with HIP events over `reps` launches.  Measured
+    after the timed step and reported beside it; it does not enter `value`.
+    Credited FLOPs as for ordinary attention (the query heads decide them)."""
+    import numpy as np
+    B, H, Hkv, N, d = 4, 16, 4, 2048, 128
+    bits = attn_synth.bf16_attention_inputs(2, B, H, N, d, with_dout=True)
+
+    def dev(x):
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(
+            torch.bfloat16).cuda()
+    q, do = dev(bits["q"]), dev(bits["do"])
+    k, v = dev(bits["k"][:, :Hkv]), dev(bits["v"][:, :Hkv])
+    out = {"workload": f"B{B} H{H} H_kv{Hkv} N{N} d{d}, bf16"}
+    for causal in (False, True):
+        o, lse = ea.attn_fwd(q, k, v, causal=causal)
+        ws = torch.empty(ea.attn_bwd_workspace_bytes(B, H, N, d), device="cuda",
+                         dtype=torch.uint8)
+        dq = torch.empty(q.shape, device="cuda", dtype=torch.float32)
+        dk, dv = (torch.empty(k.shape, device="cuda", dtype=torch.float32)
+                  for _ in range(2))
+        runs = {
+            "fwd": lambda: ea.attn_fwd(q, k, v, causal=causal, out=o, lse=lse),
+            "bwd_dq": lambda: ea.attn_bwd_dq(q, k, v, o, do, lse, ws, dq, causal=causal),
+            "bwd_dkdv": lambda: ea.attn_bwd_dkdv(q, k, v, do, ws, dk, dv, causal=causal),
+        }
+        f = credited_fwd_flops(B * H, N, d, causal, 0)
+        credit = {"fwd": f, "bwd_dq": 0.5 * f, "bwd_dkdv": 2.0 * f}
+        row = {}
+        for name, fn in runs.items():
+            fn()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / reps
+            row[name] = {"ms": round(ms, 4),
+                         "tflops": round(credit[name] / (ms * 1e-3) / 1e12, 1)}
+        tot = sum(r["ms"] for r in row.values())
+        row["fwd_bwd_tflops"] = round(3.5 * f / (tot * 1e-3) / 1e12, 1)
+        out["causal" if causal else "non_causal"] = row
+    return out
+
+
 def cpu_baseline(attn_synth, seconds_budget=16.0):
     """The fp64 oracle, as it stands, on a bounded sample of the same workload:
     for each of the four variants, forward + backward of heads (0,0), (0,1), ...
@@ -322,6 +371,7 @@ def main():
         "roofline": roofline,
         "breakdown": breakdown,
     }
+    out["gqa"] = measure_gqa(ea, torch, attn_synth)
     if args.hbm_copy_mib > 0:
         # fp32 -> bf16, so that the copy runs as an elementwise kernel (a
         # same-dtype copy may go to a DMA engine that the counters miss).
