@@ -61,6 +61,7 @@ def lib():
         L.oracle_online_fwd.argtypes = [i, i, d, i, lg, dp, dp, dp,
                                         ctypes.POINTER(lg), i, i, dp, dp]
         L.oracle_fwd_gqa.argtypes = [i, i, i, i, i, d, i, lg, dp, dp, dp, dp, dp, i]
+        L.oracle_fwd_decode.argtypes = [i, i, i, i, i, i, d, i, lg, dp, dp, dp, dp, dp, i]
         L.oracle_bwd_gqa.argtypes = [i, i, i, i, i, d, i, lg, dp, dp, dp, dp, dp, dp,
                                      dp, dp, i]
         _lib = L
@@ -201,3 +202,19 @@ def bwd_gqa(q, k, v, dout, scale: float, causal: bool = False, window: int = 0,
                          _p(q), _p(k), _p(v), _p(dout), _p(dq), _p(dk), _p(dv), _p(D),
                          int(nthreads))
     return dq, dk, dv, D
+
+
+def fwd_decode(q, k, v, scale: float, causal: bool = False, window: int = 0,
+               nthreads: int = 0):
+    """O and L for a block of Nq queries q [B, H, Nq, d] that are the last Nq
+    positions of a sequence of Nk keys k, v [B, Hkv, Nk, d]."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    assert q.ndim == 4 and k.ndim == 4 and v.shape == k.shape
+    B, H, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    assert k.shape == (B, Hkv, Nk, d) and H % Hkv == 0 and 1 <= Nq <= Nk
+    o = np.empty_like(q)
+    lse = np.empty(q.shape[:-1], np.float64)
+    lib().oracle_fwd_decode(B, H, Hkv, Nq, Nk, d, float(scale), int(causal), int(window),
+                            _p(q), _p(k), _p(v), _p(o), _p(lse), int(nthreads))
+    return o, lse

@@ -89,13 +89,13 @@ static double dot(const double* a, const double* b, int d) {
   return acc;
 }
 
-/* One query row i of one head: explicit score row S_i, its max m_i, the sum
- * l_i = sum_j exp(S_ij - m_i), the probability row P_i, O_i = P_i V and
- * L_i = m_i + ln(l_i).  srow and prow are caller scratch of length N. */
-static void fwd_row(int N, int d, double scale, int causal, long window,
-                    const double* q, const double* k, const double* v, long i,
-                    double* srow, double* prow, double* o_row, double* lse_out) {
-  const double* qi = q + (long)i * d;
+/* One query row qi, at position i among the N keys of one head: explicit
+ * score row S_i, its max m_i, the sum l_i = sum_j exp(S_ij - m_i), the
+ * probability row P_i, O_i = P_i V and L_i = m_i + ln(l_i).  srow and prow
+ * are caller scratch of length N. */
+static void query_row(int N, int d, double scale, int causal, long window,
+                      const double* qi, long i, const double* k, const double* v,
+                      double* srow, double* prow, double* o_row, double* lse_out) {
   double m = -INFINITY;
   for (long j = 0; j < N; ++j) {
     if (oracle_visible(i, j, causal, window)) {
@@ -118,6 +118,14 @@ static void fwd_row(int N, int d, double scale, int causal, long window,
     for (int c = 0; c < d; ++c) o_row[c] += prow[j] * vj[c];
   }
   if (lse_out) *lse_out = m + log(l);
+}
+
+/* Row i of one head whose queries and keys are the same N positions. */
+static void fwd_row(int N, int d, double scale, int causal, long window,
+                    const double* q, const double* k, const double* v, long i,
+                    double* srow, double* prow, double* o_row, double* lse_out) {
+  query_row(N, d, scale, causal, window, q + (long)i * d, i, k, v, srow, prow, o_row,
+            lse_out);
 }
 
 /* Forward over BH heads, every row.  q,k,v,o: [BH][N][d]; lse: [BH][N]
@@ -198,6 +206,35 @@ void oracle_fwd_gqa(int B, int H, int Hkv, int N, int d, double scale, int causa
       long qoff = bh * (long)N * d, kvoff = kv_head_of(bh, H, Hkv) * (long)N * d;
       fwd_row(N, d, scale, causal, window, q + qoff, k + kvoff, v + kvoff, i, srow,
               prow, o + r * d, lse ? lse + r : NULL);
+    }
+    free(srow);
+    free(prow);
+  }
+}
+
+/* A short block of Nq queries against Nk keys (decode: the FlashAttention-3
+ * page's point on inference, one new query per step against every cached
+ * key).  The block is the last Nq positions of the sequence: query row i sits
+ * at key position Nk - Nq + i and the masks of the ordinary forward apply to
+ * that position (causal: j <= Nk - Nq + i).  The pages fix no alignment for
+ * Nq < Nk; this one reduces to the ordinary forward when Nq = Nk.  Shared
+ * key/value heads as in oracle_fwd_gqa.
+ * q, o [B][H][Nq][d]; k, v [B][Hkv][Nk][d]; lse [B][H][Nq]. */
+void oracle_fwd_decode(int B, int H, int Hkv, int Nq, int Nk, int d, double scale,
+                       int causal, long window, const double* q, const double* k,
+                       const double* v, double* o, double* lse, int nthreads) {
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+  long total = (long)B * H * Nq;
+#pragma omp parallel
+  {
+    double* srow = (double*)malloc(sizeof(double) * (size_t)Nk);
+    double* prow = (double*)malloc(sizeof(double) * (size_t)Nk);
+#pragma omp for schedule(dynamic, 4)
+    for (long r = 0; r < total; ++r) {
+      long bh = r / Nq, i = r % Nq;
+      long kvoff = kv_head_of(bh, H, Hkv) * (long)Nk * d;
+      query_row(Nk, d, scale, causal, window, q + r * d, (long)(Nk - Nq) + i, k + kvoff,
+                v + kvoff, srow, prow, o + r * d, lse ? lse + r : NULL);
     }
     free(srow);
     free(prow);

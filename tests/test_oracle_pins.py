@@ -382,3 +382,59 @@ def test_mqa_shared_head_gradient_is_sum_over_query_heads():
     _, dk1, dv1, _ = oracle.bwd(q1, k, v, do1, 0.5, False, 0)
     np.testing.assert_allclose(dk, H * dk1, rtol=1e-13, atol=1e-14)
     np.testing.assert_allclose(dv, H * dv1, rtol=1e-13, atol=1e-14)
+
+
+# ---------------------------------------------------------------- decode
+def torch_mask_rect(Nq, Nk, causal, window):
+    """Visibility for queries at positions Nk - Nq .. Nk - 1 against Nk keys."""
+    i = torch.arange(Nk - Nq, Nk)[:, None]
+    j = torch.arange(Nk)[None, :]
+    m = torch.ones(Nq, Nk, dtype=torch.bool)
+    if causal:
+        m &= j <= i
+    if window > 0:
+        m &= (i - j).abs() < window
+    return m
+
+
+@pytest.mark.parametrize("B,H,Hkv,Nq,Nk,d", [(1, 2, 2, 1, 37, 8), (2, 4, 2, 3, 50, 4),
+                                             (1, 6, 1, 5, 64, 16), (1, 1, 1, 9, 9, 8)])
+@pytest.mark.parametrize("causal,window", [(False, 0), (True, 0), (True, 7), (False, 6)])
+def test_decode_matches_torch_sdpa(B, H, Hkv, Nq, Nk, d, causal, window):
+    """Queries as the last Nq positions of the key sequence: torch fp64 SDPA
+    with the rectangular mask, on key/value heads repeated per group."""
+    q = rnd(930, B, H, Nq, d)
+    k, v = rnd(931, B, Hkv, Nk, d), rnd(932, B, Hkv, Nk, d)
+    s = 1.0 / math.sqrt(d)
+    o, lse = oracle.fwd_decode(q, k, v, s, causal, window)
+    g = H // Hkv
+    tq = torch.from_numpy(q)
+    tk = torch.from_numpy(k).repeat_interleave(g, dim=1)
+    tv = torch.from_numpy(v).repeat_interleave(g, dim=1)
+    mask = torch_mask_rect(Nq, Nk, causal, window)
+    to = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=mask,
+                                                          scale=s)
+    ts = (tq @ tk.transpose(-1, -2).contiguous()) * s
+    tl = torch.logsumexp(ts.masked_fill(~mask, float("-inf")), dim=-1)
+    np.testing.assert_allclose(o, to.numpy(), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, tl.numpy(), rtol=0, atol=1e-12)
+
+
+def test_decode_with_full_query_block_is_the_forward():
+    B, H, N, d = 1, 2, 23, 8
+    q, k, v = (rnd(940 + t, B, H, N, d) for t in range(3))
+    for causal, window in ((False, 0), (True, 0), (True, 5)):
+        o1, l1 = oracle.fwd_decode(q, k, v, 0.4, causal, window)
+        o2, l2 = oracle.fwd(q, k, v, 0.4, causal, window)
+        np.testing.assert_array_equal(o1, o2)
+        np.testing.assert_array_equal(l1, l2)
+
+
+def test_decode_last_rows_of_the_forward():
+    """A block of the last Nq queries gives the forward's last Nq rows."""
+    B, H, N, d, Nq = 1, 1, 31, 4, 6
+    q, k, v = (rnd(950 + t, B, H, N, d) for t in range(3))
+    o, lse = oracle.fwd(q, k, v, 0.5, True, 9)
+    o2, l2 = oracle.fwd_decode(q[:, :, N - Nq:], k, v, 0.5, True, 9)
+    np.testing.assert_array_equal(o2, o[:, :, N - Nq:])
+    np.testing.assert_array_equal(l2, lse[:, :, N - Nq:])
