@@ -23,7 +23,8 @@ ATTN_OUT_BF16, ATTN_OUT_F32 = 0, 1
 
 # Entry points declared in include/attn.h.
 EXPORTS = ("attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_bwd_preprocess",
-           "attn_bwd_dkdv", "attn_bwd_dq", "attn_fwd_fp8", "attn_status_str")
+           "attn_bwd_dkdv", "attn_bwd_dq", "attn_fwd_fp8", "attn_decode_workspace_bytes",
+           "attn_fwd_decode", "attn_status_str")
 
 
 class AttnDesc(ctypes.Structure):
@@ -31,6 +32,13 @@ class AttnDesc(ctypes.Structure):
                 ("N", ctypes.c_int32), ("d", ctypes.c_int32),
                 ("scale", ctypes.c_float), ("causal", ctypes.c_int32),
                 ("window", ctypes.c_int32), ("H_kv", ctypes.c_int32)]
+
+
+class AttnDecodeDesc(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("H_kv", ctypes.c_int32),
+                ("N_q", ctypes.c_int32), ("N_k", ctypes.c_int32), ("d", ctypes.c_int32),
+                ("scale", ctypes.c_float), ("causal", ctypes.c_int32),
+                ("window", ctypes.c_int32)]
 
 
 class AttnError(RuntimeError):
@@ -61,6 +69,11 @@ def _load():
     L.attn_bwd_dkdv.restype = ctypes.c_int
     L.attn_fwd_fp8.argtypes = [dp, vp, vp, vp, f32, f32, f32, vp, i32, vp, vp]
     L.attn_fwd_fp8.restype = ctypes.c_int
+    ddp = ctypes.POINTER(AttnDecodeDesc)
+    L.attn_decode_workspace_bytes.argtypes = [ddp]
+    L.attn_decode_workspace_bytes.restype = sz
+    L.attn_fwd_decode.argtypes = [ddp, vp, vp, vp, vp, i32, vp, vp, sz, vp]
+    L.attn_fwd_decode.restype = ctypes.c_int
     L.attn_status_str.argtypes = [ctypes.c_int]
     L.attn_status_str.restype = ctypes.c_char_p
     return L
@@ -277,4 +290,53 @@ def attn_fwd_fp8(q8, k8, v8, q_descale: float, k_descale: float, v_descale: floa
     _check(lib.attn_fwd_fp8(ctypes.byref(desc), _ptr(q8), _ptr(k8), _ptr(v8),
                             float(q_descale), float(k_descale), float(v_descale),
                             _ptr(o), od, _ptr(lse), _stream()), "attn_fwd_fp8")
+    return (o, lse) if return_lse else o
+
+
+def make_decode_desc(B: int, H: int, H_kv: int, N_q: int, N_k: int, d: int, scale: float,
+                     causal: bool, window: int) -> AttnDecodeDesc:
+    return AttnDecodeDesc(int(B), int(H), int(H_kv), int(N_q), int(N_k), int(d),
+                          float(scale), int(bool(causal)), int(window))
+
+
+def attn_decode_workspace_bytes(B: int, H: int, H_kv: int, N_q: int, N_k: int, d: int,
+                                causal: bool = False, window: int = 0) -> int:
+    desc = make_decode_desc(B, H, H_kv, N_q, N_k, d, 1.0, causal, window)
+    return int(lib.attn_decode_workspace_bytes(ctypes.byref(desc)))
+
+
+def attn_fwd_decode(q, k, v, scale: float | None = None, causal: bool = False,
+                    window: int = 0, out_dtype=torch.bfloat16, return_lse: bool = True,
+                    out=None, lse=None, workspace=None):
+    """O (and LSE) for a block of N_q queries q [B, H, N_q, d] that are the last
+    N_q positions of the N_k keys k, v [B, H_kv, N_k, d] (bf16)."""
+    for t in (q, k, v):
+        if (not t.is_cuda or t.dtype != torch.bfloat16 or not t.is_contiguous()
+                or t.dim() != 4):
+            raise ValueError("q, k, v must be contiguous 4-d bf16 device tensors")
+    B, H, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    if k.shape != (B, Hkv, Nk, d) or v.shape != k.shape or H % Hkv or Nq > Nk:
+        raise ValueError("q must be [B, H, N_q, d], k and v [B, H_kv, N_k, d] with H a "
+                         "multiple of H_kv and N_q <= N_k")
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    if out_dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("out_dtype must be torch.bfloat16 or torch.float32")
+    o = torch.empty(q.shape, device=q.device, dtype=out_dtype) if out is None else out
+    _check_like(q, out_dtype, out=o)
+    if return_lse and lse is None:
+        lse = torch.empty((B, H, Nq), device=q.device, dtype=torch.float32)
+    if lse is not None and (not lse.is_cuda or lse.dtype != torch.float32
+                            or lse.shape != (B, H, Nq) or not lse.is_contiguous()):
+        raise ValueError("lse must be a contiguous fp32 device tensor [B, H, N_q]")
+    desc = make_decode_desc(B, H, Hkv, Nq, Nk, d, scale, causal, window)
+    need = int(lib.attn_decode_workspace_bytes(ctypes.byref(desc)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), device=q.device, dtype=torch.uint8)
+    if not workspace.is_cuda or _ws_bytes(workspace) < need:
+        raise ValueError(f"workspace must be a device tensor of >= {need} bytes")
+    od = ATTN_OUT_F32 if out_dtype == torch.float32 else ATTN_OUT_BF16
+    _check(lib.attn_fwd_decode(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(o), od,
+                               _ptr(lse), _ptr(workspace), _ws_bytes(workspace),
+                               _stream()), "attn_fwd_decode")
     return (o, lse) if return_lse else o

@@ -187,6 +187,75 @@ attn_status attn_fwd_fp8(const attn_desc* desc, const uint8_t* q8,
   return from_hip(attn::launch_fwd_fp8(a, (hipStream_t)stream));
 }
 
+}  // extern "C"
+
+namespace {
+
+attn_status check_decode_desc(const attn_decode_desc* d) {
+  if (!d) return ATTN_EINVAL;
+  if (d->B < 1 || d->H < 1 || d->N_q < 1 || d->N_k < 1 || d->N_q > d->N_k)
+    return ATTN_EINVAL;
+  if (d->window < 0 || (d->causal != 0 && d->causal != 1)) return ATTN_EINVAL;
+  if (d->H_kv < 0 || (d->H_kv > 0 && d->H % d->H_kv != 0)) return ATTN_EINVAL;
+  if (!isfinite(d->scale) || !(d->scale > 0.f)) return ATTN_EINVAL;
+  if (d->d != 64 && d->d != 128) return ATTN_EUNSUPPORTED;
+  const int64_t hkv = d->H_kv > 0 ? d->H_kv : d->H;
+  if ((int64_t)d->B * d->H * d->N_q * d->d >= ((int64_t)1 << 31) ||
+      (int64_t)d->B * hkv * d->N_k * d->d >= ((int64_t)1 << 31))
+    return ATTN_EUNSUPPORTED;
+  return ATTN_OK;
+}
+
+attn::DecodePlan decode_plan_of(const attn_decode_desc* d) {
+  return attn::decode_plan(d->B, d->H, d->H_kv > 0 ? d->H_kv : d->H, d->N_q, d->N_k,
+                           d->window);
+}
+
+size_t pad256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+}  // namespace
+
+extern "C" {
+
+size_t attn_decode_workspace_bytes(const attn_decode_desc* desc) {
+  if (check_decode_desc(desc) != ATTN_OK) return 0;
+  const attn::DecodePlan pl = decode_plan_of(desc);
+  const size_t rows = (size_t)desc->B * desc->H * desc->N_q;
+  return pad256(rows * pl.P * desc->d * sizeof(float)) + pad256(rows * pl.P * sizeof(float));
+}
+
+attn_status attn_fwd_decode(const attn_decode_desc* desc, const void* q, const void* k,
+                            const void* v, void* o, int32_t o_dtype, float* lse,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  attn_status st = check_decode_desc(desc);
+  if (st != ATTN_OK) return st;
+  if (o_dtype != ATTN_OUT_BF16 && o_dtype != ATTN_OUT_F32) return ATTN_EINVAL;
+  st = check_ptrs({q, k, v, o, workspace}, {lse});
+  if (st != ATTN_OK) return st;
+  if (workspace_bytes < attn_decode_workspace_bytes(desc)) return ATTN_EINVAL;
+  const attn::DecodePlan pl = decode_plan_of(desc);
+  attn::DecodeArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.opart = (float*)workspace;
+  a.lpart = (float*)((char*)workspace +
+                     pad256((size_t)desc->B * desc->H * desc->N_q * pl.P * desc->d * 4));
+  a.B = desc->B;
+  a.H = desc->H;
+  a.Hkv = desc->H_kv > 0 ? desc->H_kv : desc->H;
+  a.Nq = desc->N_q;
+  a.Nk = desc->N_k;
+  a.d = desc->d;
+  a.scale = desc->scale;
+  a.causal = desc->causal;
+  a.window = desc->window;
+  a.out_f32 = (o_dtype == ATTN_OUT_F32);
+  return from_hip(attn::launch_decode(a, (hipStream_t)stream));
+}
+
 const char* attn_status_str(attn_status s) {
   switch (s) {
     case ATTN_OK:

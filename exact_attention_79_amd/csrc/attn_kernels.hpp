@@ -39,7 +39,28 @@ struct BwdArgs {
   int causal, window;
 };
 
+// A block of Nq queries (the last Nq positions) against Nk keys, split over
+// the keys into P chunks whose partial results are merged.
+struct DecodeArgs {
+  const void* q;       // bf16 [B*H][Nq][d]
+  const void* k;       // bf16 [B*Hkv][Nk][d]
+  const void* v;
+  void* o;             // bf16 or fp32 [B*H][Nq][d]
+  float* lse;          // fp32 [B*H][Nq] or nullptr
+  float* opart;        // workspace: fp32 [B*H*Nq][P][d]
+  float* lpart;        // workspace: fp32 [B*H*Nq][P]
+  int B, H, Hkv, Nq, Nk, d;
+  float scale;
+  int causal, window, out_f32;
+};
+struct DecodePlan {
+  int G, R, RB;        // query heads per key/value head, their rows, row blocks
+  int P, CW, kmin;     // chunks, keys per chunk, first key any row sees
+};
+DecodePlan decode_plan(int B, int H, int Hkv, int Nq, int Nk, int window);
+
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream);
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_fwd_fp8(const FwdArgs& a, hipStream_t stream);
 // The backward stages; launch_bwd = dq (which also fills the workspace),
 // then dkdv.  preprocess fills the workspace on its own.

@@ -156,6 +156,34 @@ attn_status attn_fwd_fp8(const attn_desc* desc, const uint8_t* q8,
                          float k_descale, float v_descale, void* o,
                          int32_t o_dtype, float* lse, void* stream);
 
+/* A short block of queries against a long key/value sequence (decode): the
+ * N_q queries of each head are the last N_q positions of a sequence of N_k
+ * keys, so query row i sits at key position N_k - N_q + i and the masks above
+ * apply to that position (causal: key j visible iff j <= N_k - N_q + i; the
+ * pages fix no alignment for N_q < N_k, and this one gives attn_fwd's rows
+ * when N_q = N_k).  Decode is bound by reading K and V once (FlashAttention-3
+ * page, the point on inference), so the keys are split into chunks that run
+ * in parallel, each giving a partial (O_c, L_c) per query row, and a second
+ * launch merges them with the softmax decomposition of the FLASH-ATTN page
+ * ("Tiling and Recomputation"): L = ln sum_c e^{L_c}, O = sum_c e^{L_c - L} O_c.
+ *   q        : bf16 [B,H,N_q,d];  k, v : bf16 [B,H_kv,N_k,d] (H_kv = 0 means H)
+ *   o, lse   : as attn_fwd, [B,H,N_q,d] and [B,H,N_q] (lse may be NULL)
+ *   workspace: device memory of at least attn_decode_workspace_bytes(desc)
+ *              bytes (the partials); its contents on entry do not matter.
+ * Errors as above, and ATTN_EINVAL when N_q < 1 or N_q > N_k. */
+typedef struct {
+  int32_t B, H, H_kv; /* batch, query heads, key/value heads (0 = H)        */
+  int32_t N_q, N_k, d; /* queries per head, keys per head, head dim (64/128) */
+  float scale;        /* s in softmax(s * Q K^T); finite and > 0             */
+  int32_t causal;     /* 0 or 1                                              */
+  int32_t window;     /* 0 = no window; W > 0 as in the masking rule above   */
+} attn_decode_desc;
+
+size_t attn_decode_workspace_bytes(const attn_decode_desc* desc);
+attn_status attn_fwd_decode(const attn_decode_desc* desc, const void* q, const void* k,
+                            const void* v, void* o, int32_t o_dtype, float* lse,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static, human-readable text for a status code. */
 const char* attn_status_str(attn_status status);
 

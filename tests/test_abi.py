@@ -27,7 +27,8 @@ def ea():
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted(
         ["attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_bwd_preprocess",
-         "attn_bwd_dkdv", "attn_bwd_dq", "attn_fwd_fp8", "attn_status_str"])
+         "attn_bwd_dkdv", "attn_bwd_dq", "attn_fwd_fp8", "attn_decode_workspace_bytes",
+         "attn_fwd_decode", "attn_status_str"])
 
 
 def test_library_exports_every_declared_symbol(ea):
@@ -132,3 +133,32 @@ def test_binding_refuses_host_tensors(ea):
     q = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         ea.attn_fwd(q, q, q)
+
+
+@pytest.mark.parametrize("field,value,expect", [
+    ("N_q", 0, 1), ("N_q", 100, 1), ("N_k", 0, 1), ("H_kv", 3, 1), ("H_kv", -1, 1),
+    ("window", -2, 1), ("scale", 0.0, 1), ("d", 96, 2), ("causal", 3, 1),
+])
+def test_decode_rejects_bad_descriptors(ea, field, value, expect):
+    desc = ea.make_decode_desc(1, 4, 2, 4, 64, 64, 0.125, True, 0)
+    assert ea.lib.attn_decode_workspace_bytes(ctypes.byref(desc)) > 0
+    setattr(desc, field, value)
+    assert ea.lib.attn_decode_workspace_bytes(ctypes.byref(desc)) == 0
+    vp = ctypes.c_void_p
+    f = vp(FAKE)
+    assert ea.lib.attn_fwd_decode(ctypes.byref(desc), f, f, f, f, 0, None, f, 1 << 30,
+                                  None) == expect
+
+
+def test_decode_rejects_small_workspace_and_null_pointers(ea):
+    desc = ea.make_decode_desc(2, 8, 2, 1, 5000, 128, 0.1, False, 0)
+    ws = ea.lib.attn_decode_workspace_bytes(ctypes.byref(desc))
+    assert ws > 0 and ws % 256 == 0
+    vp = ctypes.c_void_p
+    f = vp(FAKE)
+    assert ea.lib.attn_fwd_decode(ctypes.byref(desc), f, f, f, f, 0, None, f, ws - 1,
+                                  None) == ea.ATTN_EINVAL
+    assert ea.lib.attn_fwd_decode(ctypes.byref(desc), f, None, f, f, 0, None, f, ws,
+                                  None) == ea.ATTN_EINVAL
+    assert ea.lib.attn_fwd_decode(ctypes.byref(desc), f, f, f, f, 5, None, f, ws,
+                                  None) == ea.ATTN_EINVAL
