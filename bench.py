@@ -246,6 +246,40 @@ def measure_gqa(ea, torch, attn_synth, reps=10):
     return out
 
 
+def measure_decode(ea, torch, attn_synth, reps=20):
+    """Decode: one query per head at the end of a 32768-key sequence, B4 H32
+    with 8 key/value heads, d128 (attn_fwd_decode: key-split pass + merge).
+    HBM-bound: algorithmic bytes = K and V read once + Q read + O written.
+    Measured after the timed step; it does not enter `value`."""
+    import numpy as np
+    B, H, Hkv, Nq, Nk, d = 4, 32, 8, 1, 32768, 128
+    qb = attn_synth.bf16_attention_inputs(7, B, H, Nq, d)["q"]
+    kv = attn_synth.bf16_attention_inputs(8, B, Hkv, Nk, d)
+
+    def dev(x):
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(
+            torch.bfloat16).cuda()
+    q, k, v = dev(qb), dev(kv["k"]), dev(kv["v"])
+    o, lse = ea.attn_fwd_decode(q, k, v)
+    ws = torch.empty(ea.attn_decode_workspace_bytes(B, H, Hkv, Nq, Nk, d), device="cuda",
+                     dtype=torch.uint8)
+    fn = lambda: ea.attn_fwd_decode(q, k, v, out=o, lse=lse, workspace=ws)
+    fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    nbytes = 2 * B * Hkv * Nk * d * 2 + 2 * B * H * Nq * d * 2
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    return {"workload": f"B{B} H{H} H_kv{Hkv} N_q{Nq} N_k{Nk} d{d}, bf16, non-causal",
+            "us": round(ms * 1e3, 1), "algorithmic_bytes": nbytes,
+            "gbps": round(gbps, 1), "frac_of_hbm": round(gbps / HBM_GBPS, 4)}
+
+
 def cpu_baseline(attn_synth, seconds_budget=16.0):
     """The fp64 oracle, as it stands, on a bounded sample of the same workload:
     for each of the four variants, forward + backward of heads (0,0), (0,1), ...
@@ -372,6 +406,7 @@ def main():
         "breakdown": breakdown,
     }
     out["gqa"] = measure_gqa(ea, torch, attn_synth)
+    out["decode"] = measure_decode(ea, torch, attn_synth)
     if args.hbm_copy_mib > 0:
         # fp32 -> bf16, so that the copy runs as an elementwise kernel (a
         # same-dtype copy may go to a DMA engine that the counters miss).

@@ -206,27 +206,69 @@ struct DecMergeParams {
   int P, out_f32;
 };
 
-// One workgroup per query row, one thread per output element:
-// L = ln sum_c e^{L_c}, O = sum_c e^{L_c - L} O_c.
+// One workgroup of 256 threads per query row: L = ln sum_c e^{L_c} and
+// O = sum_c e^{L_c - L} O_c.  The weights e^{L_c - L} are formed once in LDS;
+// the 256 / D slices of threads then each sum every (256/D)-th partial for
+// all D elements (coalesced rows of O_c) and the slices are added in LDS.
 template <int D>
-__global__ __launch_bounds__(D) void decode_merge_kernel(DecMergeParams p) {
-  const int rg = blockIdx.x, d = threadIdx.x;
+__global__ __launch_bounds__(256) void decode_merge_kernel(DecMergeParams p) {
+  constexpr int NT = 256, S = NT / D;
+  __shared__ float sW[1024];
+  __shared__ float sRed[NT];
+  const int rg = blockIdx.x, tid = threadIdx.x;
   const float* L = p.lpart + (size_t)rg * p.P;
+  // max_c L_c
   float m = -__builtin_inff();
-  for (int c = 0; c < p.P; ++c) m = fmaxf(m, L[c]);
+  for (int c = tid; c < p.P; c += NT) {
+    const float x = L[c];
+    sW[c] = x;
+    m = fmaxf(m, x);
+  }
+  sRed[tid] = m;
+  __syncthreads();
+  for (int k = NT / 2; k > 0; k >>= 1) {
+    if (tid < k) sRed[tid] = fmaxf(sRed[tid], sRed[tid + k]);
+    __syncthreads();
+  }
+  m = sRed[0];
+  __syncthreads();
+  // sum_c e^{L_c - m}
   float s = 0.f;
-  for (int c = 0; c < p.P; ++c)
-    if (L[c] != -__builtin_inff()) s += __expf(L[c] - m);
-  const float lt = m + __logf(s);
-  float acc = 0.f;
+  for (int c = tid; c < p.P; c += NT)
+    if (sW[c] != -__builtin_inff()) s += __expf(sW[c] - m);
+  sRed[tid] = s;
+  __syncthreads();
+  for (int k = NT / 2; k > 0; k >>= 1) {
+    if (tid < k) sRed[tid] += sRed[tid + k];
+    __syncthreads();
+  }
+  const float lt = m + __logf(sRed[0]);
+  for (int c = tid; c < p.P; c += NT)
+    sW[c] = (sW[c] == -__builtin_inff()) ? 0.f : __expf(sW[c] - lt);
+  __syncthreads();
+  // slice sl sums partials sl, sl + S, ... for element d
+  const int d = tid % D, sl = tid / D;
   const float* O = p.opart + (size_t)rg * p.P * D + d;
-  for (int c = 0; c < p.P; ++c)
-    if (L[c] != -__builtin_inff()) acc = fmaf(__expf(L[c] - lt), O[(size_t)c * D], acc);
-  if (p.out_f32)
-    ((float*)p.o)[(size_t)rg * D + d] = acc;
-  else
-    ((__bf16*)p.o)[(size_t)rg * D + d] = (__bf16)acc;
-  if (d == 0 && p.lse) p.lse[rg] = lt;
+  float a0 = 0.f, a1 = 0.f;
+  int c = sl;
+  for (; c + S < p.P; c += 2 * S) {
+    a0 = fmaf(sW[c], O[(size_t)c * D], a0);
+    a1 = fmaf(sW[c + S], O[(size_t)(c + S) * D], a1);
+  }
+  if (c < p.P) a0 = fmaf(sW[c], O[(size_t)c * D], a0);
+  __syncthreads();
+  sRed[tid] = a0 + a1;
+  __syncthreads();
+  if (sl == 0) {
+    float acc = sRed[d];
+#pragma unroll
+    for (int k = 1; k < S; ++k) acc += sRed[k * D + d];
+    if (p.out_f32)
+      ((float*)p.o)[(size_t)rg * D + d] = acc;
+    else
+      ((__bf16*)p.o)[(size_t)rg * D + d] = (__bf16)acc;
+    if (d == 0 && p.lse) p.lse[rg] = lt;
+  }
 }
 
 DecodePlan decode_plan(int B, int H, int Hkv, int Nq, int Nk, int window) {
@@ -295,9 +337,9 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   m.out_f32 = a.out_f32;
   const unsigned rows = (unsigned)((long)a.B * a.H * a.Nq);
   if (a.d == 128)
-    hipLaunchKernelGGL((decode_merge_kernel<128>), dim3(rows), dim3(128), 0, stream, m);
+    hipLaunchKernelGGL((decode_merge_kernel<128>), dim3(rows), dim3(256), 0, stream, m);
   else
-    hipLaunchKernelGGL((decode_merge_kernel<64>), dim3(rows), dim3(64), 0, stream, m);
+    hipLaunchKernelGGL((decode_merge_kernel<64>), dim3(rows), dim3(256), 0, stream, m);
   return hipGetLastError();
 }
 
