@@ -15,7 +15,7 @@ from __future__ import annotations
 
 import numpy as np
 
-T_Q, T_K, T_V, T_DO, T_OUTLIER = 0, 1, 2, 3, 4
+T_Q, T_K, T_V, T_DO, T_OUTLIER, T_SIGNS = 0, 1, 2, 3, 4, 5
 E4M3_MAX = 448.0
 
 
@@ -106,4 +106,69 @@ def fp8_attention_inputs(workload: int, B: int, H: int, N: int, d: int,
         descale = amax / E4M3_MAX if amax > 0 else 1.0
         out[name] = e4m3_codes(x / descale)
         out[name + "_descale"] = descale
+    return out
+
+
+def sylvester_hadamard(d: int) -> np.ndarray:
+    """The d x d Hadamard matrix of Sylvester's construction (d a power of 2):
+    H_1 = [1], H_2n = [[H_n, H_n], [H_n, -H_n]]."""
+    assert d >= 1 and d & (d - 1) == 0
+    h = np.ones((1, 1))
+    while h.shape[0] < d:
+        h = np.block([[h, h], [h, -h]])
+    return h
+
+
+def incoherent_matrix(workload: int, d: int) -> np.ndarray:
+    """A random orthogonal d x d matrix M = diag(s) H_d / sqrt(d) with seeded
+    random signs s (the randomness of incoherent processing, drawn here and
+    handed to both sides as part of the inputs)."""
+    rng = np.random.Generator(np.random.PCG64(seed_of(workload, T_SIGNS)))
+    signs = rng.choice(np.array([-1.0, 1.0]), size=d)
+    return signs[:, None] * sylvester_hadamard(d) / np.sqrt(d)
+
+
+def _quantise_rows(x: np.ndarray, block_rows):
+    """e4m3 codes of x [..., R, d]: one descale per tensor (block_rows None)
+    or per block of block_rows rows of each head, descale = amax / 448."""
+    if block_rows is None:
+        amax = float(np.abs(x).max())
+        descale = float(np.float32(amax / E4M3_MAX)) if amax > 0 else 1.0
+        return e4m3_codes(x / descale), descale
+    R = x.shape[-2]
+    nblk = (R + block_rows - 1) // block_rows
+    descales = np.empty(x.shape[:-2] + (nblk,), np.float64)
+    codes = np.empty(x.shape, np.uint8)
+    for b in range(nblk):
+        blk = x[..., b * block_rows:(b + 1) * block_rows, :]
+        amax = np.abs(blk).max(axis=(-2, -1))
+        # fp32-representable, as the kernel receives them
+        ds = np.where(amax > 0, amax / E4M3_MAX, 1.0).astype(np.float32).astype(np.float64)
+        descales[..., b] = ds
+        codes[..., b * block_rows:(b + 1) * block_rows, :] = e4m3_codes(blk / ds[..., None, None])
+    return codes, descales
+
+
+def fp8_attention_inputs_v2(workload: int, B: int, H: int, N: int, d: int,
+                            blocks: bool = False, incoherent: bool = False,
+                            outlier_scale: float = 10.0,
+                            outlier_fraction: float = 0.01) -> dict:
+    """The fp64 Q, K, V of fp8_attention_inputs (same seeds and outlier
+    channels), optionally with incoherent processing (Q and K multiplied by
+    incoherent_matrix before quantising), quantised per tensor or per block
+    (128 query rows, 64 key/value rows of each head; descales fp64 arrays).
+    Returns the codes, the descales and the original fp64 tensors ("q_in",
+    "k_in", "v_in") for measuring the error against unquantised attention."""
+    shape = (B, H, N, d)
+    ch = outlier_channels(workload, d, outlier_fraction)
+    out = {"channels": ch}
+    m = incoherent_matrix(workload, d) if incoherent else None
+    for name, t, rows in (("q", T_Q, 128), ("k", T_K, 64), ("v", T_V, 64)):
+        x = normal(seed_of(workload, t), shape)
+        if outlier_scale != 1.0:
+            x[..., ch] *= outlier_scale
+        out[name + "_in"] = x
+        if m is not None and name in ("q", "k"):
+            x = x @ m
+        out[name], out[name + "_descale"] = _quantise_rows(x, rows if blocks else None)
     return out

@@ -24,7 +24,7 @@ ATTN_OUT_BF16, ATTN_OUT_F32 = 0, 1
 # Entry points declared in include/attn.h.
 EXPORTS = ("attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_bwd_preprocess",
            "attn_bwd_dkdv", "attn_bwd_dq", "attn_fwd_fp8", "attn_decode_workspace_bytes",
-           "attn_fwd_decode", "attn_status_str")
+           "attn_fwd_decode", "attn_fwd_fp8_blocks", "attn_status_str")
 
 
 class AttnDesc(ctypes.Structure):
@@ -69,6 +69,8 @@ def _load():
     L.attn_bwd_dkdv.restype = ctypes.c_int
     L.attn_fwd_fp8.argtypes = [dp, vp, vp, vp, f32, f32, f32, vp, i32, vp, vp]
     L.attn_fwd_fp8.restype = ctypes.c_int
+    L.attn_fwd_fp8_blocks.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp]
+    L.attn_fwd_fp8_blocks.restype = ctypes.c_int
     ddp = ctypes.POINTER(AttnDecodeDesc)
     L.attn_decode_workspace_bytes.argtypes = [ddp]
     L.attn_decode_workspace_bytes.restype = sz
@@ -339,4 +341,35 @@ def attn_fwd_decode(q, k, v, scale: float | None = None, causal: bool = False,
     _check(lib.attn_fwd_decode(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(o), od,
                                _ptr(lse), _ptr(workspace), _ws_bytes(workspace),
                                _stream()), "attn_fwd_decode")
+    return (o, lse) if return_lse else o
+
+
+def attn_fwd_fp8_blocks(q8, k8, v8, q_descales, k_descales, v_descales,
+                        scale: float | None = None, causal: bool = False, window: int = 0,
+                        out_dtype=torch.bfloat16, return_lse: bool = True, out=None,
+                        lse=None):
+    """fp8 forward with one descale per block: q_descales fp32 [B, H, ceil(N/128)],
+    k_descales and v_descales fp32 [B, H_kv, ceil(N/64)] (device tensors)."""
+    _check_qkv(q8, k8, v8, (torch.uint8, torch.float8_e4m3fn))
+    B, H, N, d = q8.shape
+    Hkv = k8.shape[1]
+    shapes = {"q_descales": (q_descales, (B, H, (N + 127) // 128)),
+              "k_descales": (k_descales, (B, Hkv, (N + 63) // 64)),
+              "v_descales": (v_descales, (B, Hkv, (N + 63) // 64))}
+    for name, (t, shp) in shapes.items():
+        if (not t.is_cuda or t.dtype != torch.float32 or tuple(t.shape) != shp
+                or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous fp32 device tensor {shp}")
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    if out_dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("out_dtype must be torch.bfloat16 or torch.float32")
+    o = torch.empty(q8.shape, device=q8.device, dtype=out_dtype) if out is None else out
+    _check_like(q8, out_dtype, out=o)
+    if return_lse and lse is None:
+        lse = torch.empty((B, H, N), device=q8.device, dtype=torch.float32)
+    desc = make_desc(B, H, N, d, scale, causal, window, Hkv)
+    od = ATTN_OUT_F32 if out_dtype == torch.float32 else ATTN_OUT_BF16
+    _check(lib.attn_fwd_fp8_blocks(ctypes.byref(desc), _ptr(q8), _ptr(k8), _ptr(v8),
+                                   _ptr(q_descales), _ptr(k_descales), _ptr(v_descales),
+                                   _ptr(o), od, _ptr(lse), _stream()), "attn_fwd_fp8_blocks")
     return (o, lse) if return_lse else o

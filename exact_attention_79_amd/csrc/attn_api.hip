@@ -56,6 +56,7 @@ attn::FwdArgs fwd_args(const attn_desc* d, const void* q, const void* k,
   a.window = d->window;
   a.out_f32 = (o_dtype == ATTN_OUT_F32);
   a.q_descale = a.k_descale = a.v_descale = 1.f;
+  a.q_scales = a.k_scales = a.v_scales = nullptr;
   return a;
 }
 
@@ -184,6 +185,26 @@ attn_status attn_fwd_fp8(const attn_desc* desc, const uint8_t* q8,
   a.q_descale = q_descale;
   a.k_descale = k_descale;
   a.v_descale = v_descale;
+  return from_hip(attn::launch_fwd_fp8(a, (hipStream_t)stream));
+}
+
+attn_status attn_fwd_fp8_blocks(const attn_desc* desc, const uint8_t* q8,
+                                const uint8_t* k8, const uint8_t* v8,
+                                const float* q_descales, const float* k_descales,
+                                const float* v_descales, void* o, int32_t o_dtype,
+                                float* lse, void* stream) {
+  attn_status st = check_desc(desc);
+  if (st != ATTN_OK) return st;
+  if (o_dtype != ATTN_OUT_BF16 && o_dtype != ATTN_OUT_F32) return ATTN_EINVAL;
+  st = check_ptrs({q8, k8, v8, o}, {lse});
+  if (st != ATTN_OK) return st;
+  if (!q_descales || !k_descales || !v_descales || ((uintptr_t)q_descales & 3) ||
+      ((uintptr_t)k_descales & 3) || ((uintptr_t)v_descales & 3))
+    return ATTN_EINVAL;
+  attn::FwdArgs a = fwd_args(desc, q8, k8, v8, o, o_dtype, lse);
+  a.q_scales = q_descales;
+  a.k_scales = k_descales;
+  a.v_scales = v_descales;
   return from_hip(attn::launch_fwd_fp8(a, (hipStream_t)stream));
 }
 

@@ -101,12 +101,17 @@ struct FwdFp8Params {
   int N;
   int n_qtiles;
   float scale;      // softmax scale s
-  float qk_descale; // dq * dk
-  float v_descale;
+  // Descales: one per tensor (q_descale, k_descale, v_descale), or, when
+  // the arrays are given, one per block: qs[b*H+h][query block of BR rows],
+  // ks and vs [b*Hkv+h][key block of BC rows].
+  float q_descale, k_descale, v_descale;
+  const float* qs;
+  const float* ks;
+  const float* vs;
   int causal, window, out_f32;
 };
 
-template <int D, int NW>
+template <int D, int NW, bool BLOCKS>
 __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8_kernel(FwdFp8Params p) {
   constexpr int BC = 64;  // keys per tile = one 64-deep fp8 MFMA step
   constexpr int BR = 32 * NW;
@@ -160,9 +165,23 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8_kernel(FwdFp8Params p) {
   f32x16 oacc[D / 32];
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) oacc[dt] = (f32x16){};
+  // The running max M is kept in base-2 logit units (s * q.k * log2 e), so
+  // that tiles with different key descales compare directly: tile t's raw
+  // code products are scaled by s2t(t) = s2q * dk(t).
   float m_run = kMaxInit, l_run = 0.f;
-  const float s2 = p.scale * p.qk_descale * kLog2e;
-  const float tau = 8.0f / s2;
+  const int kvh = kv_head(bh, p.H, p.Hkv);
+  const int n_kt = (N + BC - 1) / BC;
+  const float s2q = p.scale * kLog2e * (BLOCKS ? p.qs[(size_t)bh * p.n_qtiles + qt] : p.q_descale);
+  const float s2k = s2q * p.k_descale;  // per-tensor key descale
+  auto s2t = [&](int t) {
+    return BLOCKS ? s2q * p.ks[(size_t)kvh * n_kt + min(t, n_kt - 1)] : s2k;
+  };
+  // With block descales, log2 of tile t's value descale, folded into the
+  // weights of that tile; a per-tensor value descale is applied once in the
+  // epilogue instead (exactly).
+  auto vlog = [&](int t) {
+    return BLOCKS ? __builtin_amdgcn_logf(p.vs[(size_t)kvh * n_kt + min(t, n_kt - 1)]) : 0.f;
+  };
 
   // K row reads: the A operand of K-step ks for M-tile mt (32 bytes of row
   // 32 mt + n: chunks 4 ks + 2 h and 4 ks + 2 h + 1).
@@ -236,12 +255,13 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8_kernel(FwdFp8Params p) {
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[mt][r]);
     return mx;
   };
-  // Running max update for a tile whose in-lane max is mx; returns the
-  // tile's row max (both wave halves).
-  auto update_max = [&](float mx) {
-    mx = halves_max(mx);
-    const float m_new = (mx > m_run + tau) ? mx : m_run;
-    const float alpha = fast_exp2((m_run - m_new) * s2);
+  // Running max update for a tile whose in-lane raw max is mx and whose
+  // scale is st; returns the tile's row max in logit units (both halves).
+  // The max only moves when it grows by more than 8 (2^8 in weight).
+  auto update_max = [&](float mx, float st) {
+    mx = halves_max(mx) * st;
+    const float m_new = (mx > m_run + 8.f) ? mx : m_run;
+    const float alpha = fast_exp2(m_run - m_new);
     m_run = m_new;
     if (__ballot(alpha != 1.f)) {
       l_run *= alpha;
@@ -261,7 +281,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8_kernel(FwdFp8Params p) {
   f32x16 scur[2];
   scores(sK0, scur);
   mask_tile(t_lo, scur);
-  float tmx = update_max(tile_max(scur));
+  float tmx = update_max(tile_max(scur), s2t(t_lo));
 
   constexpr int kLoadsPerIter = 2 * (BC * D / 16) / (64 * NW);
   constexpr int kWaitOlderLoads = waitcnt_vm(kLoadsPerIter);
@@ -273,13 +293,14 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8_kernel(FwdFp8Params p) {
                        uint8_t* Vf) {
     tile_load_lds8<D, BC, NW, false>(rk, (t + 3) * BC, Kf, w, lane);
     tile_load_lds8<D, BC, NW, true>(rv, (t + 2) * BC, Vf, w, lane);
-    // Block scale of this tile's probabilities: the row's largest weight
-    // 2^y (y = s2 tmx - s2 m_run <= 8) is brought into [128, 256) by 2^-e,
-    // e = floor(y) - 7, folded into the exponent of every weight.
-    const float mb = m_run * s2;
-    const float y = fmaxf(tmx * s2 - mb, -200.f);
+    // Weights of this tile, times its value descale dv: the row's largest
+    // one, 2^y (y = tmx - M + log2 dv), is brought into [128, 256) by 2^-e,
+    // e = floor(y) - 7; both factors are folded into the exponent of every
+    // weight, and the MFMA's block scale 2^e puts 2^e back.
+    const float s2 = s2t(t), lv = vlog(t);
+    const float y = fmaxf(tmx - m_run + lv, -200.f);
     const int e = max(-123, min(127, (int)floorf(y) - 7));
-    const float mbe = mb + (float)e;
+    const float mbe = m_run + (float)e - lv;
 
     // Bundles 0..NS-1: the next tile's score MFMAs, each with a slice of
     // this tile's weights (exp2, then e4m3 hi and 16x residual lo terms);
@@ -350,13 +371,14 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8_kernel(FwdFp8Params p) {
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    l_run += __builtin_ldexpf(lsum, e);
+    // l sums the weights themselves: lsum 2^e / dv.
+    l_run += BLOCKS ? __builtin_ldexpf(lsum, e) * fast_exp2(-lv) : __builtin_ldexpf(lsum, e);
     if (t + 1 < t_hi) {
       float mx = part[0];
 #pragma unroll
       for (int c = 1; c < NCH; ++c) mx = fmaxf(mx, part[c]);
       if (mask_tile(t + 1, snext)) mx = tile_max(snext);
-      tmx = update_max(mx);
+      tmx = update_max(mx, s2t(t + 1));
     }
     // The loads issued one iteration ago (K_{t+2}, V_{t+1}) have landed for
     // this wave; after the barrier they have for every wave, and the slots
@@ -376,7 +398,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8_kernel(FwdFp8Params p) {
 
   const float l_tot = halves_sum(l_run);
   if (my_q < N) {
-    const float inv = p.v_descale / l_tot;
+    const float inv = (BLOCKS ? 1.f : p.v_descale) / l_tot;
     const size_t row = head + (size_t)my_q * D;
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
@@ -394,7 +416,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8_kernel(FwdFp8Params p) {
       }
     if (h == 0 && p.lse)
       p.lse[(size_t)bh * N + my_q] =
-          (m_run * s2 + __builtin_amdgcn_logf(l_tot)) * kLn2;
+          (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
   }
 }
 
@@ -412,13 +434,21 @@ static hipError_t launch_fp8_d(const FwdArgs& a, hipStream_t stream) {
   p.N = a.N;
   p.n_qtiles = (a.N + 32 * NW - 1) / (32 * NW);
   p.scale = a.scale;
-  p.qk_descale = a.q_descale * a.k_descale;
+  p.q_descale = a.q_descale;
+  p.k_descale = a.k_descale;
   p.v_descale = a.v_descale;
+  p.qs = a.q_scales;
+  p.ks = a.k_scales;
+  p.vs = a.v_scales;
   p.causal = a.causal;
   p.window = a.window;
   p.out_f32 = a.out_f32;
   const unsigned grid = (unsigned)(a.BH * p.n_qtiles);
-  hipLaunchKernelGGL((fwd_fp8_kernel<D, NW>), dim3(grid), dim3(NW * 64), 0, stream, p);
+  if (a.q_scales)
+    hipLaunchKernelGGL((fwd_fp8_kernel<D, NW, true>), dim3(grid), dim3(NW * 64), 0, stream, p);
+  else
+    hipLaunchKernelGGL((fwd_fp8_kernel<D, NW, false>), dim3(grid), dim3(NW * 64), 0, stream,
+                       p);
   return hipGetLastError();
 }
 

@@ -19,7 +19,10 @@ struct FwdArgs {
   float scale;         // softmax scale s
   int causal, window;
   int out_f32;         // 1: o is fp32, 0: bf16
-  float q_descale, k_descale, v_descale;  // fp8 only
+  float q_descale, k_descale, v_descale;  // fp8 only: one per tensor, or
+  const float* q_scales;  // ... one per block (nullptr: per tensor): [BH][N/128]
+  const float* k_scales;  // [B*Hkv][N/64]
+  const float* v_scales;  // [B*Hkv][N/64]
 };
 
 struct BwdArgs {

@@ -156,6 +156,25 @@ attn_status attn_fwd_fp8(const attn_desc* desc, const uint8_t* q8,
                          float k_descale, float v_descale, void* o,
                          int32_t o_dtype, float* lse, void* stream);
 
+/* The fp8 forward with one descale per block instead of per tensor (the
+ * FLASH-ATTN page's FlashAttention-3 summary, block quantisation: Q, K, V cut
+ * into row blocks that are quantised independently, the S tiles rescaled by
+ * the blocks' factors at no extra cost).  Block sizes are this kernel's
+ * tiles: 128 query rows, 64 key rows.
+ *   q_descales : fp32 [B,H,ceil(N/128)]   (query block qb covers rows 128 qb ..)
+ *   k_descales : fp32 [B,H_kv,ceil(N/64)] (key block kb covers rows 64 kb ..)
+ *   v_descales : fp32 [B,H_kv,ceil(N/64)]
+ * The real inputs are code * the descale of the code's block; every descale
+ * must be finite and > 0 (device memory: not checked).  Incoherent processing
+ * (multiplying Q and K by one random orthogonal matrix before quantising,
+ * same page) needs nothing from the kernel, since (QM)(KM)^T = QK^T: the
+ * caller transforms and quantises.  Other arguments as attn_fwd_fp8. */
+attn_status attn_fwd_fp8_blocks(const attn_desc* desc, const uint8_t* q8,
+                                const uint8_t* k8, const uint8_t* v8,
+                                const float* q_descales, const float* k_descales,
+                                const float* v_descales, void* o, int32_t o_dtype,
+                                float* lse, void* stream);
+
 /* A short block of queries against a long key/value sequence (decode): the
  * N_q queries of each head are the last N_q positions of a sequence of N_k
  * keys, so query row i sits at key position N_k - N_q + i and the masks above

@@ -49,6 +49,7 @@ def lib():
         i, lg, d = ctypes.c_int, ctypes.c_long, ctypes.c_double
         L.oracle_bf16_decode.argtypes = [ctypes.c_void_p, dp, lg]
         L.oracle_e4m3_decode.argtypes = [ctypes.c_void_p, d, dp, lg]
+        L.oracle_e4m3_decode_blocks.argtypes = [ctypes.c_void_p, lg, lg, i, i, dp, dp]
         L.oracle_e4m3_to_f64.argtypes = [ctypes.c_uint8]
         L.oracle_e4m3_to_f64.restype = d
         L.oracle_visible.argtypes = [lg, lg, i, lg]
@@ -90,6 +91,20 @@ def decode_e4m3(codes: np.ndarray, descale: float = 1.0) -> np.ndarray:
     codes = np.ascontiguousarray(codes, dtype=np.uint8)
     out = np.empty(codes.shape, np.float64)
     lib().oracle_e4m3_decode(codes.ctypes.data, float(descale), _p(out), codes.size)
+    return out
+
+
+def decode_e4m3_blocks(codes: np.ndarray, descales: np.ndarray, block_rows: int) -> np.ndarray:
+    """e4m3 codes [..., R, d] with one descale per block of block_rows rows of
+    each head (descales [..., ceil(R / block_rows)]) -> exact fp64 values."""
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    R, d = codes.shape[-2:]
+    heads = int(np.prod(codes.shape[:-2])) if codes.ndim > 2 else 1
+    ds = _f64(descales)
+    assert ds.shape == codes.shape[:-2] + ((R + block_rows - 1) // block_rows,)
+    out = np.empty(codes.shape, np.float64)
+    lib().oracle_e4m3_decode_blocks(codes.ctypes.data, heads, R, d, block_rows, _p(ds),
+                                    _p(out))
     return out
 
 

@@ -72,6 +72,20 @@ void oracle_e4m3_decode(const uint8_t* src, double descale, double* dst, long n)
   for (long i = 0; i < n; ++i) dst[i] = oracle_e4m3_to_f64(src[i]) * descale;
 }
 
+/* Block-quantised tensor [heads][rows][d]: row r of head h is code value *
+ * descales[h * nblk + r / block_rows] (FLASH-ATTN page, FlashAttention-3
+ * summary, block quantisation: one scale per block of rows). */
+void oracle_e4m3_decode_blocks(const uint8_t* src, long heads, long rows, int d,
+                               int block_rows, const double* descales, double* dst) {
+  const long nblk = (rows + block_rows - 1) / block_rows;
+  for (long hh = 0; hh < heads; ++hh)
+    for (long r = 0; r < rows; ++r) {
+      const double ds = descales[hh * nblk + r / block_rows];
+      const long off = (hh * rows + r) * d;
+      for (int c = 0; c < d; ++c) dst[off + c] = oracle_e4m3_to_f64(src[off + c]) * ds;
+    }
+}
+
 /* ---- visibility: which keys a query may attend to ---- */
 int oracle_visible(long i, long j, int causal, long window) {
   if (causal && j > i) return 0;

@@ -28,7 +28,7 @@ def test_header_declares_the_boundary():
     assert declared_functions() == sorted(
         ["attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_bwd_preprocess",
          "attn_bwd_dkdv", "attn_bwd_dq", "attn_fwd_fp8", "attn_decode_workspace_bytes",
-         "attn_fwd_decode", "attn_status_str"])
+         "attn_fwd_decode", "attn_fwd_fp8_blocks", "attn_status_str"])
 
 
 def test_library_exports_every_declared_symbol(ea):

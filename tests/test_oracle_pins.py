@@ -438,3 +438,30 @@ def test_decode_last_rows_of_the_forward():
     o2, l2 = oracle.fwd_decode(q[:, :, N - Nq:], k, v, 0.5, True, 9)
     np.testing.assert_array_equal(o2, o[:, :, N - Nq:])
     np.testing.assert_array_equal(l2, lse[:, :, N - Nq:])
+
+
+# ---------------------------------------------------------------- fp8 blocks
+def test_block_decode_matches_per_block_scaling():
+    """Block decode = per-tensor decode of each block with its own descale
+    (checked against torch's e4m3 conversion)."""
+    codes = np.random.Generator(np.random.PCG64(960)).integers(0, 256, (2, 3, 10, 4),
+                                                              dtype=np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0x10  # no NaN codes
+    ds = np.array([[[0.5, 2.0, 0.25], [1.0, 3.0, 0.125], [4.0, 1.5, 0.75]],
+                   [[0.1, 0.2, 0.3], [0.4, 0.5, 0.6], [0.7, 0.8, 0.9]]])
+    got = oracle.decode_e4m3_blocks(codes, ds, 4)
+    t = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    for b in range(3):
+        np.testing.assert_array_equal(got[:, :, 4 * b:4 * b + 4],
+                                      t[:, :, 4 * b:4 * b + 4] * ds[:, :, b, None, None])
+
+
+def test_incoherent_matrix_is_orthogonal_and_keeps_scores():
+    for d in (64, 128):
+        m = attn_synth.incoherent_matrix(3, d)
+        np.testing.assert_allclose(m @ m.T, np.eye(d), atol=1e-13)
+        q, k = rnd(970, 5, d), rnd(971, 7, d)
+        np.testing.assert_allclose((q @ m) @ (k @ m).T, q @ k.T, atol=1e-12)
+    h = attn_synth.sylvester_hadamard(4)
+    np.testing.assert_array_equal(h, [[1, 1, 1, 1], [1, -1, 1, -1], [1, 1, -1, -1],
+                                      [1, -1, -1, 1]])
