@@ -22,7 +22,7 @@ it is null.  --hbm-copy-mib M adds, after the timed region, one plain
 device-to-device copy of M MiB whose known size calibrates those counters.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                       [--hbm-copy-mib M]
+                       [--no-extra-paths] [--hbm-copy-mib M]
 """
 from __future__ import annotations
 
@@ -72,6 +72,9 @@ def parse_args():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra-paths", action="store_true",
+                    help="skip the grouped-query and decode measurements that follow the "
+                         "timed step (for profiler runs that should see the step only)")
     ap.add_argument("--hbm-copy-mib", type=int, default=0,
                     help="after timing, one fp32 -> bf16 copy of this many MiB of "
                          "fp32 (counter calibration for rocprofv3 --pmc runs)")
@@ -405,8 +408,9 @@ def main():
         "roofline": roofline,
         "breakdown": breakdown,
     }
-    out["gqa"] = measure_gqa(ea, torch, attn_synth)
-    out["decode"] = measure_decode(ea, torch, attn_synth)
+    if not args.no_extra_paths:
+        out["gqa"] = measure_gqa(ea, torch, attn_synth)
+        out["decode"] = measure_decode(ea, torch, attn_synth)
     if args.hbm_copy_mib > 0:
         # fp32 -> bf16, so that the copy runs as an elementwise kernel (a
         # same-dtype copy may go to a DMA engine that the counters miss).
