@@ -65,6 +65,19 @@ def lib():
         L.oracle_fwd_decode.argtypes = [i, i, i, i, i, i, d, i, lg, dp, dp, dp, dp, dp, i]
         L.oracle_bwd_gqa.argtypes = [i, i, i, i, i, d, i, lg, dp, dp, dp, dp, dp, dp,
                                      dp, dp, i]
+        u64, u32 = ctypes.c_uint64, ctypes.c_uint32
+        pu64 = ctypes.POINTER(ctypes.c_uint64)
+        L.oracle_philox.argtypes = [i, i, pu64, pu64, pu64]
+        L.oracle_philox_constants.argtypes = [i, pu64]
+        L.oracle_dropout_threshold.argtypes = [d]
+        L.oracle_dropout_threshold.restype = i
+        L.oracle_dropout_byte.argtypes = [u64, u32, lg, lg, lg]
+        L.oracle_dropout_byte.restype = i
+        L.oracle_dropout_mask.argtypes = [u64, u32, i, lg, lg, lg, lg, lg, ctypes.c_void_p]
+        L.oracle_fwd_dropout.argtypes = [i, i, i, i, i, d, i, lg, d, u64, u32,
+                                         dp, dp, dp, dp, dp, i]
+        L.oracle_bwd_dropout.argtypes = [i, i, i, i, i, d, i, lg, d, u64, u32,
+                                         dp, dp, dp, dp, dp, dp, dp, dp, i]
         _lib = L
     return _lib
 
@@ -233,3 +246,75 @@ def fwd_decode(q, k, v, scale: float, causal: bool = False, window: int = 0,
     lib().oracle_fwd_decode(B, H, Hkv, Nq, Nk, d, float(scale), int(causal), int(window),
                             _p(q), _p(k), _p(v), _p(o), _p(lse), int(nthreads))
     return o, lse
+
+
+# ---- dropout ----
+
+def _u64(words):
+    a = np.ascontiguousarray(words, dtype=np.uint64)
+    return a, a.ctypes.data_as(ctypes.POINTER(ctypes.c_uint64))
+
+
+def philox(width: int, rounds: int, counter, key) -> np.ndarray:
+    """Philox-4x<width>-<rounds> of one 4-word counter and 2-word key (uint64 words)."""
+    assert width in (32, 64) and rounds >= 1
+    c, cp = _u64(counter)
+    k, kp = _u64(key)
+    assert c.shape == (4,) and k.shape == (2,)
+    out, op = _u64(np.zeros(4))
+    lib().oracle_philox(width, rounds, cp, kp, op)
+    return out
+
+
+def philox_constants(width: int) -> np.ndarray:
+    """(M0, M1, W0, W1) of the width-bit Philox."""
+    out, op = _u64(np.zeros(4))
+    lib().oracle_philox_constants(width, op)
+    return out
+
+
+def dropout_threshold(p: float) -> int:
+    """Integer threshold t = round(256 p); bytes below t are dropped."""
+    return int(lib().oracle_dropout_threshold(float(p)))
+
+
+def dropout_byte(seed: int, offset: int, bh: int, i: int, j: int) -> int:
+    return int(lib().oracle_dropout_byte(seed, offset, bh, i, j))
+
+
+def dropout_mask(seed: int, offset: int, p: float, bh: int, rows: int, cols: int,
+                 i0: int = 0, j0: int = 0) -> np.ndarray:
+    """Keep indicators Z (uint8 0/1) of query head bh, rows i0.., keys j0..."""
+    z = np.empty((rows, cols), np.uint8)
+    lib().oracle_dropout_mask(seed, offset, dropout_threshold(p), bh, i0, j0, rows, cols,
+                              z.ctypes.data)
+    return z
+
+
+def fwd_dropout(q, k, v, scale: float, p: float, seed: int, offset: int = 0,
+                causal: bool = False, window: int = 0, nthreads: int = 0):
+    """O (with dropout on P) and L for q [B, H, N, d], k, v [B, Hkv, N, d]."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, H, Hkv, N, d = _gqa_shapes(q, k)
+    assert v.shape == k.shape
+    o = np.empty_like(q)
+    lse = np.empty(q.shape[:-1], np.float64)
+    lib().oracle_fwd_dropout(B, H, Hkv, N, d, float(scale), int(causal), int(window),
+                             float(p), int(seed), int(offset), _p(q), _p(k), _p(v), _p(o),
+                             _p(lse), int(nthreads))
+    return o, lse
+
+
+def bwd_dropout(q, k, v, dout, scale: float, p: float, seed: int, offset: int = 0,
+                causal: bool = False, window: int = 0, nthreads: int = 0):
+    """dQ, dK, dV (summed over each group) and D of attention with dropout on P."""
+    q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+    B, H, Hkv, N, d = _gqa_shapes(q, k)
+    assert v.shape == k.shape and dout.shape == q.shape
+    dq = np.empty_like(q)
+    dk, dv = np.empty_like(k), np.empty_like(k)
+    D = np.empty(q.shape[:-1], np.float64)
+    lib().oracle_bwd_dropout(B, H, Hkv, N, d, float(scale), int(causal), int(window),
+                             float(p), int(seed), int(offset), _p(q), _p(k), _p(v),
+                             _p(dout), _p(dq), _p(dk), _p(dv), _p(D), int(nthreads))
+    return dq, dk, dv, D

@@ -25,6 +25,16 @@
  * softmax Jacobian dS_ij = P_ij (dP_ij - sum_k P_ik dP_ik) and the scale s
  * carried through the chain rule into dQ and dK.
  *
+ * Dropout (named by the FLASH-ATTN page as a supported variant, and in the
+ * FlashAttention-2 "Background" paragraph as an elementwise operation on P):
+ * the pages fix no random-number contract, so the reading taken here is
+ * inverted dropout on the normalised probabilities, P~ = P o Z / q with
+ * keep indicators Z drawn by the counter-based generator Philox-4x32-10
+ * (oracle_philox), keep probability q = (256 - t) / 256 for the integer
+ * threshold t = round(256 p), and L the log-sum-exp of the undropped scores.
+ * The backward applies the same Z: dV = P~^T dO, dP = (dO V^T) o Z / q,
+ * D_i = sum_j P_ij dP_ij, dS = P o (dP - D), dQ = s dS K, dK = s dS^T Q.
+ *
  * Every quantity is an explicit fp64 array: one full score row per query in
  * the forward, and the full N x N matrices P and dS of one head in the
  * backward.  No blocking, no fused recurrence: the online (block-by-block)
@@ -416,4 +426,203 @@ void oracle_bwd_gqa(int B, int H, int Hkv, int N, int d, double scale, int causa
   }
   free(dk1);
   free(dv1);
+}
+
+/* ---- dropout: counter-based random numbers and the keep rule ---- */
+
+/* Philox-4xW-R (Salmon, Moraes, Dror and Shaw, "Parallel random numbers: as
+ * easy as 1, 2, 3", SC 2011): a 4-word counter and a 2-word key; each of R
+ * rounds multiplies counter words 0 and 2 by the constants M0, M1 into
+ * double-width products, and the new counter is
+ *   (hi(M1 c2) ^ c1 ^ k0, lo(M1 c2), hi(M0 c0) ^ c3 ^ k1, lo(M0 c0));
+ * between rounds the key words grow by the Weyl constants W0, W1.  One
+ * routine serves both word widths, W = 32 and W = 64 (all words are held in
+ * uint64_t; at W = 32 only their low halves are used). */
+static const uint64_t PHILOX_M[2][2] = {{0xD2511F53ull, 0xCD9E8D57ull},
+                                        {0xD2E7470EE14C6C93ull, 0xCA5A826395121157ull}};
+static const uint64_t PHILOX_WEYL[2][2] = {{0x9E3779B9ull, 0xBB67AE85ull},
+                                           {0x9E3779B97F4A7C15ull, 0xBB67AE8584CAA73Bull}};
+
+static void mulhilo(int W, uint64_t a, uint64_t b, uint64_t* hi, uint64_t* lo) {
+  if (W == 32) {
+    const uint64_t p = a * b; /* both < 2^32: exact in 64 bits */
+    *hi = p >> 32;
+    *lo = p & 0xFFFFFFFFull;
+  } else {
+    const unsigned __int128 p = (unsigned __int128)a * b;
+    *hi = (uint64_t)(p >> 64);
+    *lo = (uint64_t)p;
+  }
+}
+
+/* W in {32, 64}; R >= 1 rounds. */
+void oracle_philox(int W, int R, const uint64_t ctr_in[4], const uint64_t key_in[2],
+                   uint64_t out[4]) {
+  const int wi = (W == 64);
+  const uint64_t mask = wi ? ~0ull : 0xFFFFFFFFull;
+  uint64_t c[4], k[2];
+  for (int x = 0; x < 4; ++x) c[x] = ctr_in[x] & mask;
+  for (int x = 0; x < 2; ++x) k[x] = key_in[x] & mask;
+  for (int r = 0; r < R; ++r) {
+    if (r > 0) {
+      k[0] = (k[0] + PHILOX_WEYL[wi][0]) & mask;
+      k[1] = (k[1] + PHILOX_WEYL[wi][1]) & mask;
+    }
+    uint64_t hi0, lo0, hi1, lo1;
+    mulhilo(W, PHILOX_M[wi][0], c[0], &hi0, &lo0);
+    mulhilo(W, PHILOX_M[wi][1], c[2], &hi1, &lo1);
+    const uint64_t n0 = hi1 ^ c[1] ^ k[0], n2 = hi0 ^ c[3] ^ k[1];
+    c[0] = n0;
+    c[1] = lo1;
+    c[2] = n2;
+    c[3] = lo0;
+  }
+  for (int x = 0; x < 4; ++x) out[x] = c[x];
+}
+
+void oracle_philox_constants(int W, uint64_t out[4]) {
+  const int wi = (W == 64);
+  out[0] = PHILOX_M[wi][0];
+  out[1] = PHILOX_M[wi][1];
+  out[2] = PHILOX_WEYL[wi][0];
+  out[3] = PHILOX_WEYL[wi][1];
+}
+
+/* Threshold t = round(256 p) (halves up) of a dropout probability p. */
+int oracle_dropout_threshold(double p) { return (int)floor(p * 256.0 + 0.5); }
+
+/* The random byte of (query head bh, query i, key j): the score matrix of a
+ * head is cut into 4 x 4 sub-blocks; sub-block (i/4, j/4) draws one
+ * Philox-4x32-10 output with counter (j/4, i/4, bh, offset) and key (low,
+ * high 32 bits of seed); word i%4 belongs to query i, and byte j%4 of that
+ * word (least significant first) to key j. */
+int oracle_dropout_byte(uint64_t seed, uint32_t offset, long bh, long i, long j) {
+  const uint64_t ctr[4] = {(uint64_t)(j >> 2), (uint64_t)(i >> 2), (uint64_t)bh, offset};
+  const uint64_t key[2] = {seed & 0xFFFFFFFFull, seed >> 32};
+  uint64_t out[4];
+  oracle_philox(32, 10, ctr, key, out);
+  return (int)((out[i & 3] >> (8 * (j & 3))) & 0xFF);
+}
+
+/* Z_ij: the element is kept iff its byte is at least the threshold. */
+int oracle_dropout_keep(uint64_t seed, uint32_t offset, int t, long bh, long i, long j) {
+  return oracle_dropout_byte(seed, offset, bh, i, j) >= t;
+}
+
+/* Keep indicators of one head, [rows][cols] from (i0, j0). */
+void oracle_dropout_mask(uint64_t seed, uint32_t offset, int t, long bh, long i0, long j0,
+                         long rows, long cols, uint8_t* z) {
+#pragma omp parallel for schedule(static)
+  for (long a = 0; a < rows; ++a)
+    for (long b = 0; b < cols; ++b)
+      z[a * cols + b] = (uint8_t)oracle_dropout_keep(seed, offset, t, bh, i0 + a, j0 + b);
+}
+
+/* Forward with dropout for q [B][H][N][d], k, v [B][Hkv][N][d]: O_i =
+ * sum_j P_ij Z_ij / keep V_j, L_i the log-sum-exp of the undropped scores. */
+void oracle_fwd_dropout(int B, int H, int Hkv, int N, int d, double scale, int causal,
+                        long window, double p, uint64_t seed, uint32_t offset,
+                        const double* q, const double* k, const double* v, double* o,
+                        double* lse, int nthreads) {
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+  const int t = oracle_dropout_threshold(p);
+  const double keep = (256.0 - t) / 256.0;
+  const long hs = (long)N * d, total = (long)B * H * N;
+#pragma omp parallel
+  {
+    double* srow = (double*)malloc(sizeof(double) * (size_t)N);
+    double* prow = (double*)malloc(sizeof(double) * (size_t)N);
+#pragma omp for schedule(dynamic, 16)
+    for (long r = 0; r < total; ++r) {
+      const long bh = r / N, i = r % N, kv = kv_head_of(bh, H, Hkv);
+      double* o_row = o + r * d;
+      query_row(N, d, scale, causal, window, q + bh * hs + i * d, i, k + kv * hs,
+                v + kv * hs, srow, prow, o_row, lse ? lse + r : NULL);
+      for (int c = 0; c < d; ++c) o_row[c] = 0.0;
+      for (long j = 0; j < N; ++j) {
+        if (prow[j] == 0.0 || !oracle_dropout_keep(seed, offset, t, bh, i, j)) continue;
+        const double w = prow[j] / keep;
+        const double* vj = v + kv * hs + j * (long)d;
+        for (int c = 0; c < d; ++c) o_row[c] += w * vj[c];
+      }
+    }
+    free(srow);
+    free(prow);
+  }
+}
+
+/* Backward with dropout, same shapes; dk, dv [B][Hkv][N][d] are summed over
+ * the query heads of each group.  Dvec [B][H][N] receives D_i. */
+void oracle_bwd_dropout(int B, int H, int Hkv, int N, int d, double scale, int causal,
+                        long window, double p, uint64_t seed, uint32_t offset,
+                        const double* q, const double* k, const double* v,
+                        const double* dout, double* dq, double* dk, double* dv,
+                        double* Dvec, int nthreads) {
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+  const int t = oracle_dropout_threshold(p);
+  const double keep = (256.0 - t) / 256.0;
+  const long hs = (long)N * d;
+  double* P = (double*)malloc(sizeof(double) * (size_t)N * (size_t)N);
+  double* Pd = (double*)malloc(sizeof(double) * (size_t)N * (size_t)N);
+  double* dS = (double*)malloc(sizeof(double) * (size_t)N * (size_t)N);
+  for (long x = 0; x < (long)B * Hkv * hs; ++x) dk[x] = dv[x] = 0.0;
+  for (long bh = 0; bh < (long)B * H; ++bh) {
+    const long kv = kv_head_of(bh, H, Hkv);
+    const double *qh = q + bh * hs, *kh = k + kv * hs, *vh = v + kv * hs;
+    const double* doh = dout + bh * hs;
+#pragma omp parallel
+    {
+      double* srow = (double*)malloc(sizeof(double) * (size_t)N);
+      double* dprow = (double*)malloc(sizeof(double) * (size_t)N);
+      double* o_row = (double*)malloc(sizeof(double) * (size_t)d);
+#pragma omp for schedule(dynamic, 8)
+      for (long i = 0; i < N; ++i) {
+        double* prow = P + i * (long)N;
+        double* pdrow = Pd + i * (long)N;
+        double* dsrow = dS + i * (long)N;
+        query_row(N, d, scale, causal, window, qh + i * (long)d, i, kh, vh, srow, prow,
+                  o_row, NULL);
+        /* Z_ij / keep, dP_ij = (dO_i . V_j) Z_ij / keep, and P~_ij = P_ij Z_ij / keep */
+        for (long j = 0; j < N; ++j) {
+          const double z = (prow[j] != 0.0 && oracle_dropout_keep(seed, offset, t, bh, i, j))
+                               ? 1.0 / keep
+                               : 0.0;
+          dprow[j] = z * dot(doh + i * (long)d, vh + j * (long)d, d);
+          pdrow[j] = prow[j] * z;
+        }
+        double Di = 0.0;
+        for (long j = 0; j < N; ++j) Di += prow[j] * dprow[j];
+        for (long j = 0; j < N; ++j) dsrow[j] = prow[j] * (dprow[j] - Di);
+        if (Dvec) Dvec[bh * N + i] = Di;
+        double* dqi = dq + bh * hs + i * (long)d;
+        for (int c = 0; c < d; ++c) dqi[c] = 0.0;
+        for (long j = 0; j < N; ++j) {
+          if (dsrow[j] == 0.0) continue;
+          const double* kj = kh + j * (long)d;
+          for (int c = 0; c < d; ++c) dqi[c] += dsrow[j] * kj[c];
+        }
+        for (int c = 0; c < d; ++c) dqi[c] *= scale;
+      }
+      free(srow);
+      free(dprow);
+      free(o_row);
+    }
+#pragma omp parallel for schedule(dynamic, 8)
+    for (long j = 0; j < N; ++j) {
+      double* dvj = dv + kv * hs + j * (long)d;
+      double* dkj = dk + kv * hs + j * (long)d;
+      for (long i = 0; i < N; ++i) {
+        const double pd = Pd[i * (long)N + j], ds = dS[i * (long)N + j];
+        const double* doi = doh + i * (long)d;
+        const double* qi = qh + i * (long)d;
+        if (pd != 0.0)
+          for (int c = 0; c < d; ++c) dvj[c] += pd * doi[c];
+        if (ds != 0.0)
+          for (int c = 0; c < d; ++c) dkj[c] += scale * ds * qi[c];
+      }
+    }
+  }
+  free(P);
+  free(Pd);
+  free(dS);
 }
