@@ -73,7 +73,7 @@ def parse_args():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra-paths", action="store_true",
-                    help="skip the grouped-query and decode measurements that follow the "
+                    help="skip the grouped-query, decode and dropout measurements that follow the "
                          "timed step (for profiler runs that should see the step only)")
     ap.add_argument("--hbm-copy-mib", type=int, default=0,
                     help="after timing, one fp32 -> bf16 copy of this many MiB of "
@@ -249,6 +249,57 @@ def measure_gqa(ea, torch, attn_synth, reps=10):
     return out
 
 
+def measure_dropout(ea, torch, attn_synth, reps=10, p=0.1):
+    """Dropout on P (p = 0.1) at B4 H16 N2048 d128, causal and non-causal: the
+    forward and the whole backward (dQ pass + dK/dV pass), each timed with
+    HIP events over `reps` calls, beside the same calls without dropout.
+    Measured after the timed step; it does not enter `value`.  Credited FLOPs
+    as without dropout."""
+    import numpy as np
+    B, H, N, d = 4, 16, 2048, 128
+    bits = attn_synth.bf16_attention_inputs(2, B, H, N, d, with_dout=True)
+
+    def dev(x):
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(
+            torch.bfloat16).cuda()
+    q, k, v, do = (dev(bits[n]) for n in ("q", "k", "v", "do"))
+    out = {"workload": f"B{B} H{H} N{N} d{d}, bf16, p={p}"}
+    ws = torch.empty(ea.attn_bwd_workspace_bytes(B, H, N, d), device="cuda",
+                     dtype=torch.uint8)
+    grads = tuple(torch.empty(q.shape, device="cuda", dtype=torch.float32) for _ in range(3))
+    for causal in (False, True):
+        o, lse = ea.attn_fwd_dropout(q, k, v, p, 1, 0, causal=causal)
+        o0, lse0 = ea.attn_fwd(q, k, v, causal=causal)
+        runs = {
+            "fwd": lambda: ea.attn_fwd_dropout(q, k, v, p, 1, 0, causal=causal, out=o,
+                                               lse=lse),
+            "bwd": lambda: ea.attn_bwd_dropout(q, k, v, o, do, lse, p, 1, 0, causal=causal,
+                                               workspace=ws, grads=grads),
+            "fwd_plain": lambda: ea.attn_fwd(q, k, v, causal=causal, out=o0, lse=lse0),
+            "bwd_plain": lambda: ea.attn_bwd(q, k, v, o0, do, lse0, causal=causal,
+                                             workspace=ws, grads=grads),
+        }
+        f = credited_fwd_flops(B * H, N, d, causal, 0)
+        credit = {"fwd": f, "bwd": 2.5 * f, "fwd_plain": f, "bwd_plain": 2.5 * f}
+        row = {}
+        for name, fn in runs.items():
+            fn()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / reps
+            row[name] = {"ms": round(ms, 4),
+                         "tflops": round(credit[name] / (ms * 1e-3) / 1e12, 1)}
+        row["fwd_bwd_tflops"] = round(3.5 * f / ((row["fwd"]["ms"] + row["bwd"]["ms"])
+                                                 * 1e-3) / 1e12, 1)
+        out["causal" if causal else "non_causal"] = row
+    return out
+
+
 def measure_decode(ea, torch, attn_synth, reps=20):
     """Decode: one query per head at the end of a 32768-key sequence, B4 H32
     with 8 key/value heads, d128 (attn_fwd_decode: key-split pass + merge).
@@ -411,6 +462,7 @@ def main():
     if not args.no_extra_paths:
         out["gqa"] = measure_gqa(ea, torch, attn_synth)
         out["decode"] = measure_decode(ea, torch, attn_synth)
+        out["dropout"] = measure_dropout(ea, torch, attn_synth)
     if args.hbm_copy_mib > 0:
         # fp32 -> bf16, so that the copy runs as an elementwise kernel (a
         # same-dtype copy may go to a DMA engine that the counters miss).

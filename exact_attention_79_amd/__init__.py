@@ -24,7 +24,8 @@ ATTN_OUT_BF16, ATTN_OUT_F32 = 0, 1
 # Entry points declared in include/attn.h.
 EXPORTS = ("attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_bwd_preprocess",
            "attn_bwd_dkdv", "attn_bwd_dq", "attn_fwd_fp8", "attn_decode_workspace_bytes",
-           "attn_fwd_decode", "attn_fwd_fp8_blocks", "attn_status_str")
+           "attn_fwd_decode", "attn_fwd_fp8_blocks", "attn_fwd_dropout", "attn_bwd_dropout",
+           "attn_status_str")
 
 
 class AttnDesc(ctypes.Structure):
@@ -39,6 +40,11 @@ class AttnDecodeDesc(ctypes.Structure):
                 ("N_q", ctypes.c_int32), ("N_k", ctypes.c_int32), ("d", ctypes.c_int32),
                 ("scale", ctypes.c_float), ("causal", ctypes.c_int32),
                 ("window", ctypes.c_int32)]
+
+
+class AttnDropout(ctypes.Structure):
+    _fields_ = [("p", ctypes.c_float), ("offset", ctypes.c_uint32),
+                ("seed", ctypes.c_uint64)]
 
 
 class AttnError(RuntimeError):
@@ -76,6 +82,11 @@ def _load():
     L.attn_decode_workspace_bytes.restype = sz
     L.attn_fwd_decode.argtypes = [ddp, vp, vp, vp, vp, i32, vp, vp, sz, vp]
     L.attn_fwd_decode.restype = ctypes.c_int
+    drp = ctypes.POINTER(AttnDropout)
+    L.attn_fwd_dropout.argtypes = [dp, drp, vp, vp, vp, vp, i32, vp, vp]
+    L.attn_fwd_dropout.restype = ctypes.c_int
+    L.attn_bwd_dropout.argtypes = [dp, drp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.attn_bwd_dropout.restype = ctypes.c_int
     L.attn_status_str.argtypes = [ctypes.c_int]
     L.attn_status_str.restype = ctypes.c_char_p
     return L
@@ -123,10 +134,8 @@ def _check_qkv(q, k, v, dtypes):
                          "multiple of H_kv")
 
 
-def attn_fwd(q, k, v, scale: float | None = None, causal: bool = False,
-             window: int = 0, out_dtype=torch.bfloat16, return_lse: bool = True,
-             out=None, lse=None):
-    """O (and the fp32 LSE) for bf16 q, k, v of shape [B, H, N, d]."""
+def _fwd_prep(q, k, v, scale, causal, window, out_dtype, return_lse, out, lse):
+    """Checks, outputs and descriptor of the bf16 forward."""
     _check_qkv(q, k, v, (torch.bfloat16,))
     B, H, N, d = q.shape
     scale = 1.0 / math.sqrt(d) if scale is None else scale
@@ -141,8 +150,37 @@ def attn_fwd(q, k, v, scale: float | None = None, causal: bool = False,
         raise ValueError("lse must be a contiguous fp32 device tensor [B, H, N]")
     desc = make_desc(B, H, N, d, scale, causal, window, k.shape[1])
     od = ATTN_OUT_F32 if out_dtype == torch.float32 else ATTN_OUT_BF16
+    return desc, o, lse, od
+
+
+def attn_fwd(q, k, v, scale: float | None = None, causal: bool = False,
+             window: int = 0, out_dtype=torch.bfloat16, return_lse: bool = True,
+             out=None, lse=None):
+    """O (and the fp32 LSE) for bf16 q, k, v of shape [B, H, N, d]."""
+    desc, o, lse, od = _fwd_prep(q, k, v, scale, causal, window, out_dtype, return_lse,
+                                 out, lse)
     _check(lib.attn_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(o), od,
                         _ptr(lse), _stream()), "attn_fwd")
+    return (o, lse) if return_lse else o
+
+
+def make_dropout(p: float, seed: int, offset: int = 0) -> AttnDropout:
+    """Dropout description: probability p, Philox key `seed`, counter word `offset`."""
+    if not (0 <= seed < 2**64 and 0 <= offset < 2**32):
+        raise ValueError("seed must fit in 64 bits and offset in 32 bits")
+    return AttnDropout(float(p), int(offset), int(seed))
+
+
+def attn_fwd_dropout(q, k, v, p: float, seed: int, offset: int = 0,
+                     scale: float | None = None, causal: bool = False, window: int = 0,
+                     out_dtype=torch.bfloat16, return_lse: bool = True, out=None, lse=None):
+    """attn_fwd with dropout on P (keep bytes from Philox-4x32-10, see attn.h)."""
+    desc, o, lse, od = _fwd_prep(q, k, v, scale, causal, window, out_dtype, return_lse,
+                                 out, lse)
+    drop = make_dropout(p, seed, offset)
+    _check(lib.attn_fwd_dropout(ctypes.byref(desc), ctypes.byref(drop), _ptr(q), _ptr(k),
+                                _ptr(v), _ptr(o), od, _ptr(lse), _stream()),
+           "attn_fwd_dropout")
     return (o, lse) if return_lse else o
 
 
@@ -151,9 +189,8 @@ def attn_bwd_workspace_bytes(B: int, H: int, N: int, d: int) -> int:
     return int(lib.attn_bwd_workspace_bytes(ctypes.byref(desc)))
 
 
-def attn_bwd(q, k, v, o, dout, lse, scale: float | None = None,
-             causal: bool = False, window: int = 0, workspace=None, grads=None):
-    """dQ, dK, dV (fp32) for bf16 q, k, v, o, dout and the forward's fp32 lse."""
+def _bwd_prep(q, k, v, o, dout, lse, scale, causal, window, workspace, grads):
+    """Checks, outputs, workspace and descriptor of the bf16 backward."""
     _check_qkv(q, k, v, (torch.bfloat16,))
     _check_like(q, torch.bfloat16, o=o, dout=dout)
     desc = _bwd_desc(q, k, scale, causal, window)
@@ -166,10 +203,31 @@ def attn_bwd(q, k, v, o, dout, lse, scale: float | None = None,
     _check_like(q, torch.float32, dq=dq)
     _check_like(k, torch.float32, dk=dk, dv=dv)
     _check_lse_ws(q, lse, workspace, desc)
+    return desc, workspace, (dq, dk, dv)
+
+
+def attn_bwd(q, k, v, o, dout, lse, scale: float | None = None,
+             causal: bool = False, window: int = 0, workspace=None, grads=None):
+    """dQ, dK, dV (fp32) for bf16 q, k, v, o, dout and the forward's fp32 lse."""
+    desc, workspace, (dq, dk, dv) = _bwd_prep(q, k, v, o, dout, lse, scale, causal, window,
+                                              workspace, grads)
     _check(lib.attn_bwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
                         _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
-                        _ptr(workspace), workspace.numel() * workspace.element_size(),
-                        _stream()), "attn_bwd")
+                        _ptr(workspace), _ws_bytes(workspace), _stream()), "attn_bwd")
+    return dq, dk, dv
+
+
+def attn_bwd_dropout(q, k, v, o, dout, lse, p: float, seed: int, offset: int = 0,
+                     scale: float | None = None, causal: bool = False, window: int = 0,
+                     workspace=None, grads=None):
+    """attn_bwd of attn_fwd_dropout (same p, seed and offset as that forward)."""
+    desc, workspace, (dq, dk, dv) = _bwd_prep(q, k, v, o, dout, lse, scale, causal, window,
+                                              workspace, grads)
+    drop = make_dropout(p, seed, offset)
+    _check(lib.attn_bwd_dropout(ctypes.byref(desc), ctypes.byref(drop), _ptr(q), _ptr(k),
+                                _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk),
+                                _ptr(dv), _ptr(workspace), _ws_bytes(workspace), _stream()),
+           "attn_bwd_dropout")
     return dq, dk, dv
 
 

@@ -57,6 +57,7 @@ attn::FwdArgs fwd_args(const attn_desc* d, const void* q, const void* k,
   a.out_f32 = (o_dtype == ATTN_OUT_F32);
   a.q_descale = a.k_descale = a.v_descale = 1.f;
   a.q_scales = a.k_scales = a.v_scales = nullptr;
+  a.drop = attn::DropoutArgs{0u, 0u, 0ull};
   return a;
 }
 
@@ -90,7 +91,19 @@ attn::BwdArgs bwd_args(const attn_desc* d, const void* q, const void* k,
   a.scale = d->scale;
   a.causal = d->causal;
   a.window = d->window;
+  a.drop = attn::DropoutArgs{0u, 0u, 0ull};
   return a;
+}
+
+// The keep threshold t = round(256 p) of a dropout description.
+attn_status dropout_args(const attn_dropout* drop, attn::DropoutArgs* out) {
+  if (!drop || !isfinite(drop->p) || drop->p < 0.f) return ATTN_EINVAL;
+  const double t = floor((double)drop->p * 256.0 + 0.5);
+  if (t > 255.0) return ATTN_EINVAL;
+  out->thresh = (uint32_t)t;
+  out->offset = drop->offset;
+  out->seed = drop->seed;
+  return ATTN_OK;
 }
 
 }  // namespace
@@ -168,6 +181,36 @@ attn_status attn_bwd_dkdv(const attn_desc* desc, const void* q, const void* k,
       bwd_args(desc, q, k, v, nullptr, dout, nullptr, nullptr, dk, dv,
                (void*)workspace),
       (hipStream_t)stream));
+}
+
+attn_status attn_fwd_dropout(const attn_desc* desc, const attn_dropout* drop,
+                             const void* q, const void* k, const void* v, void* o,
+                             int32_t o_dtype, float* lse, void* stream) {
+  attn_status st = check_desc(desc);
+  if (st != ATTN_OK) return st;
+  if (o_dtype != ATTN_OUT_BF16 && o_dtype != ATTN_OUT_F32) return ATTN_EINVAL;
+  st = check_ptrs({q, k, v, o}, {lse});
+  if (st != ATTN_OK) return st;
+  attn::FwdArgs a = fwd_args(desc, q, k, v, o, o_dtype, lse);
+  st = dropout_args(drop, &a.drop);
+  if (st != ATTN_OK) return st;
+  return from_hip(attn::launch_fwd_bf16(a, (hipStream_t)stream));
+}
+
+attn_status attn_bwd_dropout(const attn_desc* desc, const attn_dropout* drop,
+                             const void* q, const void* k, const void* v, const void* o,
+                             const void* dout, const float* lse, float* dq, float* dk,
+                             float* dv, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  attn_status st = check_desc(desc);
+  if (st != ATTN_OK) return st;
+  st = check_ptrs({q, k, v, o, dout, lse, dq, dk, dv, workspace}, {});
+  if (st != ATTN_OK) return st;
+  if (workspace_bytes < attn_bwd_workspace_bytes(desc)) return ATTN_EINVAL;
+  attn::BwdArgs a = bwd_args(desc, q, k, v, o, dout, lse, dq, dk, dv, workspace);
+  st = dropout_args(drop, &a.drop);
+  if (st != ATTN_OK) return st;
+  return from_hip(attn::launch_bwd(a, (hipStream_t)stream));
 }
 
 attn_status attn_fwd_fp8(const attn_desc* desc, const uint8_t* q8,

@@ -91,6 +91,7 @@ struct BwdKParams {
   int n_tiles;
   float scale;
   int causal, window;
+  Dropout drop;
 };
 
 // ---------------------------------------------------------------- dK, dV
@@ -103,7 +104,9 @@ struct BwdKParams {
 // registers (the FLASH-ATTN page's MQA/GQA paragraph).  Iteration i computes
 // S and dP for tile i+1 on the matrix cores while the VALU forms P and dS
 // for tile i, then accumulates dV += P^T dO and dK += dS^T Q for tile i.
-template <int D, int NW, int BQ>
+// DROP: dropout on P with the forward's keep bytes: dV takes the kept P (its
+// 1 / keep scale applied once at the end) and dS = P (Z dP / keep - D).
+template <int D, int NW, int BQ, bool DROP>
 __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(BwdKParams p) {
   constexpr int BKV = 32 * NW;
   constexpr int KS = D / 16;
@@ -166,7 +169,7 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(BwdKParams p) {
   // load cursor (lj, lt) runs two tiles ahead of the compute cursor ct.
   // Past the last head it keeps reading the last head's rows (in bounds;
   // those tiles are never used).
-  int lj = 0, lt = t_lo, ct = t_lo;
+  int lj = 0, lt = t_lo, ct = t_lo, cj = 0;
   auto load_tile = [&](__bf16* Qf, __bf16* Of, float* Lf, float* Df) {
     const int bhq = bh0 + min(lj, G - 1);
     const size_t qhead = (size_t)bhq * N * D;
@@ -214,7 +217,17 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(BwdKParams p) {
                        __bf16* Of, float* Lf, float* Df) {
     load_tile(Qf, Of, Lf, Df);
     const int i0 = ct * BQ;
-    if (++ct == t_hi) ct = t_lo;
+    const int bhq = bh0 + cj;  // query head of this tile
+    if (++ct == t_hi) {
+      ct = t_lo;
+      ++cj;
+    }
+    u32x4 keepw[BQ / 32];
+    if constexpr (DROP) {
+#pragma unroll
+      for (int mt = 0; mt < BQ / 32; ++mt)
+        keepw[mt] = dropout_bytes<true>(p.drop, bhq, i0 + 32 * mt, kw0, lane);
+    }
     bool need_mask = false;
     if (p.causal) need_mask |= i0 < kw0 + 31;
     if (W > 0) {
@@ -285,8 +298,14 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(BwdKParams p) {
       for (int u = 0; u < EPB; ++u) {
         const int e = EPB * i + u, mt2 = e >> 4, r = e & 15, g = 4 * mt2 + (r >> 2);
         const float pv = fast_exp2(fmaf(scur[mt2][r], s2, -lb[g][r & 3]));
-        const float ds = pv * (dpcur[mt2][r] - dl[g][r & 3]);
-        pop[e >> 3][e & 7] = (__bf16)pv;
+        float dpv = dpcur[mt2][r], pk = pv;
+        if constexpr (DROP) {
+          const bool kp = dropout_keep(keepw[mt2], r, p.drop.thresh);
+          dpv = kp ? dpv * p.drop.inv_keep : 0.f;
+          pk = kp ? pv : 0.f;
+        }
+        const float ds = pv * (dpv - dl[g][r & 3]);
+        pop[e >> 3][e & 7] = (__bf16)pk;
         dsop[e >> 3][e & 7] = (__bf16)ds;
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -320,6 +339,7 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(BwdKParams p) {
 
   if (my_k < N) {
     const size_t row = head + (size_t)my_k * D;
+    const float vs = DROP ? p.drop.inv_keep : 1.f;
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
@@ -328,8 +348,13 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(BwdKParams p) {
         *(f32x4*)(p.dk + row + d0) =
             (f32x4){dkacc[dt][4 * g] * p.scale, dkacc[dt][4 * g + 1] * p.scale,
                     dkacc[dt][4 * g + 2] * p.scale, dkacc[dt][4 * g + 3] * p.scale};
-        *(f32x4*)(p.dv + row + d0) = (f32x4){dvacc[dt][4 * g], dvacc[dt][4 * g + 1],
-                                             dvacc[dt][4 * g + 2], dvacc[dt][4 * g + 3]};
+        if constexpr (DROP)
+          *(f32x4*)(p.dv + row + d0) =
+              (f32x4){dvacc[dt][4 * g] * vs, dvacc[dt][4 * g + 1] * vs,
+                      dvacc[dt][4 * g + 2] * vs, dvacc[dt][4 * g + 3] * vs};
+        else
+          *(f32x4*)(p.dv + row + d0) = (f32x4){dvacc[dt][4 * g], dvacc[dt][4 * g + 1],
+                                               dvacc[dt][4 * g + 2], dvacc[dt][4 * g + 3]};
       }
   }
 }
@@ -339,7 +364,10 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(BwdKParams p) {
 // side); K/V tiles of BC keys stream through three LDS slots fetched one
 // tile ahead.  Iteration t computes S^T and dP^T of tile t+1 on the matrix
 // cores while the VALU forms P and dS^T of tile t, then dQ^T += K_t^T dS_t^T.
-template <int D, int NW, int BC>
+// DROP: dS = P (Z dP / keep - D) with the forward's keep bytes.  (Two waves
+// per SIMD even though the keep bytes then spill a few registers: measured
+// faster than one wave per SIMD without spills.)
+template <int D, int NW, int BC, bool DROP>
 __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdKParams p) {
   constexpr int BR = 32 * NW;
   constexpr int KS = D / 16;
@@ -456,6 +484,12 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdKParams p) {
                                                                   : scur[mt][r];
         }
     }
+    u32x4 keepw[BC / 32];
+    if constexpr (DROP) {
+#pragma unroll
+      for (int mt = 0; mt < BC / 32; ++mt)
+        keepw[mt] = dropout_bytes<false>(p.drop, bh, wq0, kv0 + 32 * mt, lane);
+    }
     constexpr int NS = 2 * (BC / 32) * KS;
     constexpr int NP = (BC / 16) * (D / 32);
     constexpr int EPB = (BC / 2) / NS;
@@ -486,7 +520,10 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdKParams p) {
       for (int u = 0; u < EPB; ++u) {
         const int e = EPB * i + u, mt2 = e >> 4, r = e & 15;
         const float pv = fast_exp2(fmaf(scur[mt2][r], s2, -Lb));
-        dsop[e >> 3][e & 7] = (__bf16)(pv * (dpcur[mt2][r] - Dl));
+        float dpv = dpcur[mt2][r];
+        if constexpr (DROP)
+          dpv = dropout_keep(keepw[mt2], r, p.drop.thresh) ? dpv * p.drop.inv_keep : 0.f;
+        dsop[e >> 3][e & 7] = (__bf16)(pv * (dpv - Dl));
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -545,11 +582,15 @@ static BwdKParams bwd_params(const BwdArgs& a, int tile_rows) {
   p.causal = a.causal;
   p.window = a.window;
   p.n_tiles = (a.N + tile_rows - 1) / tile_rows;
+  p.drop = make_dropout(a.drop);
   return p;
 }
 
 constexpr int kBwdWaves = 4;
 constexpr int kBwdQTile = 64;  // query rows per step of the dK/dV kernel
+// With dropout, 32-row steps: the keep bytes need registers that the 64-row
+// step does not have to spare.
+constexpr int kDropQTile = 32;
 
 hipError_t launch_bwd_preprocess(const BwdArgs& a, hipStream_t stream) {
   const int rows = a.BH * a.N;
@@ -572,11 +613,18 @@ hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream) {
   // One workgroup per key block of every key/value head.
   const int BHkv = a.BH / a.H * a.Hkv;
   const dim3 grid((unsigned)(BHkv * p.n_tiles)), block(64 * kBwdWaves);
-  if (a.d == 128)
-    hipLaunchKernelGGL((bwd_dkdv_kernel<128, kBwdWaves, kBwdQTile>), grid, block, 0,
+  const bool drop = a.drop.thresh > 0;
+  if (a.d == 128 && drop)
+    hipLaunchKernelGGL((bwd_dkdv_kernel<128, kBwdWaves, kDropQTile, true>), grid, block, 0,
+                       stream, p);
+  else if (a.d == 128)
+    hipLaunchKernelGGL((bwd_dkdv_kernel<128, kBwdWaves, kBwdQTile, false>), grid, block,
+                       0, stream, p);
+  else if (drop)
+    hipLaunchKernelGGL((bwd_dkdv_kernel<64, kBwdWaves, kDropQTile, true>), grid, block, 0,
                        stream, p);
   else
-    hipLaunchKernelGGL((bwd_dkdv_kernel<64, kBwdWaves, kBwdQTile>), grid, block, 0,
+    hipLaunchKernelGGL((bwd_dkdv_kernel<64, kBwdWaves, kBwdQTile, false>), grid, block, 0,
                        stream, p);
   return hipGetLastError();
 }
@@ -584,10 +632,17 @@ hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream) {
 hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream) {
   const BwdKParams p = bwd_params(a, 32 * kBwdWaves);
   const dim3 grid((unsigned)(a.BH * p.n_tiles)), block(64 * kBwdWaves);
-  if (a.d == 128)
-    hipLaunchKernelGGL((bwd_dq_kernel<128, kBwdWaves, 32>), grid, block, 0, stream, p);
+  const bool drop = a.drop.thresh > 0;
+  if (a.d == 128 && drop)
+    hipLaunchKernelGGL((bwd_dq_kernel<128, kBwdWaves, 32, true>), grid, block, 0, stream, p);
+  else if (a.d == 128)
+    hipLaunchKernelGGL((bwd_dq_kernel<128, kBwdWaves, 32, false>), grid, block, 0, stream,
+                       p);
+  else if (drop)
+    hipLaunchKernelGGL((bwd_dq_kernel<64, kBwdWaves, 64, true>), grid, block, 0, stream, p);
   else
-    hipLaunchKernelGGL((bwd_dq_kernel<64, kBwdWaves, 64>), grid, block, 0, stream, p);
+    hipLaunchKernelGGL((bwd_dq_kernel<64, kBwdWaves, 64, false>), grid, block, 0, stream,
+                       p);
   return hipGetLastError();
 }
 

@@ -17,6 +17,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "attn_kernels.hpp"
+
 namespace attn {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -222,6 +224,111 @@ __device__ __forceinline__ void vec_load_lds(__amdgpu_buffer_rsrc_t rs, int row0
 // of this wave are outstanding (LDS and export counters not waited on).
 __host__ __device__ constexpr int waitcnt_vm(int n) {
   return (n & 0xF) | (0x7 << 4) | (0xF << 8) | ((n >> 4) << 14);
+}
+
+// ---- dropout on P: keep bytes from a counter-based generator ----
+//
+// The pages name dropout on the probabilities without fixing a random-number
+// contract; the one implemented here: element (query i, key j) of query head
+// bh is kept iff its byte is >= the threshold t = round(256 p), kept values
+// are scaled by 256 / (256 - t), and the byte comes from Philox-4x32-10
+// (Salmon et al., SC 2011) with counter (j/4, i/4, bh, offset) and key
+// (seed low, seed high): word i%4 of the output belongs to query i, byte j%4
+// of that word (least significant first) to key j.  One generator call thus
+// covers a 4 x 4 sub-block of the score matrix, which either MFMA C layout
+// (query per lane or key per lane) reaches with one call per lane per 32 x 32
+// block plus a transpose within each group of four lanes.
+struct Dropout {
+  uint32_t thresh;   // t; 0 = no dropout
+  uint32_t offset;   // counter word 3
+  uint32_t key0, key1;
+  float inv_keep;    // 256 / (256 - t)
+};
+
+inline Dropout make_dropout(const DropoutArgs& a) {
+  Dropout d;
+  d.thresh = a.thresh;
+  d.offset = a.offset;
+  d.key0 = (uint32_t)a.seed;
+  d.key1 = (uint32_t)(a.seed >> 32);
+  d.inv_keep = a.thresh ? 256.f / (float)(256u - a.thresh) : 1.f;
+  return d;
+}
+
+__device__ __forceinline__ u32x4 philox4x32_10(u32x4 c, uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c[0];
+    const uint64_t p1 = (uint64_t)0xCD9E8D57u * c[2];
+    c = (u32x4){(uint32_t)(p1 >> 32) ^ c[1] ^ k0, (uint32_t)p1,
+                (uint32_t)(p0 >> 32) ^ c[3] ^ k1, (uint32_t)p0};
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  return c;
+}
+
+// Lane i of each group of four reads lane i ^ 1 (quad_perm 1,0,3,2) or
+// lane i ^ 2 (quad_perm 2,3,0,1).
+__device__ __forceinline__ uint32_t quad_xor1(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xF, 0xF, false);
+}
+__device__ __forceinline__ uint32_t quad_xor2(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x4E, 0xF, 0xF, false);
+}
+
+// Word w of lane s (s = lane % 4) becomes word s of lane w, within each group
+// of four lanes: two exchange steps, one per bit of (s, w), in each of which
+// the lanes whose bit differs from the word's swap words with the partner.
+__device__ __forceinline__ u32x4 quad_transpose(u32x4 a, int s) {
+  const bool b0 = s & 1, b1 = s & 2;
+  const uint32_t u1 = quad_xor1(b0 ? a[0] : a[1]);
+  const uint32_t u3 = quad_xor1(b0 ? a[2] : a[3]);
+  a[0] = b0 ? u1 : a[0];
+  a[1] = b0 ? a[1] : u1;
+  a[2] = b0 ? u3 : a[2];
+  a[3] = b0 ? a[3] : u3;
+  const uint32_t v0 = quad_xor2(b1 ? a[0] : a[2]);
+  const uint32_t v1 = quad_xor2(b1 ? a[1] : a[3]);
+  a[0] = b1 ? v0 : a[0];
+  a[1] = b1 ? v1 : a[1];
+  a[2] = b1 ? a[2] : v0;
+  a[3] = b1 ? a[3] : v1;
+  return a;
+}
+
+// Byte b of word r becomes byte r of word b.
+__device__ __forceinline__ u32x4 byte_transpose(u32x4 w) {
+  u32x4 o;
+#pragma unroll
+  for (int b = 0; b < 4; ++b)
+    o[b] = ((w[0] >> (8 * b)) & 0xFFu) | (((w[1] >> (8 * b)) & 0xFFu) << 8) |
+           (((w[2] >> (8 * b)) & 0xFFu) << 16) | (((w[3] >> (8 * b)) & 0xFFu) << 24);
+  return o;
+}
+
+// Keep bytes of the 32 x 32 score block of query head bh whose queries start
+// at qb and keys at kb (both multiples of 32), arranged like this lane's C
+// registers: register r's byte is byte r % 4 of word r / 4.  KEY_PER_LANE
+// false: the block is S^T (keys on M, one query per lane); true: S (queries
+// on M, one key per lane).
+template <bool KEY_PER_LANE>
+__device__ __forceinline__ u32x4 dropout_bytes(const Dropout& dr, int bh, int qb, int kb,
+                                               int lane) {
+  const int n = lane & 31, h = lane >> 5, s = n & 3;
+  // This lane draws the sub-block of its quad's 4 rows (n & ~3 on the lane
+  // side) and of the rows 8s + 4h .. +3 on the M side.
+  const uint32_t I = KEY_PER_LANE ? (uint32_t)(qb / 4 + 2 * s + h) : (uint32_t)(qb / 4 + (n >> 2));
+  const uint32_t J = KEY_PER_LANE ? (uint32_t)(kb / 4 + (n >> 2)) : (uint32_t)(kb / 4 + 2 * s + h);
+  u32x4 w = philox4x32_10((u32x4){J, I, (uint32_t)bh, dr.offset}, dr.key0, dr.key1);
+  // Word r is query row r of the sub-block and byte b its key b; a key-per-
+  // lane layout wants one word per key instead.
+  if (KEY_PER_LANE) w = byte_transpose(w);
+  return quad_transpose(w, s);
+}
+
+__device__ __forceinline__ bool dropout_keep(const u32x4& m, int r, uint32_t thresh) {
+  return ((m[r >> 2] >> (8 * (r & 3))) & 0xFFu) >= thresh;
 }
 
 }  // namespace attn

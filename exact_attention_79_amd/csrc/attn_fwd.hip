@@ -50,9 +50,12 @@ struct FwdKParams {
   int n_qtiles;
   float scale;
   int causal, window, out_f32;
+  Dropout drop;
 };
 
-template <int D, int NW, int BC>
+// DROP: dropout on P (the keep bytes of attn_device.hpp); l and L stay those
+// of the undropped probabilities, and the 1 / keep scale is applied with 1 / l.
+template <int D, int NW, int BC, bool DROP>
 __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdKParams p) {
   constexpr int BR = 32 * NW;  // queries per workgroup
   static_assert(BC == 32 || BC == 64, "the pipeline is written for 32- or 64-key tiles");
@@ -234,6 +237,12 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdKParams p) {
     for (int mt = 0; mt < BC / 32; ++mt) snext[mt] = (f32x16){};
     bf16x8 ka[NS], va[NP], pop[BC / 16];
     float lsum = 0.f;
+    u32x4 keepw[BC / 32];
+    if constexpr (DROP) {
+#pragma unroll
+      for (int mt = 0; mt < BC / 32; ++mt)
+        keepw[mt] = dropout_bytes<false>(p.drop, bh, wq0, t * BC + 32 * mt, lane);
+    }
 #pragma unroll
     for (int i = 0; i < AHEAD; ++i) ka[i] = kread(i);
     __builtin_amdgcn_sched_barrier(0);
@@ -245,8 +254,9 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdKParams p) {
 #pragma unroll
       for (int u = 0; u < EPB; ++u) {
         const int e = EPB * i + u, mt = e >> 4, r = e & 15;
-        const float x = fast_exp2(fmaf(scur[mt][r], s2, -mb));
+        float x = fast_exp2(fmaf(scur[mt][r], s2, -mb));
         lsum += x;
+        if constexpr (DROP) x = dropout_keep(keepw[mt], r, p.drop.thresh) ? x : 0.f;
         pop[e >> 3][e & 7] = (__bf16)x;
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -300,7 +310,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdKParams p) {
   // ---- epilogue: O = O~ / l, L = ln 2 * (m s2 + log2 l) ----
   const float l_tot = halves_sum(l_run);
   if (my_q < N) {
-    const float inv = 1.f / l_tot;
+    const float inv = (DROP ? p.drop.inv_keep : 1.f) / l_tot;
     const size_t row = head + (size_t)my_q * D;
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
@@ -322,7 +332,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdKParams p) {
   }
 }
 
-template <int D, int NW, int BC>
+template <int D, int NW, int BC, bool DROP>
 static hipError_t launch_fwd_cfg(const FwdArgs& a, hipStream_t stream) {
   FwdKParams p;
   p.q = (const __bf16*)a.q;
@@ -338,15 +348,20 @@ static hipError_t launch_fwd_cfg(const FwdArgs& a, hipStream_t stream) {
   p.causal = a.causal;
   p.window = a.window;
   p.out_f32 = a.out_f32;
+  p.drop = make_dropout(a.drop);
   const unsigned grid = (unsigned)(a.BH * p.n_qtiles);
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, BC>), dim3(grid), dim3(NW * 64), 0,
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, BC, DROP>), dim3(grid), dim3(NW * 64), 0,
                      stream, p);
   return hipGetLastError();
 }
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream) {
-  if (a.d == 128) return launch_fwd_cfg<128, 4, 32>(a, stream);
-  return launch_fwd_cfg<64, 4, 64>(a, stream);
+  if (a.drop.thresh > 0) {
+    if (a.d == 128) return launch_fwd_cfg<128, 4, 32, true>(a, stream);
+    return launch_fwd_cfg<64, 4, 64, true>(a, stream);
+  }
+  if (a.d == 128) return launch_fwd_cfg<128, 4, 32, false>(a, stream);
+  return launch_fwd_cfg<64, 4, 64, false>(a, stream);
 }
 
 }  // namespace attn

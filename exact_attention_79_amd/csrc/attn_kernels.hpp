@@ -7,6 +7,13 @@
 
 namespace attn {
 
+// Dropout on P for the bf16 forward and backward (thresh = 0: none).
+struct DropoutArgs {
+  uint32_t thresh;     // bytes below it are dropped: round(256 p)
+  uint32_t offset;     // fourth counter word
+  uint64_t seed;       // Philox key
+};
+
 // BH = B * H query heads; K and V (and dK, dV) have B * Hkv heads, and query
 // head h of batch b reads key/value head b * Hkv + h / (H / Hkv).
 struct FwdArgs {
@@ -23,6 +30,7 @@ struct FwdArgs {
   const float* q_scales;  // ... one per block (nullptr: per tensor): [BH][N/128]
   const float* k_scales;  // [B*Hkv][N/64]
   const float* v_scales;  // [B*Hkv][N/64]
+  DropoutArgs drop;    // bf16 kernel only
 };
 
 struct BwdArgs {
@@ -40,6 +48,7 @@ struct BwdArgs {
   int BH, H, Hkv, N, d;
   float scale;
   int causal, window;
+  DropoutArgs drop;
 };
 
 // A block of Nq queries (the last Nq positions) against Nk keys, split over

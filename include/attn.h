@@ -203,6 +203,44 @@ attn_status attn_fwd_decode(const attn_decode_desc* desc, const void* q, const v
                             const void* v, void* o, int32_t o_dtype, float* lse,
                             void* workspace, size_t workspace_bytes, void* stream);
 
+/* Dropout on the probabilities (the FLASH-ATTN page lists dropout among the
+ * variants the fused kernel supports, and its FlashAttention-2 "Background"
+ * paragraph names dropout on P as one of the elementwise steps that the fused
+ * kernel keeps on chip).  The pages fix no random-number contract; this is
+ * the library's:
+ *   t       = round(256 p), halves up (t = floor(256 p + 1/2), in double);
+ *   byte    = byte (j mod 4) (least significant first) of word (i mod 4) of
+ *             Philox-4x32-10 (Salmon, Moraes, Dror, Shaw, SC 2011) with counter
+ *             (floor(j/4), floor(i/4), bh, offset) and key (seed mod 2^32,
+ *             floor(seed / 2^32)), for query head bh = b * H + h, query i and
+ *             key j of that head;
+ *   Z_ij    = 1 if byte >= t, else 0 (keep probability q = (256 - t) / 256);
+ *   O       = (P o Z / q) V, with P the softmax of the masked scores, and lse
+ *             the log-sum-exp of those scores (dropout does not change it).
+ * The backward uses the same Z: dV = (P o Z / q)^T dO, dP = (dO V^T) o Z / q,
+ * dS = P o (dP - D) with D_i = sum_k dO_ik O_ik of the dropped O, dQ = s dS K,
+ * dK = s dS^T Q.  p = 0 runs the ordinary kernels. */
+typedef struct {
+  float p;            /* dropout probability: 0 <= p and round(256 p) <= 255 */
+  uint32_t offset;    /* fourth counter word (e.g. a step number)            */
+  uint64_t seed;      /* Philox key                                          */
+} attn_dropout;
+
+/* attn_fwd with dropout on P (bf16 inputs; o, lse as attn_fwd).  ATTN_EINVAL
+ * also for a NULL `drop`, p not finite, p < 0 or round(256 p) > 255. */
+attn_status attn_fwd_dropout(const attn_desc* desc, const attn_dropout* drop,
+                             const void* q, const void* k, const void* v, void* o,
+                             int32_t o_dtype, float* lse, void* stream);
+
+/* attn_bwd of attn_fwd_dropout: the same desc and drop (p, offset, seed) as
+ * the forward that produced o and lse; other arguments and errors as attn_bwd
+ * and attn_fwd_dropout.  Enqueues the dQ pass, then the dK/dV pass. */
+attn_status attn_bwd_dropout(const attn_desc* desc, const attn_dropout* drop,
+                             const void* q, const void* k, const void* v, const void* o,
+                             const void* dout, const float* lse, float* dq, float* dk,
+                             float* dv, void* workspace, size_t workspace_bytes,
+                             void* stream);
+
 /* Static, human-readable text for a status code. */
 const char* attn_status_str(attn_status status);
 

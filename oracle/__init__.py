@@ -74,9 +74,9 @@ def lib():
         L.oracle_dropout_byte.argtypes = [u64, u32, lg, lg, lg]
         L.oracle_dropout_byte.restype = i
         L.oracle_dropout_mask.argtypes = [u64, u32, i, lg, lg, lg, lg, lg, ctypes.c_void_p]
-        L.oracle_fwd_dropout.argtypes = [i, i, i, i, i, d, i, lg, d, u64, u32,
+        L.oracle_fwd_dropout.argtypes = [i, i, i, i, i, d, i, lg, d, u64, u32, lg,
                                          dp, dp, dp, dp, dp, i]
-        L.oracle_bwd_dropout.argtypes = [i, i, i, i, i, d, i, lg, d, u64, u32,
+        L.oracle_bwd_dropout.argtypes = [i, i, i, i, i, d, i, lg, d, u64, u32, lg,
                                          dp, dp, dp, dp, dp, dp, dp, dp, i]
         _lib = L
     return _lib
@@ -292,22 +292,24 @@ def dropout_mask(seed: int, offset: int, p: float, bh: int, rows: int, cols: int
 
 
 def fwd_dropout(q, k, v, scale: float, p: float, seed: int, offset: int = 0,
-                causal: bool = False, window: int = 0, nthreads: int = 0):
-    """O (with dropout on P) and L for q [B, H, N, d], k, v [B, Hkv, N, d]."""
+                causal: bool = False, window: int = 0, nthreads: int = 0, bh0: int = 0):
+    """O (with dropout on P) and L for q [B, H, N, d], k, v [B, Hkv, N, d]; the
+    query heads are heads bh0, bh0 + 1, ... of the generator's numbering."""
     q, k, v = _f64(q), _f64(k), _f64(v)
     B, H, Hkv, N, d = _gqa_shapes(q, k)
     assert v.shape == k.shape
     o = np.empty_like(q)
     lse = np.empty(q.shape[:-1], np.float64)
     lib().oracle_fwd_dropout(B, H, Hkv, N, d, float(scale), int(causal), int(window),
-                             float(p), int(seed), int(offset), _p(q), _p(k), _p(v), _p(o),
-                             _p(lse), int(nthreads))
+                             float(p), int(seed), int(offset), int(bh0), _p(q), _p(k),
+                             _p(v), _p(o), _p(lse), int(nthreads))
     return o, lse
 
 
 def bwd_dropout(q, k, v, dout, scale: float, p: float, seed: int, offset: int = 0,
-                causal: bool = False, window: int = 0, nthreads: int = 0):
-    """dQ, dK, dV (summed over each group) and D of attention with dropout on P."""
+                causal: bool = False, window: int = 0, nthreads: int = 0, bh0: int = 0):
+    """dQ, dK, dV (summed over each group) and D of attention with dropout on P
+    (head numbering as fwd_dropout)."""
     q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
     B, H, Hkv, N, d = _gqa_shapes(q, k)
     assert v.shape == k.shape and dout.shape == q.shape
@@ -315,6 +317,6 @@ def bwd_dropout(q, k, v, dout, scale: float, p: float, seed: int, offset: int = 
     dk, dv = np.empty_like(k), np.empty_like(k)
     D = np.empty(q.shape[:-1], np.float64)
     lib().oracle_bwd_dropout(B, H, Hkv, N, d, float(scale), int(causal), int(window),
-                             float(p), int(seed), int(offset), _p(q), _p(k), _p(v),
-                             _p(dout), _p(dq), _p(dk), _p(dv), _p(D), int(nthreads))
+                             float(p), int(seed), int(offset), int(bh0), _p(q), _p(k),
+                             _p(v), _p(dout), _p(dq), _p(dk), _p(dv), _p(D), int(nthreads))
     return dq, dk, dv, D

@@ -519,9 +519,12 @@ void oracle_dropout_mask(uint64_t seed, uint32_t offset, int t, long bh, long i0
 }
 
 /* Forward with dropout for q [B][H][N][d], k, v [B][Hkv][N][d]: O_i =
- * sum_j P_ij Z_ij / keep V_j, L_i the log-sum-exp of the undropped scores. */
+ * sum_j P_ij Z_ij / keep V_j, L_i the log-sum-exp of the undropped scores.
+ * The query heads given are heads bh0, bh0 + 1, ... of the generator's
+ * numbering (bh0 = 0 for a whole tensor; a slice of heads passes its first
+ * head's index). */
 void oracle_fwd_dropout(int B, int H, int Hkv, int N, int d, double scale, int causal,
-                        long window, double p, uint64_t seed, uint32_t offset,
+                        long window, double p, uint64_t seed, uint32_t offset, long bh0,
                         const double* q, const double* k, const double* v, double* o,
                         double* lse, int nthreads) {
   if (nthreads > 0) omp_set_num_threads(nthreads);
@@ -540,7 +543,7 @@ void oracle_fwd_dropout(int B, int H, int Hkv, int N, int d, double scale, int c
                 v + kv * hs, srow, prow, o_row, lse ? lse + r : NULL);
       for (int c = 0; c < d; ++c) o_row[c] = 0.0;
       for (long j = 0; j < N; ++j) {
-        if (prow[j] == 0.0 || !oracle_dropout_keep(seed, offset, t, bh, i, j)) continue;
+        if (prow[j] == 0.0 || !oracle_dropout_keep(seed, offset, t, bh0 + bh, i, j)) continue;
         const double w = prow[j] / keep;
         const double* vj = v + kv * hs + j * (long)d;
         for (int c = 0; c < d; ++c) o_row[c] += w * vj[c];
@@ -551,10 +554,10 @@ void oracle_fwd_dropout(int B, int H, int Hkv, int N, int d, double scale, int c
   }
 }
 
-/* Backward with dropout, same shapes; dk, dv [B][Hkv][N][d] are summed over
- * the query heads of each group.  Dvec [B][H][N] receives D_i. */
+/* Backward with dropout, same shapes and head numbering; dk, dv [B][Hkv][N][d]
+ * are summed over the query heads of each group.  Dvec [B][H][N] receives D_i. */
 void oracle_bwd_dropout(int B, int H, int Hkv, int N, int d, double scale, int causal,
-                        long window, double p, uint64_t seed, uint32_t offset,
+                        long window, double p, uint64_t seed, uint32_t offset, long bh0,
                         const double* q, const double* k, const double* v,
                         const double* dout, double* dq, double* dk, double* dv,
                         double* Dvec, int nthreads) {
@@ -584,7 +587,7 @@ void oracle_bwd_dropout(int B, int H, int Hkv, int N, int d, double scale, int c
                   o_row, NULL);
         /* Z_ij / keep, dP_ij = (dO_i . V_j) Z_ij / keep, and P~_ij = P_ij Z_ij / keep */
         for (long j = 0; j < N; ++j) {
-          const double z = (prow[j] != 0.0 && oracle_dropout_keep(seed, offset, t, bh, i, j))
+          const double z = (prow[j] != 0.0 && oracle_dropout_keep(seed, offset, t, bh0 + bh, i, j))
                                ? 1.0 / keep
                                : 0.0;
           dprow[j] = z * dot(doh + i * (long)d, vh + j * (long)d, d);

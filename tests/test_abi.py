@@ -28,7 +28,8 @@ def test_header_declares_the_boundary():
     assert declared_functions() == sorted(
         ["attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_bwd_preprocess",
          "attn_bwd_dkdv", "attn_bwd_dq", "attn_fwd_fp8", "attn_decode_workspace_bytes",
-         "attn_fwd_decode", "attn_fwd_fp8_blocks", "attn_status_str"])
+         "attn_fwd_decode", "attn_fwd_fp8_blocks", "attn_fwd_dropout", "attn_bwd_dropout",
+         "attn_status_str"])
 
 
 def test_library_exports_every_declared_symbol(ea):
@@ -126,6 +127,43 @@ def test_fp8_rejects_bad_descales(ea):
     for qs, ks, vs in ((0.0, 1.0, 1.0), (1.0, -1.0, 1.0), (1.0, 1.0, math.nan)):
         assert ea.lib.attn_fwd_fp8(ctypes.byref(desc), vp(FAKE), vp(FAKE), vp(FAKE),
                                    qs, ks, vs, vp(FAKE), 0, None, None) == ea.ATTN_EINVAL
+
+
+@pytest.mark.parametrize("p,expect", [(-0.1, 1), (math.nan, 1), (math.inf, 1),
+                                      (255.5 / 256, 1), (0.999, 1)])
+def test_dropout_rejects_bad_probabilities(ea, p, expect):
+    """p must be finite, >= 0, with round(256 p) <= 255; checked before any launch."""
+    desc = ea.make_desc(1, 2, 64, 64, 0.1, False, 0)
+    ws = ea.lib.attn_bwd_workspace_bytes(ctypes.byref(desc))
+    vp = ctypes.c_void_p
+    f = vp(FAKE)
+    drop = ea.AttnDropout(p, 0, 1)
+    assert ea.lib.attn_fwd_dropout(ctypes.byref(desc), ctypes.byref(drop), f, f, f, f, 0,
+                                   None, None) == expect
+    assert ea.lib.attn_bwd_dropout(ctypes.byref(desc), ctypes.byref(drop), *([f] * 10), ws,
+                                   None) == expect
+
+
+def test_dropout_rejects_null_description_and_bad_arguments(ea):
+    desc = ea.make_desc(1, 2, 64, 64, 0.1, False, 0)
+    ws = ea.lib.attn_bwd_workspace_bytes(ctypes.byref(desc))
+    vp = ctypes.c_void_p
+    f = vp(FAKE)
+    drop = ea.AttnDropout(0.1, 0, 1)
+    assert ea.lib.attn_fwd_dropout(ctypes.byref(desc), None, f, f, f, f, 0, None, None) == 1
+    assert ea.lib.attn_bwd_dropout(ctypes.byref(desc), None, *([f] * 10), ws, None) == 1
+    assert ea.lib.attn_fwd_dropout(ctypes.byref(desc), ctypes.byref(drop), f, None, f, f, 0,
+                                   None, None) == 1
+    assert ea.lib.attn_fwd_dropout(ctypes.byref(desc), ctypes.byref(drop), f, f, f, f, 5,
+                                   None, None) == 1
+    assert ea.lib.attn_bwd_dropout(ctypes.byref(desc), ctypes.byref(drop), *([f] * 10),
+                                   ws - 1, None) == 1
+    bad = ea.make_desc(1, 2, 64, 80, 0.1, False, 0)
+    assert ea.lib.attn_fwd_dropout(ctypes.byref(bad), ctypes.byref(drop), f, f, f, f, 0,
+                                   None, None) == 2
+    assert ctypes.sizeof(ea.AttnDropout) == 16
+    with pytest.raises(ValueError):
+        ea.make_dropout(0.1, -1)
 
 
 def test_binding_refuses_host_tensors(ea):

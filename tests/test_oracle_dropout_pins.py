@@ -191,6 +191,22 @@ def test_gqa_dropout_equals_repeated_heads():
     np.testing.assert_allclose(dv, dv1.reshape(2, 2, 2, 19, 8).sum(2), atol=1e-13)
 
 
+def test_head_offset_numbers_a_slice_like_the_whole():
+    q, k, v, do = (rnd(90 + x, 2, 3, 21, 8) for x in range(4))
+    o, lse = oracle.fwd_dropout(q, k, v, 0.4, 0.3, 12, 3, causal=True)
+    g = oracle.bwd_dropout(q, k, v, do, 0.4, 0.3, 12, 3, causal=True)
+    b, h = 1, 2
+    sl = (slice(b, b + 1), slice(h, h + 1))
+    o1, lse1 = oracle.fwd_dropout(q[sl], k[sl], v[sl], 0.4, 0.3, 12, 3, causal=True,
+                                  bh0=b * 3 + h)
+    np.testing.assert_array_equal(o1, o[sl])
+    np.testing.assert_array_equal(lse1, lse[sl])
+    g1 = oracle.bwd_dropout(q[sl], k[sl], v[sl], do[sl], 0.4, 0.3, 12, 3, causal=True,
+                            bh0=b * 3 + h)
+    for a, r in zip(g1, g):
+        np.testing.assert_array_equal(a, r[sl])
+
+
 # ---------------------------------------------------------------- backward
 
 def torch_dropout_attention(q, k, v, z, keep, scale, causal, window):
