@@ -300,6 +300,99 @@ def measure_dropout(ea, torch, attn_synth, reps=10, p=0.1):
     return out
 
 
+def _time_ms(torch, fn, reps):
+    fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def measure_configs(ea, torch, reps=10):
+    """Every workload of the metric beside the timed step: the single-head
+    forward (latency and HBM rate), the long-context causal and window
+    forwards, the B4 H16 N4096 causal backward, the fp8 forward, and the
+    N >= 4096, d = 128 points at which the forward and backward targets are
+    stated.  Inputs are N(0,1) draws of torch's seeded device generator (the
+    same distributions as the tests' inputs, drawn on the device because the
+    host generator needs tens of seconds at these sizes); the fp8 inputs get
+    the outlier channel (x10) and per-tensor e4m3 scales on the device too.
+    Measured after the timed step; none of it enters `value`."""
+    gen = torch.Generator(device="cuda").manual_seed(79)
+
+    def randn(*shape):
+        return torch.randn(shape, device="cuda", generator=gen).bfloat16()
+
+    def pct(tf, peak=PEAK_BF16_TFLOPS):
+        return round(100.0 * tf / peak, 1)
+
+    out = {}
+    # Single head, fp32 output: launch-latency bound, reported as time and GB/s.
+    q, k, v = randn(1, 1, 256, 64), randn(1, 1, 256, 64), randn(1, 1, 256, 64)
+    o = torch.empty(q.shape, device="cuda", dtype=torch.float32)
+    lse = torch.empty((1, 1, 256), device="cuda", dtype=torch.float32)
+    ms = _time_ms(torch, lambda: ea.attn_fwd(q, k, v, out_dtype=torch.float32, out=o,
+                                             lse=lse), 50)
+    nbytes = 3 * 256 * 64 * 2 + 256 * 64 * 4 + 256 * 4
+    out["fwd B1 H1 N256 d64 fp32-out"] = {"us": round(ms * 1e3, 2),
+                                          "gbps": round(nbytes / (ms * 1e-3) / 1e9, 1)}
+    # Long context, causal and causal window 4096.
+    B, H, N, d = 1, 32, 16384, 128
+    q, k, v = randn(B, H, N, d), randn(B, H, N, d), randn(B, H, N, d)
+    o, lse = ea.attn_fwd(q, k, v, causal=True)
+    for window in (0, 4096):
+        f = credited_fwd_flops(B * H, N, d, True, window)
+        ms = _time_ms(torch, lambda: ea.attn_fwd(q, k, v, causal=True, window=window,
+                                                 out=o, lse=lse), reps)
+        tf = f / (ms * 1e-3) / 1e12
+        out[f"fwd B1 H32 N16384 d128 causal window={window}"] = {
+            "ms": round(ms, 4), "tflops": round(tf, 1), "pct_peak": pct(tf)}
+    del q, k, v, o, lse
+    # The forward and backward targets (N >= 4096, d = 128) and the causal backward.
+    for B, H, N, causal in ((4, 16, 4096, True), (4, 16, 4096, False), (2, 32, 8192, False),
+                            (2, 32, 8192, True)):
+        d = 128
+        q, k, v, do = (randn(B, H, N, d) for _ in range(4))
+        o, lse = ea.attn_fwd(q, k, v, causal=causal)
+        ws = torch.empty(ea.attn_bwd_workspace_bytes(B, H, N, d), device="cuda",
+                         dtype=torch.uint8)
+        grads = tuple(torch.empty(q.shape, device="cuda", dtype=torch.float32)
+                      for _ in range(3))
+        f = credited_fwd_flops(B * H, N, d, causal, 0)
+        ms_f = _time_ms(torch, lambda: ea.attn_fwd(q, k, v, causal=causal, out=o, lse=lse),
+                        reps)
+        ms_b = _time_ms(torch, lambda: ea.attn_bwd(q, k, v, o, do, lse, causal=causal,
+                                                   workspace=ws, grads=grads), reps)
+        tf_f, tf_b = f / (ms_f * 1e-3) / 1e12, 2.5 * f / (ms_b * 1e-3) / 1e12
+        out[f"B{B} H{H} N{N} d{d} {'causal' if causal else 'non-causal'}"] = {
+            "fwd": {"ms": round(ms_f, 4), "tflops": round(tf_f, 1), "pct_peak": pct(tf_f)},
+            "bwd": {"ms": round(ms_b, 4), "tflops": round(tf_b, 1), "pct_peak": pct(tf_b)}}
+        del q, k, v, do, o, lse, ws, grads
+    # fp8 forward with one x10 outlier channel and per-tensor e4m3 scales.
+    B, H, N, d = 2, 32, 8192, 128
+    codes, descales = [], []
+    for _ in range(3):
+        x = torch.randn((B, H, N, d), device="cuda", generator=gen)
+        x[..., 17] *= 10.0
+        ds = float(x.abs().max()) / 448.0
+        codes.append((x / ds).to(torch.float8_e4m3fn).view(torch.uint8).contiguous())
+        descales.append(ds)
+        del x
+    o = torch.empty((B, H, N, d), device="cuda", dtype=torch.bfloat16)
+    lse = torch.empty((B, H, N), device="cuda", dtype=torch.float32)
+    f = credited_fwd_flops(B * H, N, d, False, 0)
+    ms = _time_ms(torch, lambda: ea.attn_fwd_fp8(*codes, *descales, out=o, lse=lse), reps)
+    tf = f / (ms * 1e-3) / 1e12
+    out["fp8 fwd B2 H32 N8192 d128 non-causal"] = {
+        "ms": round(ms, 4), "tflops": round(tf, 1), "pct_fp8_peak": pct(tf, PEAK_FP8_TFLOPS),
+        "pct_bf16_peak": pct(tf)}
+    return out
+
+
 def measure_decode(ea, torch, attn_synth, reps=20):
     """Decode: one query per head at the end of a 32768-key sequence, B4 H32
     with 8 key/value heads, d128 (attn_fwd_decode: key-split pass + merge).
@@ -463,6 +556,7 @@ def main():
         out["gqa"] = measure_gqa(ea, torch, attn_synth)
         out["decode"] = measure_decode(ea, torch, attn_synth)
         out["dropout"] = measure_dropout(ea, torch, attn_synth)
+        out["configs"] = measure_configs(ea, torch)
     if args.hbm_copy_mib > 0:
         # fp32 -> bf16, so that the copy runs as an elementwise kernel (a
         # same-dtype copy may go to a DMA engine that the counters miss).
