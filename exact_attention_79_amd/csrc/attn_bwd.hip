@@ -124,7 +124,8 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(BwdKParams p) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int h = lane >> 5, n = lane & 31;
   // Low key blocks see the most queries under the causal mask: rank = block.
-  const TileId id = tile_order(blockIdx.x, gridDim.x / p.n_tiles, p.n_tiles, p.causal);
+  const TileId id =
+      tile_order(blockIdx.x, gridDim.x / p.n_tiles, p.n_tiles, p.causal, causal_group<D>());
   const int bkv = id.bh;  // key/value head (b * Hkv + hk)
   const int kt = id.rank;
   const int N = p.N, W = p.window;
@@ -380,7 +381,8 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdKParams p) {
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int h = lane >> 5, n = lane & 31;
-  const TileId id = tile_order(blockIdx.x, gridDim.x / p.n_tiles, p.n_tiles, p.causal);
+  const TileId id =
+      tile_order(blockIdx.x, gridDim.x / p.n_tiles, p.n_tiles, p.causal, causal_group<D>());
   const int bh = id.bh;
   const int qt = p.causal ? p.n_tiles - 1 - id.rank : id.rank;  // longest first
   const int N = p.N, W = p.window;

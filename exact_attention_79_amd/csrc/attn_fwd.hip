@@ -73,7 +73,8 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdKParams p) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int h = lane >> 5, n = lane & 31;
   // With the causal mask the last query blocks are the longest: run them first.
-  const TileId id = tile_order(blockIdx.x, gridDim.x / p.n_qtiles, p.n_qtiles, p.causal);
+  const TileId id =
+      tile_order(blockIdx.x, gridDim.x / p.n_qtiles, p.n_qtiles, p.causal, causal_group<D>());
   const int bh = id.bh;
   const int qt = p.causal ? p.n_qtiles - 1 - id.rank : id.rank;
   const int N = p.N;

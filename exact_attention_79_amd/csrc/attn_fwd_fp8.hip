@@ -128,7 +128,8 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8_kernel(FwdFp8Params p) {
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int h = lane >> 5, n = lane & 31;
-  const TileId id = tile_order(blockIdx.x, gridDim.x / p.n_qtiles, p.n_qtiles, p.causal);
+  const TileId id =
+      tile_order(blockIdx.x, gridDim.x / p.n_qtiles, p.n_qtiles, p.causal, 0);
   const int bh = id.bh;
   const int qt = p.causal ? p.n_qtiles - 1 - id.rank : id.rank;  // longest first
   const int N = p.N;
