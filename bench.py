@@ -218,7 +218,7 @@ def measure_gqa(ea, torch, attn_synth, reps=10):
     out = {"workload": f"B{B} H{H} H_kv{Hkv} N{N} d{d}, bf16"}
     for causal in (False, True):
         o, lse = ea.attn_fwd(q, k, v, causal=causal)
-        ws = torch.empty(ea.attn_bwd_workspace_bytes(B, H, N, d), device="cuda",
+        ws = torch.empty(ea.attn_bwd_workspace_bytes(B, H, N, d, Hkv, causal), device="cuda",
                          dtype=torch.uint8)
         dq = torch.empty(q.shape, device="cuda", dtype=torch.float32)
         dk, dv = (torch.empty(k.shape, device="cuda", dtype=torch.float32)

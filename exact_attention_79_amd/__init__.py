@@ -184,8 +184,11 @@ def attn_fwd_dropout(q, k, v, p: float, seed: int, offset: int = 0,
     return (o, lse) if return_lse else o
 
 
-def attn_bwd_workspace_bytes(B: int, H: int, N: int, d: int) -> int:
-    desc = make_desc(B, H, N, d, 1.0, False, 0)
+def attn_bwd_workspace_bytes(B: int, H: int, N: int, d: int, H_kv: int = 0,
+                             causal: bool = False) -> int:
+    """Workspace bytes of the backward (see include/attn.h; grouped-query
+    backwards may need partial dK/dV space, which depends on H_kv and causal)."""
+    desc = make_desc(B, H, N, d, 1.0, causal, 0, H_kv)
     return int(lib.attn_bwd_workspace_bytes(ctypes.byref(desc)))
 
 

@@ -67,6 +67,16 @@ size_t ws_array_bytes(const attn_desc* d) {
   return (rows * sizeof(float) + 255) & ~(size_t)255;
 }
 
+// The partial dK (then dV) arrays of a split group walk, each padded to 256
+// bytes; 0 when the dK/dV pass does not split (attn::dkdv_split).
+size_t ws_share_bytes(const attn_desc* d) {
+  const int split =
+      attn::dkdv_split(d->B * kv_heads(d), d->H / kv_heads(d), d->N, d->d, d->causal);
+  if (split <= 1) return 0;
+  const size_t elems = (size_t)split * d->B * kv_heads(d) * d->N * d->d;
+  return (elems * sizeof(float) + 255) & ~(size_t)255;
+}
+
 attn::BwdArgs bwd_args(const attn_desc* d, const void* q, const void* k,
                       const void* v, const void* o, const void* dout,
                       const float* lse, float* dq, float* dk, float* dv,
@@ -83,6 +93,8 @@ attn::BwdArgs bwd_args(const attn_desc* d, const void* q, const void* k,
   a.dv = dv;
   a.delta = (float*)workspace;
   a.lse2 = (float*)((char*)workspace + ws_array_bytes(d));
+  a.dk_part = (float*)((char*)workspace + 2 * ws_array_bytes(d));
+  a.dv_part = (float*)((char*)a.dk_part + ws_share_bytes(d));
   a.BH = d->B * d->H;
   a.H = d->H;
   a.Hkv = kv_heads(d);
@@ -124,7 +136,8 @@ attn_status attn_fwd(const attn_desc* desc, const void* q, const void* k,
 
 size_t attn_bwd_workspace_bytes(const attn_desc* desc) {
   if (check_desc(desc) != ATTN_OK) return 0;
-  return 2 * ws_array_bytes(desc);  // D, then L log2(e)
+  // D, then L log2(e), then the partial dK and dV of a split group walk.
+  return 2 * ws_array_bytes(desc) + 2 * ws_share_bytes(desc);
 }
 
 attn_status attn_bwd(const attn_desc* desc, const void* q, const void* k,

@@ -35,6 +35,8 @@
 // swizzle as the forward.
 #include <limits.h>
 
+#include <algorithm>
+
 #include "attn_device.hpp"
 #include "attn_kernels.hpp"
 
@@ -83,6 +85,9 @@ struct BwdKParams {
   const float* lse;  // natural-log L from the forward (dQ kernel)
   float* delta;      // workspace: D_i
   float* lse2;       // workspace: L_i log2(e)
+  float* dk_part;    // workspace: partial dK, dV of each share (split > 1)
+  float* dv_part;
+  int split;         // workgroups per key block and group (dkdv_split)
   int H, Hkv;        // query heads per batch element; key/value heads
   float* dq;
   float* dk;
@@ -132,13 +137,16 @@ __global__ __launch_bounds__(NW * 64, (dkdv_waves_per_simd<D, BQ>())) void bwd_d
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int h = lane >> 5, n = lane & 31;
   // Low key blocks see the most queries under the causal mask: rank = block.
+  // The grid's heads are (key/value head, share) pairs, the shares of one
+  // key/value head adjacent (same XCD, same K and V).
   const TileId id =
       tile_order(blockIdx.x, gridDim.x / p.n_tiles, p.n_tiles, p.causal, causal_group<D>());
-  const int bkv = id.bh;  // key/value head (b * Hkv + hk)
+  const int bkv = id.bh / p.split;   // key/value head (b * Hkv + hk)
+  const int share = id.bh % p.split;
   const int kt = id.rank;
   const int N = p.N, W = p.window;
-  const int G = p.H / p.Hkv;  // query heads reading this key/value head
-  const int bh0 = (bkv / p.Hkv) * p.H + (bkv % p.Hkv) * G;  // the first of them
+  const int G = p.H / p.Hkv / p.split;  // query heads this workgroup walks
+  const int bh0 = (bkv / p.Hkv) * p.H + (bkv % p.Hkv) * (p.H / p.Hkv) + share * G;
   const int k0 = kt * BKV;
   const int kw0 = k0 + 32 * w;
   const int my_k = kw0 + n;
@@ -346,6 +354,14 @@ __global__ __launch_bounds__(NW * 64, (dkdv_waves_per_simd<D, BQ>())) void bwd_d
     if (u + 2 < U) iteration(sQ2, sO2, sL2, sD2, sQ0, sO0, sQ1, sO1, sL1, sD1);
   }
 
+  // With the group split, this share's partial sums go to the workspace.
+  float* dk_out = p.dk;
+  float* dv_out = p.dv;
+  if (p.split > 1) {
+    const size_t part = (size_t)(gridDim.x / p.n_tiles / p.split) * N * D;
+    dk_out = p.dk_part + share * part;
+    dv_out = p.dv_part + share * part;
+  }
   if (my_k < N) {
     const size_t row = head + (size_t)my_k * D;
     const float vs = DROP ? p.drop.inv_keep : 1.f;
@@ -354,17 +370,29 @@ __global__ __launch_bounds__(NW * 64, (dkdv_waves_per_simd<D, BQ>())) void bwd_d
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int d0 = 32 * dt + 8 * g + 4 * h;
-        *(f32x4*)(p.dk + row + d0) =
+        *(f32x4*)(dk_out + row + d0) =
             (f32x4){dkacc[dt][4 * g] * p.scale, dkacc[dt][4 * g + 1] * p.scale,
                     dkacc[dt][4 * g + 2] * p.scale, dkacc[dt][4 * g + 3] * p.scale};
         if constexpr (DROP)
-          *(f32x4*)(p.dv + row + d0) =
+          *(f32x4*)(dv_out + row + d0) =
               (f32x4){dvacc[dt][4 * g] * vs, dvacc[dt][4 * g + 1] * vs,
                       dvacc[dt][4 * g + 2] * vs, dvacc[dt][4 * g + 3] * vs};
         else
-          *(f32x4*)(p.dv + row + d0) = (f32x4){dvacc[dt][4 * g], dvacc[dt][4 * g + 1],
-                                               dvacc[dt][4 * g + 2], dvacc[dt][4 * g + 3]};
+          *(f32x4*)(dv_out + row + d0) = (f32x4){dvacc[dt][4 * g], dvacc[dt][4 * g + 1],
+                                                 dvacc[dt][4 * g + 2], dvacc[dt][4 * g + 3]};
       }
+  }
+}
+
+// out = sum over `split` partial arrays of n4 float4 each (stride n4 apart),
+// in share order, so the result does not depend on scheduling.
+__global__ __launch_bounds__(256) void bwd_share_sum_kernel(const f32x4* part, f32x4* out,
+                                                            size_t n4, int split) {
+  for (size_t i = blockIdx.x * (size_t)256 + threadIdx.x; i < n4;
+       i += (size_t)gridDim.x * 256) {
+    f32x4 acc = part[i];
+    for (int s = 1; s < split; ++s) acc += part[s * n4 + i];
+    out[i] = acc;
   }
 }
 
@@ -593,6 +621,9 @@ static BwdKParams bwd_params(const BwdArgs& a, int tile_rows) {
   p.window = a.window;
   p.n_tiles = (a.N + tile_rows - 1) / tile_rows;
   p.drop = make_dropout(a.drop);
+  p.dk_part = a.dk_part;
+  p.dv_part = a.dv_part;
+  p.split = 1;
   return p;
 }
 
@@ -621,10 +652,11 @@ hipError_t launch_bwd_preprocess(const BwdArgs& a, hipStream_t stream) {
 }
 
 hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream) {
-  const BwdKParams p = bwd_params(a, 32 * kBwdWaves);
-  // One workgroup per key block of every key/value head.
+  BwdKParams p = bwd_params(a, 32 * kBwdWaves);
+  // One workgroup per key block of every key/value head and share of its group.
   const int BHkv = a.BH / a.H * a.Hkv;
-  const dim3 grid((unsigned)(BHkv * p.n_tiles)), block(64 * kBwdWaves);
+  p.split = dkdv_split(BHkv, a.H / a.Hkv, a.N, a.d, a.causal);
+  const dim3 grid((unsigned)(BHkv * p.n_tiles * p.split)), block(64 * kBwdWaves);
   const bool drop = a.drop.thresh > 0;
   if (a.d == 128 && drop)
     hipLaunchKernelGGL((bwd_dkdv_kernel<128, kBwdWaves, kDropQTile, true>), grid, block, 0,
@@ -638,6 +670,14 @@ hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream) {
   else
     hipLaunchKernelGGL((bwd_dkdv_kernel<64, kBwdWaves, dkdv_qtile<64>(), false>), grid,
                        block, 0, stream, p);
+  if (p.split > 1) {
+    const size_t n4 = (size_t)BHkv * a.N * a.d / 4;
+    const unsigned sum_grid = (unsigned)std::min<size_t>((n4 + 255) / 256, 8192);
+    hipLaunchKernelGGL(bwd_share_sum_kernel, dim3(sum_grid), dim3(256), 0, stream,
+                       (const f32x4*)a.dk_part, (f32x4*)a.dk, n4, p.split);
+    hipLaunchKernelGGL(bwd_share_sum_kernel, dim3(sum_grid), dim3(256), 0, stream,
+                       (const f32x4*)a.dv_part, (f32x4*)a.dv, n4, p.split);
+  }
   return hipGetLastError();
 }
 

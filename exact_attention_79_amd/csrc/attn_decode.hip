@@ -24,8 +24,9 @@
 // (one 16-byte load per lane and K-step), V_t fetched by direct global->LDS
 // loads into a wave-private pair of swizzled LDS slots and read transposed
 // (ds_read_b64_tr_b16) as the A operand of O^T += V_t^T P^T, as in the
-// forward.  Two tiles are in flight per wave; with eight waves per CU that
-// keeps enough bytes outstanding to cover the HBM latency.
+// forward.  Two tiles (16 KB) are in flight per wave; the plan below runs
+// about three waves per CU, which keeps more than enough bytes outstanding
+// to cover the HBM latency (more in flight reads slower, not faster).
 #include <algorithm>
 
 #include "attn_device.hpp"

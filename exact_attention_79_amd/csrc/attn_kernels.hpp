@@ -45,6 +45,8 @@ struct BwdArgs {
   float* dv;
   float* delta;        // fp32 [BH][N] workspace: D_i = sum_k dO_ik O_ik
   float* lse2;         // fp32 [BH][N] workspace: L_i log2(e)
+  float* dk_part;      // workspace, when dkdv_split > 1: fp32 [split][B*Hkv][N][d]
+  float* dv_part;      //   partial dK, dV of each share of the query heads
   int BH, H, Hkv, N, d;
   float scale;
   int causal, window;
@@ -70,6 +72,24 @@ struct DecodePlan {
   int P, CW, kmin;     // chunks, keys per chunk, first key any row sees
 };
 DecodePlan decode_plan(int B, int H, int Hkv, int Nq, int Nk, int window);
+
+// The dK/dV pass gives each key block of a key/value head to one workgroup,
+// which walks the query heads of its group (G = H / Hkv) and sums dK, dV over
+// them in registers.  When that grid is too small for the chip (less than
+// one round of workgroups over the 256 CUs, or, causal, less than two rounds,
+// so that the uneven key blocks can even out), each group is split over
+// `split` workgroups that write partial dK, dV to the workspace, summed by a
+// second launch.  One round is 256 workgroups at d = 128 (one per CU) and
+// 512 at d = 64 (two per CU).  Returns the smallest divisor of G that reaches
+// the target, G if none does, 1 when there is nothing to split.
+inline int dkdv_split(int BHkv, int G, int N, int d, int causal) {
+  const long grid = (long)BHkv * ((N + 127) / 128);  // 128-key blocks
+  const long want = 256L * (d == 64 ? 2 : 1) * (causal ? 2 : 1);
+  if (G <= 1 || grid >= want) return 1;
+  for (int s = 2; s < G; ++s)
+    if (G % s == 0 && grid * s >= want) return s;
+  return G;
+}
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);

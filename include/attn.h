@@ -97,7 +97,14 @@ attn_status attn_fwd(const attn_desc* desc, const void* q, const void* k,
 
 /* Bytes of device workspace the backward needs for `desc`: two fp32 [B,H,N]
  * arrays, D_i = sum_k dO_ik O_ik and L_i log2(e), each padded to a multiple
- * of 256 bytes.  0 if `desc` is invalid. */
+ * of 256 bytes; for grouped-query attention (H_kv < H) whose dK/dV pass would
+ * otherwise run on too few workgroups (less than one round over the 256
+ * CUs, a round being one workgroup per CU at d = 128 and two at d = 64; with
+ * the causal mask, less than two rounds), also two fp32 arrays of
+ * S x [B,H_kv,N,d] partial dK and dV, where the query heads of each group
+ * are split into S shares (S a divisor of H / H_kv) whose sums are added by
+ * a second launch in share order (deterministic).  Depends on B, H, H_kv, N,
+ * d and causal.  0 if `desc` is invalid. */
 size_t attn_bwd_workspace_bytes(const attn_desc* desc);
 
 /* Backward (FLASH-ATTN page, FlashAttention-2 summary "Background": dV = P^T dO,

@@ -102,6 +102,33 @@ def test_bwd_workspace_and_rejections(ea):
         ea.ATTN_EUNSUPPORTED
 
 
+def split_of(B, H, H_kv, N, d, causal):
+    """The documented share count of the grouped dK/dV walk (include/attn.h)."""
+    G, grid = H // H_kv, B * H_kv * ((N + 127) // 128)
+    want = 256 * (2 if d == 64 else 1) * (2 if causal else 1)
+    if G <= 1 or grid >= want:
+        return 1
+    return next((s for s in range(2, G) if G % s == 0 and grid * s >= want), G)
+
+
+@pytest.mark.parametrize("B,H,H_kv,N,d,causal,S", [
+    (4, 16, 16, 2048, 128, True, 1), (4, 16, 4, 2048, 128, False, 1),
+    (4, 16, 4, 2048, 128, True, 2), (4, 16, 4, 2048, 64, True, 4),
+    (4, 16, 4, 2048, 64, False, 2), (1, 8, 1, 2048, 64, False, 8),
+    (2, 6, 3, 100, 64, True, 2), (8, 32, 8, 4096, 128, True, 1),
+    (4, 16, 4, 4096, 128, True, 1), (2, 12, 2, 1024, 128, True, 6)])
+def test_bwd_workspace_holds_the_split_partials(ea, B, H, H_kv, N, d, causal, S):
+    """Grouped-query backwards whose dK/dV grid would be small split each
+    group over S workgroups and keep S partial dK and dV arrays in the
+    workspace, after the D and L log2(e) arrays."""
+    assert split_of(B, H, H_kv, N, d, causal) == S
+    pad = lambda x: (x + 255) // 256 * 256
+    want = 2 * pad(B * H * N * 4)
+    if S > 1:
+        want += 2 * pad(S * B * H_kv * N * d * 4)
+    assert ea.attn_bwd_workspace_bytes(B, H, N, d, H_kv, causal) == want
+
+
 def test_bwd_stages_reject_bad_arguments(ea):
     desc = ea.make_desc(1, 2, 64, 64, 0.1, False, 0)
     ws = ea.lib.attn_bwd_workspace_bytes(ctypes.byref(desc))
