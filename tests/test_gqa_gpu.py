@@ -125,3 +125,30 @@ def test_gqa_rejects_bad_head_counts(ea):
     k = torch.zeros(1, 4, 16, 64, device="cuda", dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         ea.attn_fwd(q, k, k)
+
+
+@pytest.mark.parametrize("d,causal", [(128, True), (64, False)])
+def test_split_group_walk(ea, d, causal):
+    """MQA with a tiny key-block grid splits the group over 8 workgroups whose
+    partial dK, dV go through the workspace: the result matches the oracle,
+    is bitwise repeatable, and does not depend on what the workspace held
+    (here NaN bytes)."""
+    B, H, Hkv, N = 1, 8, 1, 700
+    log(f"case: gqa split walk B{B} H{H} Hkv{Hkv} N{N} d{d} causal={causal}")
+    assert ea.attn_bwd_workspace_bytes(B, H, N, d, Hkv, causal) > \
+        ea.attn_bwd_workspace_bytes(B, H, N, d)
+    dev, ref = gqa_case(880 + d, B, H, Hkv, N, d, with_dout=True)
+    o, lse = ea.attn_fwd(dev["q"], dev["k"], dev["v"], causal=causal)
+    nbytes = ea.attn_bwd_workspace_bytes(B, H, N, d, Hkv, causal)
+    runs = []
+    for _ in range(2):
+        ws = torch.full((nbytes,), 0xFF, device="cuda", dtype=torch.uint8)
+        runs.append(ea.attn_bwd(dev["q"], dev["k"], dev["v"], o, dev["do"], lse,
+                                causal=causal, workspace=ws))
+    torch.cuda.synchronize()
+    for a, b in zip(*runs):
+        assert torch.equal(a, b)
+    want = oracle.bwd_gqa(ref["q"], ref["k"], ref["v"], ref["do"], 1 / math.sqrt(d),
+                          causal, 0)[:3]
+    for name, g, r in zip(("dQ", "dK", "dV"), runs[0], want):
+        assert_close(np64(g), r, BF16_MAX, BF16_MEAN, name)
