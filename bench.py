@@ -15,6 +15,12 @@ stream it runs on; the dominant kernel (most GPU time per step) is reported
 against its roofline.  The fp64 CPU oracle is timed on a bounded sample of
 the same workload as a reference point (rank 0 only).
 
+After the timed step, with their own HIP-event timing and outside `value`:
+grouped-query attention (`gqa`), decode (`decode`, against HBM), dropout
+(`dropout`, beside the same calls without it) and every workload of the
+metric (`configs`: single head, long-context causal and window, the
+N >= 4096 forward/backward points, fp8); --no-extra-paths skips them.
+
 The roofline's "traffic" (HBM bytes per launch of the dominant kernel) is
 read from the rocprofv3 counter summary committed under profiles/, and only
 while the kernel sources still hash to the value recorded there; otherwise
