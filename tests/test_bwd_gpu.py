@@ -71,6 +71,24 @@ def test_backward_full_size_two_heads(ea):
 
 
 @pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_step_shape_two_heads(ea, d, causal):
+    """The backward launches bench.py times: B=4, H=16, N=2048, d in {64, 128},
+    causal and non-causal; heads (0,0) and (3,15) compared in full."""
+    B, H, N = 4, 16, 2048
+    log(f"case: bwd B{B} H{H} N{N} d{d} causal={causal}")
+    dev, ref = bf16_case(2, B, H, N, d, with_dout=True)
+    got = fwd_bwd(ea, dev, causal, 0)
+    for b, h in ((0, 0), (B - 1, H - 1)):
+        want = oracle.bwd(ref["q"][b, h], ref["k"][b, h], ref["v"][b, h],
+                          ref["do"][b, h], 1 / math.sqrt(d), causal, 0)[:3]
+        for name, g, r in zip(("dQ", "dK", "dV"), got, want):
+            assert_close(g[b, h], r, BF16_MAX, BF16_MEAN, f"{name} head ({b},{h})")
+    for g in got:
+        assert np.isfinite(g).all()
+
+
+@pytest.mark.parametrize("d", [64, 128])
 def test_gradient_invariants(ea, d):
     """sum_j dK_j = 0 (rows of dS sum to zero); constant V gives dQ = dK = 0."""
     N = 700

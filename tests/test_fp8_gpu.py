@@ -136,6 +136,32 @@ def test_fp8_full_size_sampled(ea):
     assert_close(got, want, FP8_MAX, None, "O sampled rows")
 
 
+def test_fp8_step_shape_sampled(ea):
+    """The fp8 launch bench.py times: B=4, H=16, N=2048, d=128, non-causal;
+    two heads in full and sampled rows of every head."""
+    B, H, N, d = 4, 16, 2048, 128
+    log(f"case: fp8 B{B} H{H} N{N} d{d} non-causal")
+    f8, dev, ref = fp8_case(2, B, H, N, d)
+    s = 1 / math.sqrt(d)
+    o, lse = run_fp8(ea, f8, dev, False, 0)
+    assert np.isfinite(o).all()
+    for b, h in ((0, 0), (B - 1, H - 1)):
+        o_ref, lse_ref = oracle.fwd(ref["q"][b, h], ref["k"][b, h], ref["v"][b, h], s)
+        assert_close(o[b, h], o_ref, FP8_MAX, None, f"O head ({b},{h})")
+        bound = fp8_lse_bound(ref["q"][b, h], ref["k"][b, h], s, False, 0)
+        assert_lse(lse[b, h], lse_ref, bound, f"LSE head ({b},{h})")
+    rng = np.random.default_rng(8)
+    got, want = [], []
+    for b in range(B):
+        for h in range(H):
+            rows = np.unique(rng.integers(0, N, 4))
+            o_ref, _ = oracle.fwd_rows(ref["q"][b, h], ref["k"][b, h], ref["v"][b, h],
+                                       rows, s)
+            got.append(o[b, h][rows]); want.append(o_ref)
+    assert_close(np.concatenate(got), np.concatenate(want), FP8_MAX, None,
+                 "O sampled rows")
+
+
 def test_fp8_window_one_is_exact(ea):
     """window 1: each query sees only its own key, so O = V (times descale)."""
     log("case: fp8 window 1, B1 H2 N300 d128")
