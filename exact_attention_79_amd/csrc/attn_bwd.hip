@@ -297,6 +297,30 @@ __global__ __launch_bounds__(NW * 64, (dkdv_waves_per_simd<D, BQ>())) void bwd_d
     }
 #pragma unroll
     for (int i = 0; i < AHEAD; ++i) aop[i] = arow(i);
+    // P/dS element e in three stages: a) the exponent, b) the exponential
+    // and dP - D (dropout applied), c) dS = P (dP - D) and the bf16 packs.
+    float ea[BQ / 2], eb_p[BQ / 2], eb_d[BQ / 2];
+    auto stage_a = [&](int e) {
+      const int mt2 = e >> 4, r = e & 15, g = 4 * mt2 + (r >> 2);
+      ea[e] = fmaf(scur[mt2][r], s2, -lb[g][r & 3]);
+    };
+    auto stage_b = [&](int e) {
+      const int mt2 = e >> 4, r = e & 15, g = 4 * mt2 + (r >> 2);
+      float pv = fast_exp2(ea[e]), dpv = dpcur[mt2][r];
+      if constexpr (DROP) {
+        const bool kp = dropout_keep(keepw[mt2], r, p.drop.thresh);
+        dpv = kp ? dpv * p.drop.inv_keep : 0.f;
+        pop[e >> 3][e & 7] = (__bf16)(kp ? pv : 0.f);
+      } else {
+        pop[e >> 3][e & 7] = (__bf16)pv;
+      }
+      eb_p[e] = pv;
+      eb_d[e] = dpv - dl[g][r & 3];
+    };
+    auto stage_c = [&](int e) { dsop[e >> 3][e & 7] = (__bf16)(eb_p[e] * eb_d[e]); };
+    // The last two bundles' elements (from EPB (NS - 2) on) finish in product
+    // bundles 0 and 1; their K-step is first read at product bundle 2 (D/32) kk.
+    static_assert(2 * (D / 32) * ((EPB * (NS - 2)) / 8) > 1, "late elements read too early");
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
@@ -311,19 +335,14 @@ __global__ __launch_bounds__(NW * 64, (dkdv_waves_per_simd<D, BQ>())) void bwd_d
         dpnext[mt] = mfma32(aop[i], vop[ks], dpnext[mt]);
       else
         snext[mt] = mfma32(aop[i], kop[ks], snext[mt]);
+      // Three elements at different stages, so that their dependent chains
+      // overlap instead of stalling this (only) wave of the SIMD.
 #pragma unroll
       for (int u = 0; u < EPB; ++u) {
-        const int e = EPB * i + u, mt2 = e >> 4, r = e & 15, g = 4 * mt2 + (r >> 2);
-        const float pv = fast_exp2(fmaf(scur[mt2][r], s2, -lb[g][r & 3]));
-        float dpv = dpcur[mt2][r], pk = pv;
-        if constexpr (DROP) {
-          const bool kp = dropout_keep(keepw[mt2], r, p.drop.thresh);
-          dpv = kp ? dpv * p.drop.inv_keep : 0.f;
-          pk = kp ? pv : 0.f;
-        }
-        const float ds = pv * (dpv - dl[g][r & 3]);
-        pop[e >> 3][e & 7] = (__bf16)pk;
-        dsop[e >> 3][e & 7] = (__bf16)ds;
+        const int e = EPB * i + u;
+        if (e >= 2 * EPB) stage_c(e - 2 * EPB);
+        if (e >= EPB) stage_b(e - EPB);
+        stage_a(e);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -335,6 +354,16 @@ __global__ __launch_bounds__(NW * 64, (dkdv_waves_per_simd<D, BQ>())) void bwd_d
         dkacc[dt] = mfma32(top[j], dsop[kk], dkacc[dt]);
       else
         dvacc[dt] = mfma32(top[j], pop[kk], dvacc[dt]);
+      // The last two bundles' elements finish here, long before the K-step
+      // that reads them (the last one, from product bundle 6 (D / 32) on).
+      if (j < 2) {
+#pragma unroll
+        for (int u = 0; u < EPB; ++u) {
+          const int e = EPB * (NS - 2 + j) + u;
+          stage_c(e);
+          if (j == 0) stage_b(e + EPB);
+        }
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
     // Tile t+2 has landed for every wave; slot c may be refilled next time.
