@@ -134,7 +134,8 @@ __global__ __launch_bounds__(NW * 64, (dkdv_waves_per_simd<D, BQ>())) void bwd_d
   __shared__ __attribute__((aligned(16))) float sL0[LDROWS], sL1[LDROWS], sL2[LDROWS];
   __shared__ __attribute__((aligned(16))) float sD0[LDROWS], sD1[LDROWS], sD2[LDROWS];
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, kept scalar
   const int h = lane >> 5, n = lane & 31;
   // Low key blocks see the most queries under the causal mask: rank = block.
   // The grid's heads are (key/value head, share) pairs, the shares of one
@@ -190,8 +191,8 @@ __global__ __launch_bounds__(NW * 64, (dkdv_waves_per_simd<D, BQ>())) void bwd_d
   auto load_tile = [&](__bf16* Qf, __bf16* Of, float* Lf, float* Df) {
     const int bhq = bh0 + min(lj, G - 1);
     const size_t qhead = (size_t)bhq * N * D;
-    tile_load_lds<D, BQ, NW>(make_rsrc(p.q + qhead, head_bytes), lt * BQ, Qf, w, lane);
-    tile_load_lds<D, BQ, NW>(make_rsrc(p.dout + qhead, head_bytes), lt * BQ, Of, w, lane);
+    tile_load_lds<D, BQ, NW>(p.q + qhead, head_bytes, lt * BQ, Qf, w, lane);
+    tile_load_lds<D, BQ, NW>(p.dout + qhead, head_bytes, lt * BQ, Of, w, lane);
     if (w == 0) {
       vec_load_lds<LDROWS>(make_rsrc(p.lse2 + (size_t)bhq * N, (uint32_t)N * 4), lt * BQ,
                            Lf, lane);
@@ -444,7 +445,8 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdKParams p) {
   __shared__ __attribute__((aligned(16))) __bf16 sV1[BC * D];
   __shared__ __attribute__((aligned(16))) __bf16 sV2[BC * D];
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, kept scalar
   const int h = lane >> 5, n = lane & 31;
   const TileId id =
       tile_order(blockIdx.x, gridDim.x / p.n_tiles, p.n_tiles, p.causal, causal_group<D>());
@@ -458,8 +460,8 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdKParams p) {
   const size_t kv_off = (size_t)kv_head(bh, p.H, p.Hkv) * N * D;
   const uint32_t head_bytes = (uint32_t)N * D * 2;
   const auto rq = make_rsrc(p.q + head, head_bytes);
-  const auto rk = make_rsrc(p.k + kv_off, head_bytes);
-  const auto rv = make_rsrc(p.v + kv_off, head_bytes);
+  const __bf16* kh = p.k + kv_off;
+  const __bf16* vh = p.v + kv_off;
   const auto rdo = make_rsrc(p.dout + head, head_bytes);
   const auto ro = make_rsrc(p.o + head, head_bytes);
 
@@ -519,10 +521,10 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdKParams p) {
     }
   };
 
-  tile_load_lds<D, BC, NW>(rk, t_lo * BC, sK0, w, lane);
-  tile_load_lds<D, BC, NW>(rv, t_lo * BC, sV0, w, lane);
-  tile_load_lds<D, BC, NW>(rk, (t_lo + 1) * BC, sK1, w, lane);
-  tile_load_lds<D, BC, NW>(rv, (t_lo + 1) * BC, sV1, w, lane);
+  tile_load_lds<D, BC, NW>(kh, head_bytes, t_lo * BC, sK0, w, lane);
+  tile_load_lds<D, BC, NW>(vh, head_bytes, t_lo * BC, sV0, w, lane);
+  tile_load_lds<D, BC, NW>(kh, head_bytes, (t_lo + 1) * BC, sK1, w, lane);
+  tile_load_lds<D, BC, NW>(vh, head_bytes, (t_lo + 1) * BC, sV1, w, lane);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   f32x16 scur[BC / 32], dpcur[BC / 32];
@@ -532,8 +534,8 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdKParams p) {
   // (K_t in slot c), S^T, dP^T of tile t+1 (slot n); tile t+2 -> slot f.
   auto iteration = [&](int t, const __bf16* Kc, const __bf16* Kn, const __bf16* Vn,
                        __bf16* Kf, __bf16* Vf) {
-    tile_load_lds<D, BC, NW>(rk, (t + 2) * BC, Kf, w, lane);
-    tile_load_lds<D, BC, NW>(rv, (t + 2) * BC, Vf, w, lane);
+    tile_load_lds<D, BC, NW>(kh, head_bytes, (t + 2) * BC, Kf, w, lane);
+    tile_load_lds<D, BC, NW>(vh, head_bytes, (t + 2) * BC, Vf, w, lane);
     const int kv0 = t * BC;
     bool need_mask = (kv0 + BC > N) || (wq0 + 32 > N);
     if (p.causal) need_mask |= kv0 + BC - 1 > wq0;

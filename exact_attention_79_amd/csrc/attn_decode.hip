@@ -55,7 +55,8 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecKParams p) {
   constexpr int kTileLoads = KS + VLOADS;    // vector-memory ops per tile
   __shared__ __attribute__((aligned(16))) __bf16 sV[NW][2][BC * D];
 
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave index, kept scalar
   const int h = lane >> 5, n = lane & 31;
   const int wpu = (p.P + NW - 1) / NW;  // workgroups per (key/value head, row block)
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
@@ -95,7 +96,6 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecKParams p) {
   const size_t head = (size_t)bkv * p.Nk * D;
   const uint32_t head_bytes = (uint32_t)p.Nk * D * 2;
   const auto rk = make_rsrc(p.k + head, head_bytes);
-  const auto rv = make_rsrc(p.v + head, head_bytes);
   __bf16* slot0 = sV[w][0];
   __bf16* slot1 = sV[w][1];
 
@@ -105,7 +105,7 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecKParams p) {
     for (int ks = 0; ks < KS; ++ks)
       kb[ks] = __builtin_bit_cast(
           bf16x8, buf_load16(rk, (uint32_t)((kv0 + n) * D + 16 * ks + 8 * h) * 2u));
-    tile_load_lds<D, BC, 1>(rv, kv0, vs, 0, lane);
+    tile_load_lds<D, BC, 1>(p.v + head, head_bytes, kv0, vs, 0, lane);
   };
 
   f32x16 oacc[D / 32];

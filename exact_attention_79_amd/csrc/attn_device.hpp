@@ -204,24 +204,29 @@ __device__ __forceinline__ bf16x8 tile_a_tr(const __bf16* t, const TrCoord& c,
   return cat4(tile_tr4<D>(t, r, col), tile_tr4<D>(t, r + 8, col));
 }
 
-// Global -> LDS copy of a ROWS x D bf16 tile without passing through VGPRs
-// (buffer_load_dwordx4 ... lds): each wave instruction writes 64 consecutive
-// 16-byte LDS chunks (lane L -> chunk base + L), so each lane fetches the
-// global chunk that the swizzle places there.  Rows past the end of the
-// buffer resource land as zeros.  Completion is tracked by vmcnt.
+// Global -> LDS copy of rows row0 .. row0+ROWS-1 of a bf16 [rows][D] head
+// (head_bytes long) without passing through VGPRs (buffer_load_dwordx4 ...
+// lds): each wave instruction writes 64 consecutive 16-byte LDS chunks (lane
+// L -> chunk base + L), so each lane fetches the global chunk that the
+// swizzle places there.  The buffer resource starts at row row0 and is built
+// with scalar instructions, so each lane's offset is the same for every tile
+// and no vector instruction is spent on addresses.  Rows past the end of the
+// head land as zeros.  Completion is tracked by vmcnt.
 template <int D, int ROWS, int NW>
-__device__ __forceinline__ void tile_load_lds(__amdgpu_buffer_rsrc_t rs, int row0,
-                                              __bf16* t, int w, int lane) {
+__device__ __forceinline__ void tile_load_lds(const __bf16* head, uint32_t head_bytes,
+                                              int row0, __bf16* t, int w, int lane) {
   constexpr int CH = D / 8;
   constexpr int ROUNDS = ROWS * CH / (64 * NW);
   static_assert((ROWS * CH) % (64 * NW) == 0, "tile must split evenly over waves");
+  const uint32_t rows = head_bytes / (D * 2), r0 = (uint32_t)row0;
+  const auto rs = make_rsrc(head + (size_t)r0 * D, r0 < rows ? head_bytes - r0 * (D * 2) : 0u);
 #pragma unroll
   for (int i = 0; i < ROUNDS; ++i) {
     const int base = (i * NW + w) * 64;  // first physical chunk of this instruction
     const int pc = base + lane, row = pc / CH, ch = (pc % CH) ^ swz<D>(row);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        rs, (LDS_AS void*)(t + base * 8), 16,
-        (int)((uint32_t)((row0 + row) * D + ch * 8) * 2u), 0, 0, 0);
+        rs, (LDS_AS void*)(t + base * 8), 16, (int)((uint32_t)(row * D + ch * 8) * 2u), 0,
+        0, 0);
   }
 }
 

@@ -70,7 +70,8 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdKParams p) {
   __shared__ __attribute__((aligned(16))) __bf16 sV1[BC * D];
   __shared__ __attribute__((aligned(16))) __bf16 sV2[BC * D];
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, kept scalar
   const int h = lane >> 5, n = lane & 31;
   // With the causal mask the last query blocks are the longest: run them first.
   const TileId id =
@@ -85,8 +86,8 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdKParams p) {
   const size_t kv_off = (size_t)kv_head(bh, p.H, p.Hkv) * N * D;
   const uint32_t head_bytes = (uint32_t)N * D * 2;
   const auto rq = make_rsrc(p.q + head, head_bytes);
-  const auto rk = make_rsrc(p.k + kv_off, head_bytes);
-  const auto rv = make_rsrc(p.v + kv_off, head_bytes);
+  const __bf16* kh = p.k + kv_off;
+  const __bf16* vh = p.v + kv_off;
 
   // Q^T as the B operand of S^T = K Q^T: K-step ks covers d = 16ks..16ks+15,
   // lane holds d = 16ks + 8h .. +7 of its query (zero beyond N).
@@ -183,11 +184,11 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdKParams p) {
   // and the running max for the first tile.  Tiles past the last visible
   // one may be loaded and scored: rows past N read as zeros and their
   // scores are never used.
-  tile_load_lds<D, BC, NW>(rk, t_lo * BC, sK0, w, lane);
-  tile_load_lds<D, BC, NW>(rv, t_lo * BC, sV0, w, lane);
-  tile_load_lds<D, BC, NW>(rk, (t_lo + 1) * BC, sK1, w, lane);
-  tile_load_lds<D, BC, NW>(rv, (t_lo + 1) * BC, sV1, w, lane);
-  tile_load_lds<D, BC, NW>(rk, (t_lo + 2) * BC, sK2, w, lane);
+  tile_load_lds<D, BC, NW>(kh, head_bytes, t_lo * BC, sK0, w, lane);
+  tile_load_lds<D, BC, NW>(vh, head_bytes, t_lo * BC, sV0, w, lane);
+  tile_load_lds<D, BC, NW>(kh, head_bytes, (t_lo + 1) * BC, sK1, w, lane);
+  tile_load_lds<D, BC, NW>(vh, head_bytes, (t_lo + 1) * BC, sV1, w, lane);
+  tile_load_lds<D, BC, NW>(kh, head_bytes, (t_lo + 2) * BC, sK2, w, lane);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   f32x16 scur[BC / 32];
@@ -206,8 +207,8 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdKParams p) {
   // with V_{t+2}.  It leaves S_{t+1} (masked) in scur and its max in m_run.
   auto iteration = [&](int t, const __bf16* Kr, const __bf16* Vr, __bf16* Kf,
                        __bf16* Vf) {
-    tile_load_lds<D, BC, NW>(rk, (t + 3) * BC, Kf, w, lane);
-    tile_load_lds<D, BC, NW>(rv, (t + 2) * BC, Vf, w, lane);
+    tile_load_lds<D, BC, NW>(kh, head_bytes, (t + 3) * BC, Kf, w, lane);
+    tile_load_lds<D, BC, NW>(vh, head_bytes, (t + 2) * BC, Vf, w, lane);
     const float mb = m_run * s2;
 
     // Main block, scheduled by hand in bundles that the compiler may not
@@ -224,9 +225,12 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdKParams p) {
     constexpr int AHEAD = 4;
     constexpr int NV = BC / 2;                 // scores per lane per tile
     constexpr int J0 = 2;                      // first PV bundle with max work
-    constexpr int NCH = NP - J0;               // max slices
-    constexpr int CH = (NV + NCH - 1) / NCH;   // scores per slice
-    static_assert(NCH >= 1 && CH * NCH >= NV, "max slices");
+    // Scores per slice, odd so that each slice is a chain of v_max3 (an
+    // even count starts with a two-operand max whose operands the compiler
+    // must first quiet), and the number of slices that hold any.
+    constexpr int CH = ((NV + (NP - J0) - 1) / (NP - J0)) | 1;
+    constexpr int NCH = (NV + CH - 1) / CH;
+    static_assert(NCH >= 1 && NCH <= NP - J0 && CH * NCH >= NV, "max slices");
     const __bf16* Kn = Kr;
     const __bf16* Vs = Vr;
     auto kread = [&](int i) {
@@ -237,7 +241,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdKParams p) {
 #pragma unroll
     for (int mt = 0; mt < BC / 32; ++mt) snext[mt] = (f32x16){};
     bf16x8 ka[NS], va[NP], pop[BC / 16];
-    float lsum = 0.f;
+    float lsum;
     u32x4 keepw[BC / 32];
     if constexpr (DROP) {
 #pragma unroll
@@ -256,7 +260,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdKParams p) {
       for (int u = 0; u < EPB; ++u) {
         const int e = EPB * i + u, mt = e >> 4, r = e & 15;
         float x = fast_exp2(fmaf(scur[mt][r], s2, -mb));
-        lsum += x;
+        lsum = e == 0 ? x : lsum + x;  // (no 0 + x: an add the compiler must keep)
         if constexpr (DROP) x = dropout_keep(keepw[mt], r, p.drop.thresh) ? x : 0.f;
         pop[e >> 3][e & 7] = (__bf16)x;
       }
@@ -267,7 +271,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdKParams p) {
     for (int j = 0; j < NP; ++j) {
       if (j + AHEAD < NP) va[j + AHEAD] = vread(j + AHEAD);
       oacc[j % (D / 32)] = mfma32(va[j], pop[j / (D / 32)], oacc[j % (D / 32)]);
-      if (j >= J0) {
+      if (j >= J0 && j - J0 < NCH) {
         const int c = j - J0;
         float mx = snext[(c * CH) >> 4][(c * CH) & 15];
 #pragma unroll

@@ -64,24 +64,27 @@ __device__ __forceinline__ int vkey(int row) {
   return (row & ~63) | (((row >> 2) & 7) << 3) | (((row >> 5) & 1) << 2) | (row & 3);
 }
 
-// Direct global -> LDS load of a ROWS x D byte tile by NW waves: wave w's
-// instruction i fills LDS chunks (i*NW + w)*64 + lane, i.e. chunk ch of LDS
-// row r, which holds global chunk ch ^ swz8(r) of source row r (K) or of
-// source row vkey(r) (V, PERMUTE).  Rows past the buffer end read as zero.
+// Direct global -> LDS load of rows row0 .. row0+ROWS-1 of a [rows][D] byte
+// head (head_bytes long) by NW waves: wave w's instruction i fills LDS chunks
+// (i*NW + w)*64 + lane, i.e. chunk ch of LDS row r, which holds global chunk
+// ch ^ swz8(r) of source row r (K) or of source row vkey(r) (V, PERMUTE).
+// The buffer resource starts at row row0 (scalar arithmetic), so each lane's
+// offset is the same for every tile.  Rows past the head's end read as zero.
 template <int D, int ROWS, int NW, bool PERMUTE>
-__device__ __forceinline__ void tile_load_lds8(__amdgpu_buffer_rsrc_t rs, int row0,
-                                               uint8_t* t, int w, int lane) {
+__device__ __forceinline__ void tile_load_lds8(const uint8_t* head, uint32_t head_bytes,
+                                               int row0, uint8_t* t, int w, int lane) {
   constexpr int CH = D / 16;
   constexpr int ROUNDS = ROWS * CH / (64 * NW);
   static_assert((ROWS * CH) % (64 * NW) == 0 && ROWS % 64 == 0, "tile split");
+  const uint32_t rows = head_bytes / D, r0 = (uint32_t)row0;
+  const auto rs = make_rsrc(head + (size_t)r0 * D, r0 < rows ? head_bytes - r0 * D : 0u);
 #pragma unroll
   for (int i = 0; i < ROUNDS; ++i) {
     const int base = (i * NW + w) * 64;
     const int pc = base + lane, r = pc / CH, ch = (pc % CH) ^ swz8<D>(r);
     const int g = PERMUTE ? vkey(r) : r;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS_AS void*)(t + base * 16), 16,
-                                             (int)((uint32_t)((row0 + g) * D + ch * 16)),
-                                             0, 0, 0);
+                                             (int)((uint32_t)(g * D + ch * 16)), 0, 0, 0);
   }
 }
 
@@ -126,7 +129,8 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8_kernel(FwdFp8Params p) {
   __shared__ __attribute__((aligned(16))) uint8_t sV1[BC * D];
   __shared__ __attribute__((aligned(16))) uint8_t sV2[BC * D];
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, kept scalar
   const int h = lane >> 5, n = lane & 31;
   const TileId id =
       tile_order(blockIdx.x, gridDim.x / p.n_qtiles, p.n_qtiles, p.causal, 0);
@@ -140,8 +144,8 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8_kernel(FwdFp8Params p) {
   const size_t kv_off = (size_t)kv_head(bh, p.H, p.Hkv) * N * D;
   const uint32_t head_bytes = (uint32_t)N * D;
   const auto rq = make_rsrc(p.q + head, head_bytes);
-  const auto rk = make_rsrc(p.k + kv_off, head_bytes);
-  const auto rv = make_rsrc(p.v + kv_off, head_bytes);
+  const uint8_t* kh = p.k + kv_off;
+  const uint8_t* vh = p.v + kv_off;
 
   // Q^T as the B operand of S^T = K Q^T: in K-step ks a lane holds the 32
   // bytes d = 64 ks + 32 h .. +31 of its query; K rows are read the same way.
@@ -272,11 +276,11 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8_kernel(FwdFp8Params p) {
     return mx;
   };
 
-  tile_load_lds8<D, BC, NW, false>(rk, t_lo * BC, sK0, w, lane);
-  tile_load_lds8<D, BC, NW, true>(rv, t_lo * BC, sV0, w, lane);
-  tile_load_lds8<D, BC, NW, false>(rk, (t_lo + 1) * BC, sK1, w, lane);
-  tile_load_lds8<D, BC, NW, true>(rv, (t_lo + 1) * BC, sV1, w, lane);
-  tile_load_lds8<D, BC, NW, false>(rk, (t_lo + 2) * BC, sK2, w, lane);
+  tile_load_lds8<D, BC, NW, false>(kh, head_bytes, t_lo * BC, sK0, w, lane);
+  tile_load_lds8<D, BC, NW, true>(vh, head_bytes, t_lo * BC, sV0, w, lane);
+  tile_load_lds8<D, BC, NW, false>(kh, head_bytes, (t_lo + 1) * BC, sK1, w, lane);
+  tile_load_lds8<D, BC, NW, true>(vh, head_bytes, (t_lo + 1) * BC, sV1, w, lane);
+  tile_load_lds8<D, BC, NW, false>(kh, head_bytes, (t_lo + 2) * BC, sK2, w, lane);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   f32x16 scur[2];
@@ -292,8 +296,8 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8_kernel(FwdFp8Params p) {
   // Kf (K_t's slot) with K_{t+3} and Vf (V_{t-1}'s slot) with V_{t+2}.
   auto iteration = [&](int t, const uint8_t* Kr, const uint8_t* Vr, uint8_t* Kf,
                        uint8_t* Vf) {
-    tile_load_lds8<D, BC, NW, false>(rk, (t + 3) * BC, Kf, w, lane);
-    tile_load_lds8<D, BC, NW, true>(rv, (t + 2) * BC, Vf, w, lane);
+    tile_load_lds8<D, BC, NW, false>(kh, head_bytes, (t + 3) * BC, Kf, w, lane);
+    tile_load_lds8<D, BC, NW, true>(vh, head_bytes, (t + 2) * BC, Vf, w, lane);
     // Weights of this tile, times its value descale dv: the row's largest
     // one, 2^y (y = tmx - M + log2 dv), is brought into [128, 256) by 2^-e,
     // e = floor(y) - 7; both factors are folded into the exponent of every
