@@ -164,6 +164,16 @@ __global__ __launch_bounds__(NW * 64, (dkdv_waves_per_simd<D, BQ>())) void bwd_d
     kop[ks] = __builtin_bit_cast(bf16x8, buf_load16(rk, off));
     vop[ks] = __builtin_bit_cast(bf16x8, buf_load16(rv, off));
   }
+  // Without dropout the dP MFMAs start from D_i and take -V, so that they
+  // leave D_i - dP_ij: the subtraction of dsoftmax costs no vector
+  // instruction, and the dS they give is negated, which the scale applied
+  // to dK at the end undoes.  (With dropout, dP is scaled by the keep mask
+  // before D is subtracted.)
+  if constexpr (!DROP) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      vop[ks] = __builtin_bit_cast(bf16x8, __builtin_bit_cast(u32x4, vop[ks]) ^ 0x80008000u);
+  }
   f32x16 dkacc[D / 32], dvacc[D / 32];
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) dkacc[dt] = dvacc[dt] = (f32x16){};
@@ -204,11 +214,29 @@ __global__ __launch_bounds__(NW * 64, (dkdv_waves_per_simd<D, BQ>())) void bwd_d
       ++lj;
     }
   };
-  // S = Q K^T and dP = dO V^T for one tile (queries on M, this wave's keys on N).
-  auto sdp = [&](const __bf16* Qs, const __bf16* Os, f32x16* sacc, f32x16* dpacc) {
+  // Start of the dP accumulator of M-tile mt: zero with dropout, else D of
+  // the query rows this lane holds there (C layout: register 4g + c is row
+  // 32 mt + 8 g + 4 h + c).
+  auto dp_init = [&](const float* Ds, int mt) {
+    f32x16 c = {};
+    if constexpr (!DROP) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 v = *(const f32x4*)&Ds[32 * mt + 8 * g + 4 * h];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) c[4 * g + i] = v[i];
+      }
+    }
+    return c;
+  };
+  // S = Q K^T and dP = dO V^T (without dropout D - dP) for one tile
+  // (queries on M, this wave's keys on N).
+  auto sdp = [&](const __bf16* Qs, const __bf16* Os, const float* Ds, f32x16* sacc,
+                 f32x16* dpacc) {
 #pragma unroll
     for (int mt = 0; mt < BQ / 32; ++mt) {
-      sacc[mt] = dpacc[mt] = (f32x16){};
+      sacc[mt] = (f32x16){};
+      dpacc[mt] = dp_init(Ds, mt);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         sacc[mt] = mfma32(tile_row8<D>(Qs, 32 * mt + n, 2 * ks + h), kop[ks], sacc[mt]);
@@ -224,15 +252,15 @@ __global__ __launch_bounds__(NW * 64, (dkdv_waves_per_simd<D, BQ>())) void bwd_d
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   f32x16 scur[BQ / 32], dpcur[BQ / 32];
-  sdp(sQ0, sO0, scur, dpcur);
+  sdp(sQ0, sO0, sD0, scur, dpcur);
 
   // Iteration for the tile u of the sequence (query tile ct): P, dS of tile
-  // u (slot c: Qc, Oc, Lc, Dc) while S, dP of tile u+1 (slot n: Qn, On) run
-  // on the matrix cores; tile u+2 is fetched into slot f (tile u-1's, fully
-  // consumed).
+  // u (slot c: Qc, Oc, Lc, Dc) while S, dP of tile u+1 (slot n: Qn, On, Dn)
+  // run on the matrix cores; tile u+2 is fetched into slot f (tile u-1's,
+  // fully consumed).
   auto iteration = [&](const __bf16* Qc, const __bf16* Oc, const float* Lc,
-                       const float* Dc, const __bf16* Qn, const __bf16* On, __bf16* Qf,
-                       __bf16* Of, float* Lf, float* Df) {
+                       const float* Dc, const __bf16* Qn, const __bf16* On,
+                       const float* Dn, __bf16* Qf, __bf16* Of, float* Lf, float* Df) {
     load_tile(Qf, Of, Lf, Df);
     const int i0 = ct * BQ;
     const int bhq = bh0 + cj;  // query head of this tile
@@ -287,14 +315,17 @@ __global__ __launch_bounds__(NW * 64, (dkdv_waves_per_simd<D, BQ>())) void bwd_d
     };
     f32x16 snext[BQ / 32], dpnext[BQ / 32];
 #pragma unroll
-    for (int mt = 0; mt < BQ / 32; ++mt) snext[mt] = dpnext[mt] = (f32x16){};
+    for (int mt = 0; mt < BQ / 32; ++mt) {
+      snext[mt] = (f32x16){};
+      dpnext[mt] = dp_init(Dn, mt);
+    }
     bf16x8 aop[NS], top[NP], pop[BQ / 16], dsop[BQ / 16];
     constexpr int GB = 4 / EPB;  // bundles per 4-row group
     constexpr int LDA = 2;  // groups of L, D in flight ahead of their use
 #pragma unroll
     for (int g = 0; g < LDA && g < BQ / 8; ++g) {
       lb[g] = lrow(g);
-      dl[g] = drow(g);
+      if constexpr (DROP) dl[g] = drow(g);
     }
 #pragma unroll
     for (int i = 0; i < AHEAD; ++i) aop[i] = arow(i);
@@ -316,7 +347,10 @@ __global__ __launch_bounds__(NW * 64, (dkdv_waves_per_simd<D, BQ>())) void bwd_d
         pop[e >> 3][e & 7] = (__bf16)pv;
       }
       eb_p[e] = pv;
-      eb_d[e] = dpv - dl[g][r & 3];
+      if constexpr (DROP)
+        eb_d[e] = dpv - dl[g][r & 3];
+      else
+        eb_d[e] = dpv;  // D - dP from the MFMAs
     };
     auto stage_c = [&](int e) { dsop[e >> 3][e & 7] = (__bf16)(eb_p[e] * eb_d[e]); };
     // The last two bundles' elements (from EPB (NS - 2) on) finish in product
@@ -329,7 +363,7 @@ __global__ __launch_bounds__(NW * 64, (dkdv_waves_per_simd<D, BQ>())) void bwd_d
       if (i >= NS - AHEAD) top[i - (NS - AHEAD)] = atr(i - (NS - AHEAD));
       if (i % GB == 0 && i / GB + LDA < BQ / 8) {
         lb[i / GB + LDA] = lrow(i / GB + LDA);
-        dl[i / GB + LDA] = drow(i / GB + LDA);
+        if constexpr (DROP) dl[i / GB + LDA] = drow(i / GB + LDA);
       }
       const int j = i >> 1, mt = j / KS, ks = j % KS;
       if (i & 1)
@@ -379,9 +413,9 @@ __global__ __launch_bounds__(NW * 64, (dkdv_waves_per_simd<D, BQ>())) void bwd_d
 
   const int U = G * (t_hi - t_lo);  // tiles in the sequence
   for (int u = 0; u < U; u += 3) {
-    iteration(sQ0, sO0, sL0, sD0, sQ1, sO1, sQ2, sO2, sL2, sD2);
-    if (u + 1 < U) iteration(sQ1, sO1, sL1, sD1, sQ2, sO2, sQ0, sO0, sL0, sD0);
-    if (u + 2 < U) iteration(sQ2, sO2, sL2, sD2, sQ0, sO0, sQ1, sO1, sL1, sD1);
+    iteration(sQ0, sO0, sL0, sD0, sQ1, sO1, sD1, sQ2, sO2, sL2, sD2);
+    if (u + 1 < U) iteration(sQ1, sO1, sL1, sD1, sQ2, sO2, sD2, sQ0, sO0, sL0, sD0);
+    if (u + 2 < U) iteration(sQ2, sO2, sL2, sD2, sQ0, sO0, sD0, sQ1, sO1, sL1, sD1);
   }
 
   // With the group split, this share's partial sums go to the workspace.
@@ -395,14 +429,15 @@ __global__ __launch_bounds__(NW * 64, (dkdv_waves_per_simd<D, BQ>())) void bwd_d
   if (my_k < N) {
     const size_t row = head + (size_t)my_k * D;
     const float vs = DROP ? p.drop.inv_keep : 1.f;
+    const float ks_ = DROP ? p.scale : -p.scale;  // (dS negated without dropout)
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int d0 = 32 * dt + 8 * g + 4 * h;
         *(f32x4*)(dk_out + row + d0) =
-            (f32x4){dkacc[dt][4 * g] * p.scale, dkacc[dt][4 * g + 1] * p.scale,
-                    dkacc[dt][4 * g + 2] * p.scale, dkacc[dt][4 * g + 3] * p.scale};
+            (f32x4){dkacc[dt][4 * g] * ks_, dkacc[dt][4 * g + 1] * ks_,
+                    dkacc[dt][4 * g + 2] * ks_, dkacc[dt][4 * g + 3] * ks_};
         if constexpr (DROP)
           *(f32x4*)(dv_out + row + d0) =
               (f32x4){dvacc[dt][4 * g] * vs, dvacc[dt][4 * g + 1] * vs,

@@ -303,7 +303,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8_kernel(FwdFp8Params p) {
     // e = floor(y) - 7; both factors are folded into the exponent of every
     // weight, and the MFMA's block scale 2^e puts 2^e back.
     const float s2 = s2t(t), lv = vlog(t);
-    const float y = fmaxf(tmx - m_run + lv, -200.f);
+    const float y = fmaxf(BLOCKS ? tmx - m_run + lv : tmx - m_run, -200.f);
     const int e = max(-123, min(127, (int)floorf(y) - 7));
     const float mbe = m_run + (float)e - lv;
 
@@ -314,12 +314,17 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8_kernel(FwdFp8Params p) {
     constexpr int NS = 2 * KS;
     constexpr int NP = 2 * (D / 32);
     constexpr int WPB = 8 / NS;  // packed words (4 weights) per score bundle
-    constexpr int NCH = NP - 2, CH = (32 + NCH - 1) / NCH;
+    // Row-max slices of an odd size, so that each is a chain of v_max3 (an
+    // even count starts with a two-operand max whose operands the compiler
+    // must first quiet); NCH of the P V bundles after the first two take one.
+    constexpr int CH = ((32 + (NP - 2) - 1) / (NP - 2)) | 1;
+    constexpr int NCH = (32 + CH - 1) / CH;
     static_assert(WPB >= 1 && 8 % NS == 0, "bundle split");
+    static_assert(NCH <= NP - 2, "max slices");
     f32x16 snext[2];
     snext[0] = snext[1] = (f32x16){};
     i32x8 ka[NS], va[D / 32], phi, plo;
-    float lsum = 0.f, part[NCH];
+    float lsum, part[NCH];
     ka[0] = kread(Kr, 0, 0);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -334,7 +339,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8_kernel(FwdFp8Params p) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           x[j] = fast_exp2(fmaf(scur[mt][r0 + j], s2, -mbe));
-          lsum += x[j];
+          lsum = (wd == 0 && j == 0) ? x[j] : lsum + x[j];  // (no 0 + x)
         }
         // (The first convert of each pair writes the low word and keeps the
         // high one, which the second convert then fills: any old value will
@@ -361,7 +366,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8_kernel(FwdFp8Params p) {
       if ((j & 1) && dt + 1 < D / 32) va[dt + 1] = vread(Vr, dt + 1);
       oacc[dt] = mfma_fp8(va[dt], (j & 1) ? plo : phi, oacc[dt],
                           (j & 1) ? e - 4 + 127 : e + 127);
-      if (j >= 2) {
+      if (j >= 2 && j - 2 < NCH) {
         const int c = j - 2;
         float mx = snext[(c * CH) >> 4][(c * CH) & 15];
 #pragma unroll
