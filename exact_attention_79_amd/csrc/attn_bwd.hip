@@ -517,6 +517,16 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdKParams p) {
   const bool q_ok = my_q < N;
   const float Lb = q_ok ? p.lse[(size_t)bh * N + my_q] * kLog2e : 0.f;
   const float Dl = halves_sum(dpart);
+  // Without dropout the dP^T MFMAs start from D_i and take -dO, so that they
+  // leave D_i - dP_ij (as in the dK/dV pass); dS comes out negated and the
+  // dQ epilogue multiplies by -s.
+  if constexpr (!DROP) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      doop[ks] = __builtin_bit_cast(bf16x8, __builtin_bit_cast(u32x4, doop[ks]) ^ 0x80008000u);
+  }
+  const f32x16 dp0 = DROP ? (f32x16){} : (f32x16){Dl, Dl, Dl, Dl, Dl, Dl, Dl, Dl,
+                                                  Dl, Dl, Dl, Dl, Dl, Dl, Dl, Dl};
   // Leave D_i and L_i log2(e) for the dK/dV pass.
   if (q_ok && h == 0) {
     p.delta[(size_t)bh * N + my_q] = Dl;
@@ -547,7 +557,8 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdKParams p) {
   auto sdp = [&](const __bf16* Ks, const __bf16* Vs, f32x16* sacc, f32x16* dpacc) {
 #pragma unroll
     for (int mt = 0; mt < BC / 32; ++mt) {
-      sacc[mt] = dpacc[mt] = (f32x16){};
+      sacc[mt] = (f32x16){};
+      dpacc[mt] = dp0;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         sacc[mt] = mfma32(tile_row8<D>(Ks, 32 * mt + n, 2 * ks + h), qop[ks], sacc[mt]);
@@ -606,7 +617,10 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdKParams p) {
     auto atr = [&](int j) { return tile_a_tr<D>(Kc, trc, j / (D / 32), j % (D / 32)); };
     f32x16 snext[BC / 32], dpnext[BC / 32];
 #pragma unroll
-    for (int mt = 0; mt < BC / 32; ++mt) snext[mt] = dpnext[mt] = (f32x16){};
+    for (int mt = 0; mt < BC / 32; ++mt) {
+      snext[mt] = (f32x16){};
+      dpnext[mt] = dp0;
+    }
     bf16x8 aop[NS], top[NP], dsop[BC / 16];
 #pragma unroll
     for (int i = 0; i < AHEAD; ++i) aop[i] = arow(i);
@@ -627,7 +641,7 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdKParams p) {
         float dpv = dpcur[mt2][r];
         if constexpr (DROP)
           dpv = dropout_keep(keepw[mt2], r, p.drop.thresh) ? dpv * p.drop.inv_keep : 0.f;
-        dsop[e >> 3][e & 7] = (__bf16)(pv * (dpv - Dl));
+        dsop[e >> 3][e & 7] = (__bf16)(pv * (DROP ? dpv - Dl : dpv));
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -654,14 +668,15 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdKParams p) {
 
   if (q_ok) {
     const size_t row = head + (size_t)my_q * D;
+    const float qs = DROP ? p.scale : -p.scale;  // (dS negated without dropout)
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int d0 = 32 * dt + 8 * g + 4 * h;
         *(f32x4*)(p.dq + row + d0) =
-            (f32x4){dqacc[dt][4 * g] * p.scale, dqacc[dt][4 * g + 1] * p.scale,
-                    dqacc[dt][4 * g + 2] * p.scale, dqacc[dt][4 * g + 3] * p.scale};
+            (f32x4){dqacc[dt][4 * g] * qs, dqacc[dt][4 * g + 1] * qs,
+                    dqacc[dt][4 * g + 2] * qs, dqacc[dt][4 * g + 3] * qs};
       }
   }
 }
