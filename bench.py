@@ -459,12 +459,14 @@ def cpu_baseline(attn_synth, seconds_budget=16.0):
                 done_flops += 3.5 * credited_fwd_flops(1, N, d, causal, 0)
             t_total += t_var
             parts.append(f"d{d} {'causal' if causal else 'non-causal'}: {heads} heads")
+    whole = all(p.endswith(f": {B * H} heads") for p in parts)
+    which = "all heads" if whole else "the first heads"
     return {
         "value": done_flops / t_total / 1e12,
         "unit": "TFLOP/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": (f"fp64 oracle forward + backward on the first heads of the B4 H16 "
+        "sample": (f"fp64 oracle forward + backward on {which} of the B4 H16 "
                    f"N2048 workload ({'; '.join(parts)}), {t_total:.1f} s; credited "
                    f"FLOPs as for the GPU"),
     }
