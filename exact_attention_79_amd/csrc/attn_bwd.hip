@@ -473,14 +473,12 @@ template <int D, int NW, int BC, bool DROP>
 __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdKParams p) {
   constexpr int BR = 32 * NW;
   constexpr int KS = D / 16;
-  // Slot s holds K at sKV[s] and V right after it.
-  __shared__ __attribute__((aligned(16))) __bf16 sKV[3][2 * BC * D];
-  __bf16* sK0 = sKV[0];
-  __bf16* sK1 = sKV[1];
-  __bf16* sK2 = sKV[2];
-  __bf16* sV0 = sKV[0] + BC * D;
-  __bf16* sV1 = sKV[1] + BC * D;
-  __bf16* sV2 = sKV[2] + BC * D;
+  __shared__ __attribute__((aligned(16))) __bf16 sK0[BC * D];
+  __shared__ __attribute__((aligned(16))) __bf16 sK1[BC * D];
+  __shared__ __attribute__((aligned(16))) __bf16 sK2[BC * D];
+  __shared__ __attribute__((aligned(16))) __bf16 sV0[BC * D];
+  __shared__ __attribute__((aligned(16))) __bf16 sV1[BC * D];
+  __shared__ __attribute__((aligned(16))) __bf16 sV2[BC * D];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, kept scalar
