@@ -174,7 +174,9 @@ def build_step(ea, torch, attn_synth):
             # leaves D and L log2(e) in the workspace for the dK/dV pass.
             launches.append(Launch(f"attn_bwd_dq {tag}", f"bwd_dq_kernel<d{d}>", dq,
                                    0.2 * bwd, 0.6 * bwd, PEAK_BF16_TFLOPS))
-            launches.append(Launch(f"attn_bwd_dkdv {tag}", f"bwd_dkdv_kernel<d{d}>", dkdv,
+            # (At d = 128 the dK/dV pass is the paired-wave kernel.)
+            dkdv_name = "bwd_dkdv_pair_kernel" if d == 128 else "bwd_dkdv_kernel"
+            launches.append(Launch(f"attn_bwd_dkdv {tag}", f"{dkdv_name}<d{d}>", dkdv,
                                    0.8 * bwd, 0.8 * bwd, PEAK_BF16_TFLOPS))
     if INCLUDE_FP8:
         d = 128

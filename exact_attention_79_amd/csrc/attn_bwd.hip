@@ -14,10 +14,11 @@
 //     VGPRs and is written once.  Each lane owns one query row, so it forms
 //     D_i = rowsum(dO_i * O_i) itself (one read of O_i) and also leaves D_i
 //     and L_i log2(e) in the workspace for the second launch;
-//  2. bwd_dkdv_kernel: one workgroup per K/V block (the page's column-block
-//     partition of the backward), K_j and V_j resident in VGPRs, looping over
-//     the query blocks that can see them; dK_j and dV_j accumulate in VGPRs
-//     and are written once.
+//  2. bwd_dkdv_kernel (bwd_dkdv_pair_kernel at d = 128 without dropout): one
+//     workgroup per K/V block (the page's column-block partition of the
+//     backward), K_j and V_j resident in VGPRs, looping over the query blocks
+//     that can see them; dK_j and dV_j accumulate in VGPRs and are written
+//     once.
 // bwd_delta_kernel writes the same two workspace arrays on its own (for
 // callers that run the dK/dV pass without the dQ pass).
 // Splitting dQ into its own pass recomputes S and dP there (two extra
@@ -449,6 +450,359 @@ __global__ __launch_bounds__(NW * 64, (dkdv_waves_per_simd<D, BQ>())) void bwd_d
   }
 }
 
+// ---------------------------------------------------------- dK, dV (paired)
+// d = 128 without dropout.  The kernel above needs about 340 registers per
+// wave at d = 128, so it runs one wave per SIMD, and that wave mostly
+// alternates between matrix and vector work.  Here the four products of a
+// key slice are split over two waves that own the same 32 keys and share a
+// SIMD (waves w and w + NPAIR):
+//  * the P wave computes S = Q K^T, P = exp2(s log2(e) S - L log2(e)) and
+//    dV^T += dO^T P, and hands P (fp32) to its partner through LDS;
+//  * the dS wave computes D - dP = D - dO V^T (the MFMAs start from D and
+//    take -V, as above), dS = P (dP - D) (negated) and dK^T += Q^T dS, one
+//    query tile behind the P wave.
+// Each wave fits in 256 registers, so a SIMD holds both and overlaps one
+// wave's vector work with the other's MFMAs.  Every value is formed as in
+// the single-wave kernel, and each accumulator takes its products in the same
+// order, so the two kernels give the same results.
+//
+// Query tiles of 32 rows stream through four LDS slots (tile s in slot
+// s % 4): at step s the P wave reads tile s+1 (the S products of the next
+// tile) and tile s (dV), the dS wave tile s (dP) and tile s-1 (dK), and
+// tile s+2 is fetched.  P of tile s goes to exchange buffer s % 2.  One
+// barrier ends each step.
+template <int D, int NPAIR>
+__global__ __launch_bounds__(2 * NPAIR * 64, 2) void bwd_dkdv_pair_kernel(BwdKParams p) {
+  constexpr int BQ = 32;               // query rows per step
+  constexpr int NWV = 2 * NPAIR;       // waves
+  constexpr int BKV = 32 * NPAIR;      // keys per workgroup
+  constexpr int KS = D / 16;           // K-steps of S and dP
+  constexpr int DT = D / 32;           // d-tiles of dK and dV
+  constexpr int LDROWS = 64;           // L and D are staged one dword per lane
+  constexpr int PSZ = NPAIR * 16 * 64;  // floats of one P exchange buffer
+  constexpr int AHEAD = 3;             // operand reads ahead of their MFMA
+  __shared__ __attribute__((aligned(16))) __bf16 sQ0[BQ * D];
+  __shared__ __attribute__((aligned(16))) __bf16 sQ1[BQ * D];
+  __shared__ __attribute__((aligned(16))) __bf16 sQ2[BQ * D];
+  __shared__ __attribute__((aligned(16))) __bf16 sQ3[BQ * D];
+  __shared__ __attribute__((aligned(16))) __bf16 sQ4[BQ * D];
+  __shared__ __attribute__((aligned(16))) __bf16 sQ5[BQ * D];
+  __shared__ __attribute__((aligned(16))) __bf16 sO0[BQ * D];
+  __shared__ __attribute__((aligned(16))) __bf16 sO1[BQ * D];
+  __shared__ __attribute__((aligned(16))) __bf16 sO2[BQ * D];
+  __shared__ __attribute__((aligned(16))) __bf16 sO3[BQ * D];
+  __shared__ __attribute__((aligned(16))) __bf16 sO4[BQ * D];
+  __shared__ __attribute__((aligned(16))) __bf16 sO5[BQ * D];
+  __shared__ __attribute__((aligned(16))) float sL0[LDROWS], sL1[LDROWS], sL2[LDROWS], sL3[LDROWS],
+      sL4[LDROWS], sL5[LDROWS];
+  __shared__ __attribute__((aligned(16))) float sD0[LDROWS], sD1[LDROWS], sD2[LDROWS], sD3[LDROWS],
+      sD4[LDROWS], sD5[LDROWS];
+  __shared__ __attribute__((aligned(16))) float sP0[PSZ];
+  __shared__ __attribute__((aligned(16))) float sP1[PSZ];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, kept scalar
+  const bool pwave = w < NPAIR;
+  const int pr = pwave ? w : w - NPAIR;  // key slice of this wave's pair
+  const int h = lane >> 5, n = lane & 31;
+  const TileId id =
+      tile_order(blockIdx.x, gridDim.x / p.n_tiles, p.n_tiles, p.causal, causal_group<D>());
+  const int bkv = id.bh / p.split;  // key/value head (b * Hkv + hk)
+  const int share = id.bh % p.split;
+  const int kt = id.rank;
+  const int N = p.N, W = p.window;
+  const int G = p.H / p.Hkv / p.split;  // query heads this workgroup walks
+  const int bh0 = (bkv / p.Hkv) * p.H + (bkv % p.Hkv) * (p.H / p.Hkv) + share * G;
+  const int k0 = kt * BKV;
+  const int kw0 = k0 + 32 * pr;
+  const int my_k = kw0 + n;
+  const size_t head = (size_t)bkv * N * D;
+  const uint32_t head_bytes = (uint32_t)N * D * 2;
+
+  // Resident B operand (lane = key, 8 consecutive d per K-step): K^T for
+  // the P wave, -V^T for the dS wave.
+  bf16x8 bop[KS];
+  {
+    const auto r = make_rsrc((pwave ? p.k : p.v) + head, head_bytes);
+    const uint32_t sign = pwave ? 0u : 0x80008000u;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      bop[ks] = __builtin_bit_cast(
+          bf16x8, buf_load16(r, (uint32_t)(my_k * D + 16 * ks + 8 * h) * 2u) ^ sign);
+  }
+  f32x16 acc[DT];  // dV^T (P wave) or -dK^T / s (dS wave)
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) acc[dt] = (f32x16){};
+
+  // Queries that can see any key of this block, and those that see my_k.
+  const int k_last = min(k0 + BKV, N) - 1;
+  int q_lo = p.causal ? k0 : 0, q_hi = N;
+  int qmin = p.causal ? my_k : INT_MIN, qmax = INT_MAX;
+  if (W > 0) {
+    q_lo = max(q_lo, k0 - W + 1);
+    q_hi = min(q_hi, k_last + W);
+    if (!p.causal) qmin = my_k - W + 1;
+    qmax = my_k + W - 1;
+  }
+  const int t_lo = q_lo / BQ, t_hi = (q_hi + BQ - 1) / BQ;
+  const int U = G * (t_hi - t_lo);  // tiles in the sequence (query head, tile)
+
+  const float s2 = p.scale * kLog2e;
+  const TrCoord trc(lane);
+  // Byte offsets of this lane's operand reads inside a tile: row reads
+  // (K-step ks) and transposing reads (d-tile dt, rows +0 / +8; the swizzle
+  // of a transposing read does not depend on its K-step, which adds 16 rows).
+  // They are re-hidden from the optimizer at every step, so that each read
+  // is formed in its own block as offset + constant (slot and array) and the
+  // constant folds into the instruction instead of one hoisted address
+  // register per slot and read.
+  uint32_t roff[KS], toff[2 * DT];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) roff[ks] = (uint32_t)tile_off<D>(n, 2 * ks + h) * 2u;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      const int r = trc.row + 8 * x, col = 32 * dt + trc.col;
+      toff[2 * dt + x] = (uint32_t)(tile_off<D>(r, col >> 3) + (col & 7)) * 2u;
+    }
+  uint32_t poff = (uint32_t)((pr * 4 * 64 + lane) * 16);  // P exchange, this lane's first chunk
+  uint32_t lhoff = (uint32_t)(16 * h);                    // L, D rows 4h .. 4h+3 of group 0
+  auto rrow = [&](const __bf16* t, int ks) {
+    return *(const bf16x8*)((const char*)t + roff[ks]);
+  };
+  auto rtr = [&](const __bf16* t, int j) {  // A operand of K-step j / DT, d-tile j % DT
+    const int kk = j / DT, dt = j % DT;
+    const char* b = (const char*)t + 16 * kk * D * 2;
+    return cat4(lds_read_tr16(b + toff[2 * dt]), lds_read_tr16(b + toff[2 * dt + 1]));
+  };
+  auto rvec4 = [&](const float* t, int g) {  // rows 8g + 4h .. +3
+    return *(const f32x4*)((const char*)t + lhoff + 32 * g);
+  };
+
+  // Load cursor (lj, lt), two tiles ahead of the step; past the last head it
+  // keeps reading the last head's rows (in bounds, never used).
+  int lj = 0, lt = t_lo, ct = t_lo;
+  auto load_tile = [&](__bf16* Qf, __bf16* Of, float* Lf, float* Df) {
+    const int bhq = bh0 + min(lj, G - 1);
+    const size_t qhead = (size_t)bhq * N * D;
+    tile_load_lds<D, BQ, NWV>(p.q + qhead, head_bytes, lt * BQ, Qf, w, lane);
+    tile_load_lds<D, BQ, NWV>(p.dout + qhead, head_bytes, lt * BQ, Of, w, lane);
+    if (w == 0)
+      vec_load_lds<LDROWS>(make_rsrc(p.lse2 + (size_t)bhq * N, (uint32_t)N * 4), lt * BQ,
+                           Lf, lane);
+    if (w == 1)
+      vec_load_lds<LDROWS>(make_rsrc(p.delta + (size_t)bhq * N, (uint32_t)N * 4), lt * BQ,
+                           Df, lane);
+    if (++lt == t_hi) {
+      lt = t_lo;
+      ++lj;
+    }
+  };
+
+  // Prologue: tiles 0, 1 and 2.  The dS wave's first step has no tile
+  // before it; it runs on zeros (P buffer 1, slot 5 and its running D - dP),
+  // so that its dK products add exactly nothing.
+  load_tile(sQ0, sO0, sL0, sD0);
+  load_tile(sQ1, sO1, sL1, sD1);
+  load_tile(sQ2, sO2, sL2, sD2);
+  for (int i = tid; i < BQ * D / 8; i += NWV * 64) ((u32x4*)sQ5)[i] = (u32x4){};
+  for (int i = tid; i < PSZ / 4; i += NWV * 64) ((f32x4*)sP1)[i] = (f32x4){};
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  // P wave: S of the current tile (raw, unmasked); dS wave: D - dP of the
+  // tile before the current one.
+  f32x16 cur = {};
+  if (pwave) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      cur = mfma32(tile_row8<D>(sQ0, n, 2 * ks + h), bop[ks], cur);
+  }
+
+  // Step s: slots c (tile s), nx (tile s+1), pv (tile s-1), f (filled with
+  // tile s+3; tile s+2 is in flight); P of tile s is written to Pw, P of
+  // tile s-1 read from Pr.
+  // The two roles run separate loops (so that neither's registers are
+  // shuffled at joins with the other's code); each step ends with the one
+  // barrier, which the hardware counts per workgroup, not per instruction.
+  auto begin_step = [&](__bf16* Qf, __bf16* Of, float* Lf, float* Df) {
+    load_tile(Qf, Of, Lf, Df);
+#pragma unroll
+    for (int i = 0; i < KS; ++i) asm volatile("" : "+v"(roff[i]));
+#pragma unroll
+    for (int i = 0; i < 2 * DT; ++i) asm volatile("" : "+v"(toff[i]));
+    asm volatile("" : "+v"(poff), "+v"(lhoff));
+  };
+  // Tile s+2 has landed for every wave (this step's loads stay in flight:
+  // two, plus L or D for waves 0 and 1), P of tile s is visible to the dS
+  // waves, and the slot of tile s-2 may be refilled next step.
+  auto end_step = [&]() {
+    constexpr int kLgkm0 = 0x0F00;  // (lgkmcnt field cleared: wait for LDS ops)
+    if (w < 2)
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(3) & ~kLgkm0);
+    else
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(2) & ~kLgkm0);
+    __builtin_amdgcn_s_barrier();
+  };
+  // P wave, step s < U: mask S of tile s, P = exp2(S s2 - L log2 e) (to Pw
+  // and as the bf16 B operand), S of tile s+1, dV^T += dO^T P.
+  auto pstep = [&](const __bf16* Oc, const float* Lc, const __bf16* Qnx, __bf16* Qf,
+                   __bf16* Of, float* Lf, float* Df, float* Pw) {
+    begin_step(Qf, Of, Lf, Df);
+    const int i0 = ct * BQ;  // first query of tile s
+    if (++ct == t_hi) ct = t_lo;
+    bool need_mask = false;
+    if (p.causal) need_mask |= i0 < kw0 + 31;
+    if (W > 0) {
+      need_mask |= (i0 + BQ - 1) - kw0 >= W;
+      if (!p.causal) need_mask |= (kw0 + 31) - i0 >= W;
+    }
+    if (need_mask) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int q = i0 + 8 * (r >> 2) + 4 * h + (r & 3);
+        cur[r] = (q < qmin || q > qmax) ? -__builtin_inff() : cur[r];
+      }
+    }
+    // L log2(e) of the rows this lane holds: register 4g + c is row 8g + 4h + c.
+    f32x4 lb[4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) lb[g] = rvec4(Lc, g);
+    f32x16 snext = {};
+    bf16x8 aop[KS], top[2 * DT], pop[2];
+    float pv[16];
+#pragma unroll
+    for (int i = 0; i < AHEAD; ++i) aop[i] = rrow(Qnx, i);
+    __builtin_amdgcn_sched_barrier(0);
+    // S of tile s+1, with two elements of P of tile s per bundle.
+#pragma unroll
+    for (int i = 0; i < KS; ++i) {
+      if (i + AHEAD < KS) aop[i + AHEAD] = rrow(Qnx, i + AHEAD);
+      if (i >= KS - AHEAD) top[i - (KS - AHEAD)] = rtr(Oc, i - (KS - AHEAD));
+      snext = mfma32(aop[i], bop[i], snext);
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int e = 2 * i + u;
+        const float x = fast_exp2(fmaf(cur[e], s2, -lb[e >> 2][e & 3]));
+        pv[e] = x;
+        pop[e >> 3][e & 7] = (__bf16)x;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      *(f32x4*)((char*)Pw + poff + 1024 * k) =
+          (f32x4){pv[4 * k], pv[4 * k + 1], pv[4 * k + 2], pv[4 * k + 3]};
+    // dV^T += dO^T P (K-step j / DT over the tile's rows, d-tile j % DT).
+#pragma unroll
+    for (int j = 0; j < 2 * DT; ++j) {
+      if (j + AHEAD < 2 * DT) top[j + AHEAD] = rtr(Oc, j + AHEAD);
+      acc[j % DT] = mfma32(top[j], pop[j / DT], acc[j % DT]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    cur = snext;
+    end_step();
+  };
+  // dS wave, step s <= U: D - dP of tile s (from D, with -V), dS = P (dP - D)
+  // of tile s-1 (negated; P from Pr), dK^T += Q^T dS of tile s-1.
+  auto dstep = [&](const __bf16* Oc, const float* Dc, const __bf16* Qpv, __bf16* Qf,
+                   __bf16* Of, float* Lf, float* Df, const float* Pr) {
+    begin_step(Qf, Of, Lf, Df);
+    f32x16 dpn;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const f32x4 v = rvec4(Dc, g);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) dpn[4 * g + c] = v[c];
+    }
+    f32x4 pp[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) pp[k] = *(const f32x4*)((const char*)Pr + poff + 1024 * k);
+    bf16x8 aop[KS], top[2 * DT], dsop[2];
+#pragma unroll
+    for (int i = 0; i < AHEAD; ++i) aop[i] = rrow(Oc, i);
+    __builtin_amdgcn_sched_barrier(0);
+    // D - dP of tile s, with two elements of dS of tile s-1 per bundle.
+#pragma unroll
+    for (int i = 0; i < KS; ++i) {
+      if (i + AHEAD < KS) aop[i + AHEAD] = rrow(Oc, i + AHEAD);
+      if (i >= KS - AHEAD) top[i - (KS - AHEAD)] = rtr(Qpv, i - (KS - AHEAD));
+      dpn = mfma32(aop[i], bop[i], dpn);
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int e = 2 * i + u;
+        dsop[e >> 3][e & 7] = (__bf16)(pp[e >> 2][e & 3] * cur[e]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // dK^T += Q^T dS of tile s-1.
+#pragma unroll
+    for (int j = 0; j < 2 * DT; ++j) {
+      if (j + AHEAD < 2 * DT) top[j + AHEAD] = rtr(Qpv, j + AHEAD);
+      acc[j % DT] = mfma32(top[j], dsop[j / DT], acc[j % DT]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    cur = dpn;
+    end_step();
+  };
+
+  // Step s uses slot s % 6 as c, (s+1) % 6 as nx, (s+5) % 6 as pv and fills
+  // (s+3) % 6; P buffer s % 2 is written and (s+1) % 2 read.  The P wave
+  // works on tiles 0 .. U-1 and then joins the last barrier; the dS wave on
+  // tiles -1 .. U-1 (its dP products of tile U are never used).
+  if (pwave) {
+    int s = 0;
+    for (; s + 6 <= U; s += 6) {
+      pstep(sO0, sL0, sQ1, sQ3, sO3, sL3, sD3, sP0);
+      pstep(sO1, sL1, sQ2, sQ4, sO4, sL4, sD4, sP1);
+      pstep(sO2, sL2, sQ3, sQ5, sO5, sL5, sD5, sP0);
+      pstep(sO3, sL3, sQ4, sQ0, sO0, sL0, sD0, sP1);
+      pstep(sO4, sL4, sQ5, sQ1, sO1, sL1, sD1, sP0);
+      pstep(sO5, sL5, sQ0, sQ2, sO2, sL2, sD2, sP1);
+    }
+    if (s < U) pstep(sO0, sL0, sQ1, sQ3, sO3, sL3, sD3, sP0);
+    if (s + 1 < U) pstep(sO1, sL1, sQ2, sQ4, sO4, sL4, sD4, sP1);
+    if (s + 2 < U) pstep(sO2, sL2, sQ3, sQ5, sO5, sL5, sD5, sP0);
+    if (s + 3 < U) pstep(sO3, sL3, sQ4, sQ0, sO0, sL0, sD0, sP1);
+    if (s + 4 < U) pstep(sO4, sL4, sQ5, sQ1, sO1, sL1, sD1, sP0);
+    end_step();
+  } else {
+    int s = 0;
+    for (; s + 6 <= U + 1; s += 6) {
+      dstep(sO0, sD0, sQ5, sQ3, sO3, sL3, sD3, sP1);
+      dstep(sO1, sD1, sQ0, sQ4, sO4, sL4, sD4, sP0);
+      dstep(sO2, sD2, sQ1, sQ5, sO5, sL5, sD5, sP1);
+      dstep(sO3, sD3, sQ2, sQ0, sO0, sL0, sD0, sP0);
+      dstep(sO4, sD4, sQ3, sQ1, sO1, sL1, sD1, sP1);
+      dstep(sO5, sD5, sQ4, sQ2, sO2, sL2, sD2, sP0);
+    }
+    if (s <= U) dstep(sO0, sD0, sQ5, sQ3, sO3, sL3, sD3, sP1);
+    if (s + 1 <= U) dstep(sO1, sD1, sQ0, sQ4, sO4, sL4, sD4, sP0);
+    if (s + 2 <= U) dstep(sO2, sD2, sQ1, sQ5, sO5, sL5, sD5, sP1);
+    if (s + 3 <= U) dstep(sO3, sD3, sQ2, sQ0, sO0, sL0, sD0, sP0);
+    if (s + 4 <= U) dstep(sO4, sD4, sQ3, sQ1, sO1, sL1, sD1, sP1);
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // no load may land after the workgroup ends
+
+  // With the group split, this share's partial sums go to the workspace.
+  float* out = pwave ? p.dv : p.dk;
+  if (p.split > 1) {
+    const size_t part = (size_t)(gridDim.x / p.n_tiles / p.split) * N * D;
+    out = (pwave ? p.dv_part : p.dk_part) + share * part;
+  }
+  if (my_k < N) {
+    const size_t row = head + (size_t)my_k * D;
+    const float sc = pwave ? 1.f : -p.scale;  // (dS negated)
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        *(f32x4*)(out + row + 32 * dt + 8 * g + 4 * h) =
+            (f32x4){acc[dt][4 * g] * sc, acc[dt][4 * g + 1] * sc, acc[dt][4 * g + 2] * sc,
+                    acc[dt][4 * g + 3] * sc};
+  }
+}
+
 // out = sum over `split` partial arrays of n4 float4 each (stride n4 apart),
 // in share order, so the result does not depend on scheduling.
 __global__ __launch_bounds__(256) void bwd_share_sum_kernel(const f32x4* part, f32x4* out,
@@ -743,8 +1097,8 @@ hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL((bwd_dkdv_kernel<128, kBwdWaves, kDropQTile, true>), grid, block, 0,
                        stream, p);
   else if (a.d == 128)
-    hipLaunchKernelGGL((bwd_dkdv_kernel<128, kBwdWaves, dkdv_qtile<128>(), false>), grid,
-                       block, 0, stream, p);
+    hipLaunchKernelGGL((bwd_dkdv_pair_kernel<128, kBwdWaves>), grid, dim3(2 * 64 * kBwdWaves),
+                       0, stream, p);
   else if (drop)
     hipLaunchKernelGGL((bwd_dkdv_kernel<64, kBwdWaves, kDropQTile, true>), grid, block, 0,
                        stream, p);
