@@ -55,6 +55,22 @@ def test_ragged_shapes_and_masks(ea, N, d, causal, window):
         assert_close(g, r, BF16_MAX, BF16_MEAN, name)
 
 
+# At d = 128 the dK/dV pass walks 32-row query tiles in a loop unrolled six
+# steps deep, with separate tails for its two wave roles.  Non-causal, every
+# key block walks N / 32 tiles: N = 32 .. 384 covers walks of 1 to 12 tiles
+# (every remainder of the unrolled loop, twice); causal at N = 416 the four
+# key blocks walk 13, 9, 5 and 1.
+@pytest.mark.parametrize("N,causal", [(32 * u, False) for u in range(1, 13)] + [(416, True)])
+def test_dkdv_tile_walk_lengths(ea, N, causal):
+    d = 128
+    log(f"case: bwd B1 H2 N{N} d{d} causal={causal} (dK/dV walk lengths)")
+    dev, ref = bf16_case(470 + N, 1, 2, N, d, with_dout=True)
+    got = fwd_bwd(ea, dev, causal, 0)
+    want = oracle.bwd(ref["q"], ref["k"], ref["v"], ref["do"], 1 / math.sqrt(d), causal, 0)[:3]
+    for name, g, r in zip(("dQ", "dK", "dV"), got, want):
+        assert_close(g, r, BF16_MAX, BF16_MEAN, name)
+
+
 def test_backward_full_size_two_heads(ea):
     """B=4, H=16, N=4096, d=128 causal; heads (0,0) and (3,15) compared in full."""
     B, H, N, d = 4, 16, 4096, 128

@@ -40,7 +40,10 @@ def np64(t):
     return t.float().cpu().numpy().astype(np.float64)
 
 
-CASES = [(2, 8, 2, 333, 128), (1, 4, 1, 257, 64), (2, 6, 3, 100, 64), (1, 4, 4, 65, 128)]
+# (The last two: d = 128 with short walks of 32-row query tiles per key
+# block, 3 and 5 tiles per query head; such small grids split the group.)
+CASES = [(2, 8, 2, 333, 128), (1, 4, 1, 257, 64), (2, 6, 3, 100, 64), (1, 4, 4, 65, 128),
+         (1, 4, 2, 96, 128), (1, 6, 2, 160, 128)]
 MASKS = [(False, 0), (True, 0), (True, 40), (False, 30)]
 
 
