@@ -195,6 +195,8 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdKParams p) {
   scores(sK0, scur);
   mask_tile(t_lo, scur);
   update_max(tile_max(scur));
+  // Every wave has read K_0 before the first iteration refills its slot.
+  __syncthreads();
 
   // vmcnt <= the loads issued by one iteration (lgkmcnt and expcnt free).
   constexpr int kLoadsPerIter = 2 * (BC * D / 8) / (64 * NW);

@@ -287,6 +287,8 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8_kernel(FwdFp8Params p) {
   scores(sK0, scur);
   mask_tile(t_lo, scur);
   float tmx = update_max(tile_max(scur), s2t(t_lo));
+  // Every wave has read K_0 before the first iteration refills its slot.
+  __syncthreads();
 
   constexpr int kLoadsPerIter = 2 * (BC * D / 16) / (64 * NW);
   constexpr int kWaitOlderLoads = waitcnt_vm(kLoadsPerIter);
