@@ -34,6 +34,9 @@
 //  * Workgroups are renumbered per XCD (whole heads per XCD, sharing K/V in
 //    that XCD's L2) and, with the causal mask, the longest query blocks run
 //    first.
+// fwd_bf16_kernel serves d = 64 and dropout; d = 128 without dropout runs
+// fwd_pp_kernel below, which keeps this mapping but separates each wave's
+// matrix and vector work into alternating half-steps (ping-pong).
 #include "attn_device.hpp"
 #include "attn_kernels.hpp"
 
@@ -339,8 +342,287 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdKParams p) {
   }
 }
 
-template <int D, int NW, int BC, bool DROP>
-static hipError_t launch_fwd_cfg(const FwdArgs& a, hipStream_t stream) {
+// ------------------------------------------------------------- ping-pong
+// d = 128 without dropout: the same computation in workgroups of 8 waves
+// (256 queries), split into two groups (waves 0-3 and 4-7; the hardware
+// places waves w and w + 4 on the same SIMD).  Each wave alternates a matrix
+// half-step M(u) -- S of tile u+1 and O~ += P~_u V_u, 16 MFMAs and their
+// operand reads -- with a vector half-step V(u) -- mask, row max, rescale and
+// the exponentials of tile u+1 -- and the second group runs one half-step
+// behind the first, so that on every SIMD one wave feeds the matrix cores
+// while the other uses the VALU.  A barrier ends every half-step.  K_j and
+// V_j sit in slot j % 3 of their rings; at every even half-step 2u the waves
+// fetch K_{u+3} and V_{u+2}, and every half-step ends by waiting for the
+// fetches issued two half-steps earlier, so that the operands of a wave's
+// next M are in LDS during its V and the first of them are read there.
+// Under the causal mask the first group (the workgroup's first 128 queries)
+// stops computing after the last tile its queries see and from then on only
+// fetches its share of the tiles and joins the barriers.
+template <int D, int NG>
+__global__ __launch_bounds__(2 * NG * 64, 2) void fwd_pp_kernel(FwdKParams p) {
+  constexpr int BC = 32;               // keys per tile
+  constexpr int NWV = 2 * NG;          // waves
+  constexpr int BR = 32 * NWV;         // queries per workgroup
+  constexpr int KS = D / 16, DT = D / 32;
+  constexpr int AHEAD = 3;
+  __shared__ __attribute__((aligned(16))) __bf16 sK0[BC * D];
+  __shared__ __attribute__((aligned(16))) __bf16 sK1[BC * D];
+  __shared__ __attribute__((aligned(16))) __bf16 sK2[BC * D];
+  __shared__ __attribute__((aligned(16))) __bf16 sV0[BC * D];
+  __shared__ __attribute__((aligned(16))) __bf16 sV1[BC * D];
+  __shared__ __attribute__((aligned(16))) __bf16 sV2[BC * D];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, kept scalar
+  const bool lead = w < NG;  // first group: M(u) at half-step 2u
+  const int h = lane >> 5, n = lane & 31;
+  const TileId id =
+      tile_order(blockIdx.x, gridDim.x / p.n_qtiles, p.n_qtiles, p.causal, causal_group<D>());
+  const int bh = id.bh;
+  const int qt = p.causal ? p.n_qtiles - 1 - id.rank : id.rank;
+  const int N = p.N;
+  const int q0 = qt * BR;
+  const int wq0 = q0 + 32 * w;
+  const int my_q = wq0 + n;
+  const size_t head = (size_t)bh * N * D;
+  const size_t kv_off = (size_t)kv_head(bh, p.H, p.Hkv) * N * D;
+  const uint32_t head_bytes = (uint32_t)N * D * 2;
+  const auto rq = make_rsrc(p.q + head, head_bytes);
+  const __bf16* kh = p.k + kv_off;
+  const __bf16* vh = p.v + kv_off;
+
+  bf16x8 qop[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+    qop[ks] = __builtin_bit_cast(
+        bf16x8, buf_load16(rq, (uint32_t)(my_q * D + 16 * ks + 8 * h) * 2u));
+
+  const int q_last = min(q0 + BR, N) - 1;
+  int kv_lo = 0, kv_hi = N;
+  if (p.causal) kv_hi = min(kv_hi, q_last + 1);
+  if (p.window > 0) {
+    kv_lo = max(0, q0 - p.window + 1);
+    if (!p.causal) kv_hi = min(kv_hi, q_last + p.window);
+  }
+  const int t_lo = kv_lo / BC, t_hi = (kv_hi + BC - 1) / BC;
+  const int T = t_hi - t_lo;
+
+  f32x16 oacc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) oacc[dt] = (f32x16){};
+  float m_run = kMaxInit, l_run = 0.f;
+  const float s2 = p.scale * kLog2e;
+  const float tau = 8.0f / s2;
+  const TrCoord trc(lane);
+
+  int hi_key = N - 1, lo_key = 0;
+  if (p.causal) hi_key = min(hi_key, my_q);
+  if (p.window > 0) {
+    lo_key = my_q - p.window + 1;
+    if (!p.causal) hi_key = min(hi_key, my_q + p.window - 1);
+  }
+  // Masks tile t's scores when the tile straddles a boundary of this wave.
+  auto mask_tile = [&](int t, f32x16& sacc) {
+    const int kv0 = t * BC;
+    bool need = kv0 + BC > N;
+    if (p.causal) need |= kv0 + BC - 1 > wq0;
+    if (p.window > 0) {
+      need |= wq0 + 31 - kv0 >= p.window;
+      if (!p.causal) need |= kv0 + BC - 1 - wq0 >= p.window;
+    }
+    if (!need) return;
+    const int lim_hi = hi_key - kv0 - 4 * h, lim_lo = lo_key - kv0 - 4 * h;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int c = 8 * (r >> 2) + (r & 3);
+      sacc[r] = (c > lim_hi || c < lim_lo) ? -__builtin_inff() : sacc[r];
+    }
+  };
+
+  // Byte offsets of this lane's operand reads in a tile (K rows per K-step;
+  // V transposing reads per d-tile and row half), re-hidden from the
+  // optimizer at every half-step so that slot constants fold into the reads.
+  uint32_t roff[KS], toff[2 * DT];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) roff[ks] = (uint32_t)tile_off<D>(n, 2 * ks + h) * 2u;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      const int r = trc.row + 8 * x, col = 32 * dt + trc.col;
+      toff[2 * dt + x] = (uint32_t)(tile_off<D>(r, col >> 3) + (col & 7)) * 2u;
+    }
+  auto hide = [&]() {
+#pragma unroll
+    for (int i = 0; i < KS; ++i) asm volatile("" : "+v"(roff[i]));
+#pragma unroll
+    for (int i = 0; i < 2 * DT; ++i) asm volatile("" : "+v"(toff[i]));
+  };
+  auto rrow = [&](const __bf16* t, int ks) {
+    return *(const bf16x8*)((const char*)t + roff[ks]);
+  };
+  auto rtr = [&](const __bf16* t, int j) {  // K-step j / DT, d-tile j % DT
+    const char* b = (const char*)t + 16 * (j / DT) * D * 2;
+    return cat4(lds_read_tr16(b + toff[2 * (j % DT)]), lds_read_tr16(b + toff[2 * (j % DT) + 1]));
+  };
+
+  f32x16 snx;  // raw scores of the tile whose probabilities come next
+  bf16x8 pop[2];
+  // Row max of snx (masked), running max moved past it, O~ and l rescaled,
+  // then the probabilities of snx into pop and their sum into l.
+  auto softmax_step = [&]() {
+    float mx = snx[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, snx[r]);
+    mx = halves_max(mx);
+    const float m_new = (mx > m_run + tau) ? mx : m_run;
+    const float alpha = fast_exp2((m_run - m_new) * s2);
+    m_run = m_new;
+    if (__ballot(alpha != 1.f)) {
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
+    }
+    const float mb = m_run * s2;
+    float lsum;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const float x = fast_exp2(fmaf(snx[e], s2, -mb));
+      lsum = e == 0 ? x : lsum + x;
+      pop[e >> 3][e & 7] = (__bf16)x;
+    }
+    l_run += lsum;
+  };
+
+  // Prologue: K_0, K_1, K_2, V_0, V_1 (tile j = t_lo + j); S of tile 0 and
+  // its probabilities.
+  tile_load_lds<D, BC, NWV>(kh, head_bytes, t_lo * BC, sK0, w, lane);
+  tile_load_lds<D, BC, NWV>(vh, head_bytes, t_lo * BC, sV0, w, lane);
+  tile_load_lds<D, BC, NWV>(kh, head_bytes, (t_lo + 1) * BC, sK1, w, lane);
+  tile_load_lds<D, BC, NWV>(vh, head_bytes, (t_lo + 1) * BC, sV1, w, lane);
+  tile_load_lds<D, BC, NWV>(kh, head_bytes, (t_lo + 2) * BC, sK2, w, lane);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  snx = (f32x16){};
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) snx = mfma32(tile_row8<D>(sK0, n, 2 * ks + h), qop[ks], snx);
+  mask_tile(t_lo, snx);
+  softmax_step();
+  __syncthreads();  // every wave has read K_0 before its slot is refilled
+
+  // Half-step end: the wait for the fetches issued two half-steps earlier
+  // (this wave's two latest stay in flight), then the barrier; so the tiles
+  // that M(u+1) reads are in LDS for every wave from the half-step before it.
+  auto end_half = [&]() {
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(2));
+    __builtin_amdgcn_s_barrier();
+  };
+  // Fetches of even half-step 2u: K_{u+3} into K_u's slot, V_{u+2} into V_{u-1}'s.
+  auto fetch = [&](int u, __bf16* Kf, __bf16* Vf) {
+    tile_load_lds<D, BC, NWV>(kh, head_bytes, (t_lo + u + 3) * BC, Kf, w, lane);
+    tile_load_lds<D, BC, NWV>(vh, head_bytes, (t_lo + u + 2) * BC, Vf, w, lane);
+  };
+  // M(u): S of tile u+1 from Kn (into snx) and O~ += V_u^T P~_u^T from Vc,
+  // the two kinds of MFMA alternating; operand i is read AHEAD MFMAs before
+  // its use, the first AHEAD by prefetch() in the half-step before.
+  bf16x8 ka[KS], va[2 * DT];
+  auto issue = [&](int i, const __bf16* Kn, const __bf16* Vc) {
+    if (i & 1) va[i >> 1] = rtr(Vc, i >> 1);
+    else ka[i >> 1] = rrow(Kn, i >> 1);
+  };
+  auto prefetch = [&](const __bf16* Kn, const __bf16* Vc) {
+    hide();
+#pragma unroll
+    for (int i = 0; i < AHEAD; ++i) issue(i, Kn, Vc);
+  };
+  auto mstep = [&](const __bf16* Kn, const __bf16* Vc) {
+    hide();
+    f32x16 s = (f32x16){};
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < 2 * KS; ++i) {
+      if (i + AHEAD < 2 * KS) issue(i + AHEAD, Kn, Vc);
+      if (i & 1) {
+        const int j = i >> 1;
+        oacc[j % DT] = mfma32(va[j], pop[j / DT], oacc[j % DT]);
+      } else {
+        s = mfma32(ka[i >> 1], qop[i >> 1], s);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    snx = s;
+  };
+  // V(u): probabilities of tile u+1 (when this group computes one; V(-1) of
+  // the second group is the prologue's).
+  auto vstep = [&](int u, int Tg) {
+    if (u >= 0 && u + 1 < Tg) {
+      mask_tile(t_lo + u + 1, snx);
+      softmax_step();
+    }
+  };
+
+  // Half-steps 0 .. 2T: the lead group runs M(u) at 2u and V(u) at 2u+1,
+  // the other V(u-1) at 2u and M(u) at 2u+1; both end with one more.  (The
+  // operands prefetched after a group's last M are read but never used.)
+  int u = 0;
+  if (lead) {
+    // With the causal mask the first group's queries (the workgroup's first
+    // 32 * NG) see only the tiles up to theirs; it computes those and then
+    // only fetches its share of the later tiles and joins the barriers.
+    const int Tg = p.causal ? min(T, (q0 + 32 * NG - 1) / BC - t_lo + 1) : T;
+    prefetch(sK1, sV0);
+    for (; u + 3 <= Tg; u += 3) {
+      fetch(u, sK0, sV2); mstep(sK1, sV0); end_half(); vstep(u, Tg); prefetch(sK2, sV1); end_half();
+      fetch(u + 1, sK1, sV0); mstep(sK2, sV1); end_half(); vstep(u + 1, Tg); prefetch(sK0, sV2); end_half();
+      fetch(u + 2, sK2, sV1); mstep(sK0, sV2); end_half(); vstep(u + 2, Tg); prefetch(sK1, sV0); end_half();
+    }
+    if (u < Tg) { fetch(u, sK0, sV2); mstep(sK1, sV0); end_half(); vstep(u, Tg); prefetch(sK2, sV1); end_half(); }
+    if (u + 1 < Tg) { fetch(u + 1, sK1, sV0); mstep(sK2, sV1); end_half(); vstep(u + 1, Tg); prefetch(sK0, sV2); end_half(); }
+    for (u += (u < Tg) + (u + 1 < Tg); u < T; ++u) {
+      if (u % 3 == 0) fetch(u, sK0, sV2);
+      else if (u % 3 == 1) fetch(u, sK1, sV0);
+      else fetch(u, sK2, sV1);
+      end_half();
+      end_half();
+    }
+    end_half();
+  } else {
+    for (; u + 3 <= T; u += 3) {
+      fetch(u, sK0, sV2); vstep(u - 1, T); prefetch(sK1, sV0); end_half(); mstep(sK1, sV0); end_half();
+      fetch(u + 1, sK1, sV0); vstep(u, T); prefetch(sK2, sV1); end_half(); mstep(sK2, sV1); end_half();
+      fetch(u + 2, sK2, sV1); vstep(u + 1, T); prefetch(sK0, sV2); end_half(); mstep(sK0, sV2); end_half();
+    }
+    if (u < T) { fetch(u, sK0, sV2); vstep(u - 1, T); prefetch(sK1, sV0); end_half(); mstep(sK1, sV0); end_half(); }
+    if (u + 1 < T) { fetch(u + 1, sK1, sV0); vstep(u, T); prefetch(sK2, sV1); end_half(); mstep(sK2, sV1); end_half(); }
+    end_half();
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // no fetch may land after the workgroup ends
+
+  const float l_tot = halves_sum(l_run);
+  if (my_q < N) {
+    const float inv = 1.f / l_tot;
+    const size_t row = head + (size_t)my_q * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = 32 * dt + 8 * g + 4 * h;
+        const float x0 = oacc[dt][4 * g + 0] * inv, x1 = oacc[dt][4 * g + 1] * inv;
+        const float x2 = oacc[dt][4 * g + 2] * inv, x3 = oacc[dt][4 * g + 3] * inv;
+        if (p.out_f32) {
+          *(f32x4*)((float*)p.o + row + d0) = (f32x4){x0, x1, x2, x3};
+        } else {
+          *(bf16x4*)((__bf16*)p.o + row + d0) =
+              (bf16x4){(__bf16)x0, (__bf16)x1, (__bf16)x2, (__bf16)x3};
+        }
+      }
+    if (h == 0 && p.lse)
+      p.lse[(size_t)bh * N + my_q] = (m_run * s2 + __builtin_amdgcn_logf(l_tot)) * kLn2;
+  }
+}
+
+// Kernel parameters for workgroups of `rows` queries.
+static FwdKParams fwd_params(const FwdArgs& a, int rows) {
   FwdKParams p;
   p.q = (const __bf16*)a.q;
   p.k = (const __bf16*)a.k;
@@ -350,15 +632,30 @@ static hipError_t launch_fwd_cfg(const FwdArgs& a, hipStream_t stream) {
   p.H = a.H;
   p.Hkv = a.Hkv;
   p.N = a.N;
-  p.n_qtiles = (a.N + 32 * NW - 1) / (32 * NW);
+  p.n_qtiles = (a.N + rows - 1) / rows;
   p.scale = a.scale;
   p.causal = a.causal;
   p.window = a.window;
   p.out_f32 = a.out_f32;
   p.drop = make_dropout(a.drop);
+  return p;
+}
+
+template <int D, int NW, int BC, bool DROP>
+static hipError_t launch_fwd_cfg(const FwdArgs& a, hipStream_t stream) {
+  const FwdKParams p = fwd_params(a, 32 * NW);
   const unsigned grid = (unsigned)(a.BH * p.n_qtiles);
   hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, BC, DROP>), dim3(grid), dim3(NW * 64), 0,
                      stream, p);
+  return hipGetLastError();
+}
+
+// d = 128 without dropout: the ping-pong kernel (two groups of 4 waves).
+static hipError_t launch_fwd_pp128(const FwdArgs& a, hipStream_t stream) {
+  constexpr int NG = 4;
+  const FwdKParams p = fwd_params(a, 64 * NG);
+  hipLaunchKernelGGL((fwd_pp_kernel<128, NG>), dim3((unsigned)(a.BH * p.n_qtiles)),
+                     dim3(2 * NG * 64), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -367,7 +664,7 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream) {
     if (a.d == 128) return launch_fwd_cfg<128, 4, 32, true>(a, stream);
     return launch_fwd_cfg<64, 4, 64, true>(a, stream);
   }
-  if (a.d == 128) return launch_fwd_cfg<128, 4, 32, false>(a, stream);
+  if (a.d == 128) return launch_fwd_pp128(a, stream);
   return launch_fwd_cfg<64, 4, 64, false>(a, stream);
 }
 
