@@ -1035,6 +1035,265 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdKParams p) {
   }
 }
 
+// ------------------------------------------------------------ dQ ping-pong
+// d = 128 without dropout: the dQ pass in workgroups of 8 waves (256
+// queries) split into two groups one half-step apart, as the forward's
+// ping-pong kernel: M(u) issues the S^T and D - dP^T MFMAs of key tile u+1
+// and dQ^T += K_u^T dS_u^T (24 MFMAs alternating), V(u) masks and forms P and
+// dS^T of tile u+1; a barrier ends every half-step.  K_j and V_j sit in slot
+// j % 4 of their rings; at every even half-step 2u the waves fetch K_{u+3}
+// and V_{u+3}, every half-step ends by waiting for the fetches of two
+// half-steps before, and a wave reads the first operands of its next M in
+// its V.  Under the causal mask the first group stops computing after the
+// last tile its 128 queries see and then only fetches and joins the
+// barriers.  Values and accumulation order are those of bwd_dq_kernel.
+template <int D, int NG>
+__global__ __launch_bounds__(2 * NG * 64, 2) void bwd_dq_pp_kernel(BwdKParams p) {
+  constexpr int BC = 32;
+  constexpr int NWV = 2 * NG;
+  constexpr int BR = 32 * NWV;
+  constexpr int KS = D / 16, DT = D / 32;
+  constexpr int NM = 3 * KS;  // MFMAs of one M: S, dP and dQ alternating
+  constexpr int AHEAD = 3;
+  __shared__ __attribute__((aligned(16))) __bf16 sK0[BC * D];
+  __shared__ __attribute__((aligned(16))) __bf16 sK1[BC * D];
+  __shared__ __attribute__((aligned(16))) __bf16 sK2[BC * D];
+  __shared__ __attribute__((aligned(16))) __bf16 sK3[BC * D];
+  __shared__ __attribute__((aligned(16))) __bf16 sV0[BC * D];
+  __shared__ __attribute__((aligned(16))) __bf16 sV1[BC * D];
+  __shared__ __attribute__((aligned(16))) __bf16 sV2[BC * D];
+  __shared__ __attribute__((aligned(16))) __bf16 sV3[BC * D];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, kept scalar
+  const bool lead = w < NG;
+  const int h = lane >> 5, n = lane & 31;
+  const TileId id =
+      tile_order(blockIdx.x, gridDim.x / p.n_tiles, p.n_tiles, p.causal, causal_group<D>());
+  const int bh = id.bh;
+  const int qt = p.causal ? p.n_tiles - 1 - id.rank : id.rank;  // longest first
+  const int N = p.N, W = p.window;
+  const int q0 = qt * BR;
+  const int wq0 = q0 + 32 * w;
+  const int my_q = wq0 + n;
+  const size_t head = (size_t)bh * N * D;
+  const size_t kv_off = (size_t)kv_head(bh, p.H, p.Hkv) * N * D;
+  const uint32_t head_bytes = (uint32_t)N * D * 2;
+  const auto rq = make_rsrc(p.q + head, head_bytes);
+  const __bf16* kh = p.k + kv_off;
+  const __bf16* vh = p.v + kv_off;
+  const auto rdo = make_rsrc(p.dout + head, head_bytes);
+  const auto ro = make_rsrc(p.o + head, head_bytes);
+
+  // Q^T and -dO^T as B operands (lane = query), D_i = sum_k dO_ik O_ik.
+  bf16x8 qop[KS], doop[KS];
+  float dpart = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    const uint32_t off = (uint32_t)(my_q * D + 16 * ks + 8 * h) * 2u;
+    qop[ks] = __builtin_bit_cast(bf16x8, buf_load16(rq, off));
+    doop[ks] = __builtin_bit_cast(bf16x8, buf_load16(rdo, off));
+    const bf16x8 ov = __builtin_bit_cast(bf16x8, buf_load16(ro, off));
+#pragma unroll
+    for (int e = 0; e < 8; ++e) dpart = fmaf((float)doop[ks][e], (float)ov[e], dpart);
+  }
+  const bool q_ok = my_q < N;
+  const float Lb = q_ok ? p.lse[(size_t)bh * N + my_q] * kLog2e : 0.f;
+  const float Dl = halves_sum(dpart);
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+    doop[ks] = __builtin_bit_cast(bf16x8, __builtin_bit_cast(u32x4, doop[ks]) ^ 0x80008000u);
+  const f32x16 dp0 = (f32x16){Dl, Dl, Dl, Dl, Dl, Dl, Dl, Dl, Dl, Dl, Dl, Dl, Dl, Dl, Dl, Dl};
+  if (q_ok && h == 0) {
+    p.delta[(size_t)bh * N + my_q] = Dl;
+    p.lse2[(size_t)bh * N + my_q] = Lb;
+  }
+
+  const int q_last = min(q0 + BR, N) - 1;
+  int kv_lo = 0, kv_hi = N;
+  if (p.causal) kv_hi = min(kv_hi, q_last + 1);
+  if (W > 0) {
+    kv_lo = max(0, q0 - W + 1);
+    if (!p.causal) kv_hi = min(kv_hi, q_last + W);
+  }
+  const int t_lo = kv_lo / BC, t_hi = (kv_hi + BC - 1) / BC;
+  const int T = t_hi - t_lo;
+  int hi_key = N - 1, lo_key = 0;
+  if (p.causal) hi_key = min(hi_key, my_q);
+  if (W > 0) {
+    lo_key = my_q - W + 1;
+    if (!p.causal) hi_key = min(hi_key, my_q + W - 1);
+  }
+
+  f32x16 dqacc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) dqacc[dt] = (f32x16){};
+  const float s2 = p.scale * kLog2e;
+  const TrCoord trc(lane);
+
+  // Byte offsets of this lane's operand reads in a tile (rows per K-step,
+  // transposing reads per d-tile and row half), re-hidden from the optimizer
+  // before use so that slot constants fold into the reads.
+  uint32_t roff[KS], toff[2 * DT];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) roff[ks] = (uint32_t)tile_off<D>(n, 2 * ks + h) * 2u;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      const int r = trc.row + 8 * x, col = 32 * dt + trc.col;
+      toff[2 * dt + x] = (uint32_t)(tile_off<D>(r, col >> 3) + (col & 7)) * 2u;
+    }
+  auto hide = [&]() {
+#pragma unroll
+    for (int i = 0; i < KS; ++i) asm volatile("" : "+v"(roff[i]));
+#pragma unroll
+    for (int i = 0; i < 2 * DT; ++i) asm volatile("" : "+v"(toff[i]));
+  };
+  auto rrow = [&](const __bf16* t, int ks) {
+    return *(const bf16x8*)((const char*)t + roff[ks]);
+  };
+  auto rtr = [&](const __bf16* t, int j) {  // K-step j / DT, d-tile j % DT
+    const char* b = (const char*)t + 16 * (j / DT) * D * 2;
+    return cat4(lds_read_tr16(b + toff[2 * (j % DT)]), lds_read_tr16(b + toff[2 * (j % DT) + 1]));
+  };
+
+  f32x16 snx, dpnx;  // S^T and D - dP^T of the tile whose dS comes next
+  bf16x8 dsop[2];
+  // Mask, P and dS^T (negated) of tile t from snx, dpnx into dsop.
+  auto ds_step = [&](int t) {
+    const int kv0 = t * BC;
+    bool need_mask = (kv0 + BC > N) || (wq0 + 32 > N);
+    if (p.causal) need_mask |= kv0 + BC - 1 > wq0;
+    if (W > 0) {
+      need_mask |= wq0 + 31 - kv0 >= W;
+      if (!p.causal) need_mask |= kv0 + BC - 1 - wq0 >= W;
+    }
+    if (need_mask) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = kv0 + 8 * (r >> 2) + 4 * h + (r & 3);
+        snx[r] = (key > hi_key || key < lo_key || !q_ok) ? -__builtin_inff() : snx[r];
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const float pv = fast_exp2(fmaf(snx[e], s2, -Lb));
+      dsop[e >> 3][e & 7] = (__bf16)(pv * dpnx[e]);
+    }
+  };
+
+  // Prologue: K_0..K_2, V_0..V_2; S^T, D - dP^T and dS^T of tile 0.
+  tile_load_lds<D, BC, NWV>(kh, head_bytes, t_lo * BC, sK0, w, lane);
+  tile_load_lds<D, BC, NWV>(vh, head_bytes, t_lo * BC, sV0, w, lane);
+  tile_load_lds<D, BC, NWV>(kh, head_bytes, (t_lo + 1) * BC, sK1, w, lane);
+  tile_load_lds<D, BC, NWV>(vh, head_bytes, (t_lo + 1) * BC, sV1, w, lane);
+  tile_load_lds<D, BC, NWV>(kh, head_bytes, (t_lo + 2) * BC, sK2, w, lane);
+  tile_load_lds<D, BC, NWV>(vh, head_bytes, (t_lo + 2) * BC, sV2, w, lane);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  snx = (f32x16){};
+  dpnx = dp0;
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    snx = mfma32(tile_row8<D>(sK0, n, 2 * ks + h), qop[ks], snx);
+    dpnx = mfma32(tile_row8<D>(sV0, n, 2 * ks + h), doop[ks], dpnx);
+  }
+  ds_step(t_lo);
+
+  auto end_half = [&]() {
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(2));
+    __builtin_amdgcn_s_barrier();
+  };
+  // Fetches of even half-step 2u: K_{u+3} and V_{u+3} into slot (u+3) % 4.
+  auto fetch = [&](int u, __bf16* Kf, __bf16* Vf) {
+    tile_load_lds<D, BC, NWV>(kh, head_bytes, (t_lo + u + 3) * BC, Kf, w, lane);
+    tile_load_lds<D, BC, NWV>(vh, head_bytes, (t_lo + u + 3) * BC, Vf, w, lane);
+  };
+  // M(u): operand i of the 3 KS MFMAs is, by i % 3, a K row (S of tile
+  // u+1), a V row (dP of tile u+1) or a transposed K_u pair (dQ, K-step and
+  // d-tile (i / 3) / DT, (i / 3) % DT).
+  bf16x8 opd[NM];
+  auto issue = [&](int i, const __bf16* Kc, const __bf16* Kn, const __bf16* Vn) {
+    const int j = i / 3;
+    if (i % 3 == 0) opd[i] = rrow(Kn, j);
+    else if (i % 3 == 1) opd[i] = rrow(Vn, j);
+    else opd[i] = rtr(Kc, j);
+  };
+  auto prefetch = [&](const __bf16* Kc, const __bf16* Kn, const __bf16* Vn) {
+    hide();
+#pragma unroll
+    for (int i = 0; i < AHEAD; ++i) issue(i, Kc, Kn, Vn);
+  };
+  auto mstep = [&](const __bf16* Kc, const __bf16* Kn, const __bf16* Vn) {
+    hide();
+    f32x16 s = (f32x16){}, dp = dp0;
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < NM; ++i) {
+      if (i + AHEAD < NM) issue(i + AHEAD, Kc, Kn, Vn);
+      const int j = i / 3;
+      if (i % 3 == 0) s = mfma32(opd[i], qop[j], s);
+      else if (i % 3 == 1) dp = mfma32(opd[i], doop[j], dp);
+      else dqacc[j % DT] = mfma32(opd[i], dsop[j / DT], dqacc[j % DT]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    snx = s;
+    dpnx = dp;
+  };
+  auto vstep = [&](int u, int Tg) {
+    if (u >= 0 && u + 1 < Tg) ds_step(t_lo + u + 1);
+  };
+
+  int u = 0;
+  if (lead) {
+    const int Tg = p.causal ? min(T, (q0 + 32 * NG - 1) / BC - t_lo + 1) : T;
+    prefetch(sK0, sK1, sV1);
+    for (; u + 4 <= Tg; u += 4) {
+      fetch(u, sK3, sV3); mstep(sK0, sK1, sV1); end_half(); vstep(u, Tg); prefetch(sK1, sK2, sV2); end_half();
+      fetch(u + 1, sK0, sV0); mstep(sK1, sK2, sV2); end_half(); vstep(u + 1, Tg); prefetch(sK2, sK3, sV3); end_half();
+      fetch(u + 2, sK1, sV1); mstep(sK2, sK3, sV3); end_half(); vstep(u + 2, Tg); prefetch(sK3, sK0, sV0); end_half();
+      fetch(u + 3, sK2, sV2); mstep(sK3, sK0, sV0); end_half(); vstep(u + 3, Tg); prefetch(sK0, sK1, sV1); end_half();
+    }
+    if (u < Tg) { fetch(u, sK3, sV3); mstep(sK0, sK1, sV1); end_half(); vstep(u, Tg); prefetch(sK1, sK2, sV2); end_half(); }
+    if (u + 1 < Tg) { fetch(u + 1, sK0, sV0); mstep(sK1, sK2, sV2); end_half(); vstep(u + 1, Tg); prefetch(sK2, sK3, sV3); end_half(); }
+    if (u + 2 < Tg) { fetch(u + 2, sK1, sV1); mstep(sK2, sK3, sV3); end_half(); vstep(u + 2, Tg); prefetch(sK3, sK0, sV0); end_half(); }
+    for (u += (u < Tg) + (u + 1 < Tg) + (u + 2 < Tg); u < T; ++u) {
+      if (u % 4 == 0) fetch(u, sK3, sV3);
+      else if (u % 4 == 1) fetch(u, sK0, sV0);
+      else if (u % 4 == 2) fetch(u, sK1, sV1);
+      else fetch(u, sK2, sV2);
+      end_half();
+      end_half();
+    }
+    end_half();
+  } else {
+    for (; u + 4 <= T; u += 4) {
+      fetch(u, sK3, sV3); vstep(u - 1, T); prefetch(sK0, sK1, sV1); end_half(); mstep(sK0, sK1, sV1); end_half();
+      fetch(u + 1, sK0, sV0); vstep(u, T); prefetch(sK1, sK2, sV2); end_half(); mstep(sK1, sK2, sV2); end_half();
+      fetch(u + 2, sK1, sV1); vstep(u + 1, T); prefetch(sK2, sK3, sV3); end_half(); mstep(sK2, sK3, sV3); end_half();
+      fetch(u + 3, sK2, sV2); vstep(u + 2, T); prefetch(sK3, sK0, sV0); end_half(); mstep(sK3, sK0, sV0); end_half();
+    }
+    if (u < T) { fetch(u, sK3, sV3); vstep(u - 1, T); prefetch(sK0, sK1, sV1); end_half(); mstep(sK0, sK1, sV1); end_half(); }
+    if (u + 1 < T) { fetch(u + 1, sK0, sV0); vstep(u, T); prefetch(sK1, sK2, sV2); end_half(); mstep(sK1, sK2, sV2); end_half(); }
+    if (u + 2 < T) { fetch(u + 2, sK1, sV1); vstep(u + 1, T); prefetch(sK2, sK3, sV3); end_half(); mstep(sK2, sK3, sV3); end_half(); }
+    end_half();
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // no fetch may land after the workgroup ends
+
+  if (q_ok) {
+    const size_t row = head + (size_t)my_q * D;
+    const float qs = -p.scale;  // (dS negated)
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        *(f32x4*)(p.dq + row + 32 * dt + 8 * g + 4 * h) =
+            (f32x4){dqacc[dt][4 * g] * qs, dqacc[dt][4 * g + 1] * qs,
+                    dqacc[dt][4 * g + 2] * qs, dqacc[dt][4 * g + 3] * qs};
+  }
+}
+
 static BwdKParams bwd_params(const BwdArgs& a, int tile_rows) {
   BwdKParams p;
   p.q = (const __bf16*)a.q;
@@ -1122,9 +1381,11 @@ hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream) {
   const bool drop = a.drop.thresh > 0;
   if (a.d == 128 && drop)
     hipLaunchKernelGGL((bwd_dq_kernel<128, kBwdWaves, 32, true>), grid, block, 0, stream, p);
-  else if (a.d == 128)
-    hipLaunchKernelGGL((bwd_dq_kernel<128, kBwdWaves, 32, false>), grid, block, 0, stream,
-                       p);
+  else if (a.d == 128) {
+    const BwdKParams pp = bwd_params(a, 64 * kBwdWaves);
+    hipLaunchKernelGGL((bwd_dq_pp_kernel<128, kBwdWaves>), dim3((unsigned)(a.BH * pp.n_tiles)),
+                       dim3(2 * 64 * kBwdWaves), 0, stream, pp);
+  }
   else if (drop)
     hipLaunchKernelGGL((bwd_dq_kernel<64, kBwdWaves, 64, true>), grid, block, 0, stream, p);
   else
