@@ -358,13 +358,15 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdKParams p) {
 // Under the causal mask the first group (the workgroup's first 128 queries)
 // stops computing after the last tile its queries see and from then on only
 // fetches its share of the tiles and joins the barriers.
-template <int D, int NG>
+template <int D, int NG, int BC>
 __global__ __launch_bounds__(2 * NG * 64, 2) void fwd_pp_kernel(FwdKParams p) {
-  constexpr int BC = 32;               // keys per tile
+  constexpr int MT = BC / 32;          // score tiles of 32 keys per K/V tile
   constexpr int NWV = 2 * NG;          // waves
   constexpr int BR = 32 * NWV;         // queries per workgroup
   constexpr int KS = D / 16, DT = D / 32;
   constexpr int AHEAD = 3;
+  constexpr int NSM = MT * KS;         // S MFMAs of one M; as many P V MFMAs
+  static_assert(NSM == (BC / 16) * DT, "S and P V products alternate one to one");
   __shared__ __attribute__((aligned(16))) __bf16 sK0[BC * D];
   __shared__ __attribute__((aligned(16))) __bf16 sK1[BC * D];
   __shared__ __attribute__((aligned(16))) __bf16 sK2[BC * D];
@@ -422,7 +424,7 @@ __global__ __launch_bounds__(2 * NG * 64, 2) void fwd_pp_kernel(FwdKParams p) {
     if (!p.causal) hi_key = min(hi_key, my_q + p.window - 1);
   }
   // Masks tile t's scores when the tile straddles a boundary of this wave.
-  auto mask_tile = [&](int t, f32x16& sacc) {
+  auto mask_tile = [&](int t, f32x16* sacc) {
     const int kv0 = t * BC;
     bool need = kv0 + BC > N;
     if (p.causal) need |= kv0 + BC - 1 > wq0;
@@ -433,10 +435,12 @@ __global__ __launch_bounds__(2 * NG * 64, 2) void fwd_pp_kernel(FwdKParams p) {
     if (!need) return;
     const int lim_hi = hi_key - kv0 - 4 * h, lim_lo = lo_key - kv0 - 4 * h;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int c = 8 * (r >> 2) + (r & 3);
-      sacc[r] = (c > lim_hi || c < lim_lo) ? -__builtin_inff() : sacc[r];
-    }
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int c = 32 * mt + 8 * (r >> 2) + (r & 3);
+        sacc[mt][r] = (c > lim_hi || c < lim_lo) ? -__builtin_inff() : sacc[mt][r];
+      }
   };
 
   // Byte offsets of this lane's operand reads in a tile (K rows per K-step;
@@ -458,22 +462,24 @@ __global__ __launch_bounds__(2 * NG * 64, 2) void fwd_pp_kernel(FwdKParams p) {
 #pragma unroll
     for (int i = 0; i < 2 * DT; ++i) asm volatile("" : "+v"(toff[i]));
   };
-  auto rrow = [&](const __bf16* t, int ks) {
-    return *(const bf16x8*)((const char*)t + roff[ks]);
+  // (Rows 32 mt + n share row n's swizzle, so a score tile mt is a constant
+  // offset.)
+  auto rrow = [&](const __bf16* t, int mt, int ks) {
+    return *(const bf16x8*)((const char*)t + roff[ks] + mt * 32 * D * 2);
   };
   auto rtr = [&](const __bf16* t, int j) {  // K-step j / DT, d-tile j % DT
     const char* b = (const char*)t + 16 * (j / DT) * D * 2;
     return cat4(lds_read_tr16(b + toff[2 * (j % DT)]), lds_read_tr16(b + toff[2 * (j % DT) + 1]));
   };
 
-  f32x16 snx;  // raw scores of the tile whose probabilities come next
-  bf16x8 pop[2];
+  f32x16 snx[MT];  // raw scores of the tile whose probabilities come next
+  bf16x8 pop[BC / 16];
   // Row max of snx (masked), running max moved past it, O~ and l rescaled,
   // then the probabilities of snx into pop and their sum into l.
   auto softmax_step = [&]() {
-    float mx = snx[0];
+    float mx = snx[0][0];
 #pragma unroll
-    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, snx[r]);
+    for (int e = 1; e < 16 * MT; ++e) mx = fmaxf(mx, snx[e >> 4][e & 15]);
     mx = halves_max(mx);
     const float m_new = (mx > m_run + tau) ? mx : m_run;
     const float alpha = fast_exp2((m_run - m_new) * s2);
@@ -486,8 +492,8 @@ __global__ __launch_bounds__(2 * NG * 64, 2) void fwd_pp_kernel(FwdKParams p) {
     const float mb = m_run * s2;
     float lsum;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const float x = fast_exp2(fmaf(snx[e], s2, -mb));
+    for (int e = 0; e < 16 * MT; ++e) {
+      const float x = fast_exp2(fmaf(snx[e >> 4][e & 15], s2, -mb));
       lsum = e == 0 ? x : lsum + x;
       pop[e >> 3][e & 7] = (__bf16)x;
     }
@@ -503,9 +509,13 @@ __global__ __launch_bounds__(2 * NG * 64, 2) void fwd_pp_kernel(FwdKParams p) {
   tile_load_lds<D, BC, NWV>(kh, head_bytes, (t_lo + 2) * BC, sK2, w, lane);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  snx = (f32x16){};
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) snx = mfma32(tile_row8<D>(sK0, n, 2 * ks + h), qop[ks], snx);
+  for (int mt = 0; mt < MT; ++mt) {
+    snx[mt] = (f32x16){};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      snx[mt] = mfma32(tile_row8<D>(sK0, 32 * mt + n, 2 * ks + h), qop[ks], snx[mt]);
+  }
   mask_tile(t_lo, snx);
   softmax_step();
   __syncthreads();  // every wave has read K_0 before its slot is refilled
@@ -525,10 +535,10 @@ __global__ __launch_bounds__(2 * NG * 64, 2) void fwd_pp_kernel(FwdKParams p) {
   // M(u): S of tile u+1 from Kn (into snx) and O~ += V_u^T P~_u^T from Vc,
   // the two kinds of MFMA alternating; operand i is read AHEAD MFMAs before
   // its use, the first AHEAD by prefetch() in the half-step before.
-  bf16x8 ka[KS], va[2 * DT];
+  bf16x8 ka[NSM], va[NSM];
   auto issue = [&](int i, const __bf16* Kn, const __bf16* Vc) {
     if (i & 1) va[i >> 1] = rtr(Vc, i >> 1);
-    else ka[i >> 1] = rrow(Kn, i >> 1);
+    else ka[i >> 1] = rrow(Kn, (i >> 1) / KS, (i >> 1) % KS);
   };
   auto prefetch = [&](const __bf16* Kn, const __bf16* Vc) {
     hide();
@@ -537,20 +547,24 @@ __global__ __launch_bounds__(2 * NG * 64, 2) void fwd_pp_kernel(FwdKParams p) {
   };
   auto mstep = [&](const __bf16* Kn, const __bf16* Vc) {
     hide();
-    f32x16 s = (f32x16){};
+    f32x16 s[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) s[mt] = (f32x16){};
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int i = 0; i < 2 * KS; ++i) {
-      if (i + AHEAD < 2 * KS) issue(i + AHEAD, Kn, Vc);
+    for (int i = 0; i < 2 * NSM; ++i) {
+      if (i + AHEAD < 2 * NSM) issue(i + AHEAD, Kn, Vc);
       if (i & 1) {
         const int j = i >> 1;
         oacc[j % DT] = mfma32(va[j], pop[j / DT], oacc[j % DT]);
       } else {
-        s = mfma32(ka[i >> 1], qop[i >> 1], s);
+        const int si = i >> 1;
+        s[si / KS] = mfma32(ka[si], qop[si % KS], s[si / KS]);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    snx = s;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) snx[mt] = s[mt];
   };
   // V(u): probabilities of tile u+1 (when this group computes one; V(-1) of
   // the second group is the prologue's).
@@ -650,11 +664,13 @@ static hipError_t launch_fwd_cfg(const FwdArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// d = 128 without dropout: the ping-pong kernel (two groups of 4 waves).
-static hipError_t launch_fwd_pp128(const FwdArgs& a, hipStream_t stream) {
+// Without dropout: the ping-pong kernel (two groups of 4 waves), 32-key tiles
+// at d = 128 and 64-key tiles at d = 64.
+template <int D, int BC>
+static hipError_t launch_fwd_pp(const FwdArgs& a, hipStream_t stream) {
   constexpr int NG = 4;
   const FwdKParams p = fwd_params(a, 64 * NG);
-  hipLaunchKernelGGL((fwd_pp_kernel<128, NG>), dim3((unsigned)(a.BH * p.n_qtiles)),
+  hipLaunchKernelGGL((fwd_pp_kernel<D, NG, BC>), dim3((unsigned)(a.BH * p.n_qtiles)),
                      dim3(2 * NG * 64), 0, stream, p);
   return hipGetLastError();
 }
@@ -664,8 +680,8 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream) {
     if (a.d == 128) return launch_fwd_cfg<128, 4, 32, true>(a, stream);
     return launch_fwd_cfg<64, 4, 64, true>(a, stream);
   }
-  if (a.d == 128) return launch_fwd_pp128(a, stream);
-  return launch_fwd_cfg<64, 4, 64, false>(a, stream);
+  if (a.d == 128) return launch_fwd_pp<128, 32>(a, stream);
+  return launch_fwd_pp<64, 64>(a, stream);
 }
 
 }  // namespace attn
