@@ -34,7 +34,7 @@
 //  * Workgroups are renumbered per XCD (whole heads per XCD, sharing K/V in
 //    that XCD's L2) and, with the causal mask, the longest query blocks run
 //    first.
-// fwd_bf16_kernel serves d = 64 and dropout; d = 128 without dropout runs
+// fwd_bf16_kernel serves dropout; without dropout the forward runs
 // fwd_pp_kernel below, which keeps this mapping but separates each wave's
 // matrix and vector work into alternating half-steps (ping-pong).
 #include "attn_device.hpp"
@@ -343,7 +343,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdKParams p) {
 }
 
 // ------------------------------------------------------------- ping-pong
-// d = 128 without dropout: the same computation in workgroups of 8 waves
+// Without dropout: the same computation in workgroups of 8 waves
 // (256 queries), split into two groups (waves 0-3 and 4-7; the hardware
 // places waves w and w + 4 on the same SIMD).  Each wave alternates a matrix
 // half-step M(u) -- S of tile u+1 and O~ += P~_u V_u, 16 MFMAs and their
