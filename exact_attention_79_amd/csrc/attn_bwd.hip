@@ -600,12 +600,13 @@ __global__ __launch_bounds__(2 * NPAIR * 64, 2) void bwd_dkdv_pair_kernel(BwdKPa
     }
   };
 
-  // Prologue: tiles 0, 1 and 2.  The dS wave's first step has no tile
+  // Prologue: tiles 0 to 3.  The dS wave's first step has no tile
   // before it; it runs on zeros (P buffer 1, slot 5 and its running D - dP),
   // so that its dK products add exactly nothing.
   load_tile(sQ0, sO0, sL0, sD0);
   load_tile(sQ1, sO1, sL1, sD1);
   load_tile(sQ2, sO2, sL2, sD2);
+  load_tile(sQ3, sO3, sL3, sD3);
   for (int i = tid; i < BQ * D / 8; i += NWV * 64) ((u32x4*)sQ5)[i] = (u32x4){};
   for (int i = tid; i < PSZ / 4; i += NWV * 64) ((f32x4*)sP1)[i] = (f32x4){};
   __builtin_amdgcn_s_waitcnt(0);
@@ -620,7 +621,7 @@ __global__ __launch_bounds__(2 * NPAIR * 64, 2) void bwd_dkdv_pair_kernel(BwdKPa
   }
 
   // Step s: slots c (tile s), nx (tile s+1), pv (tile s-1), f (filled with
-  // tile s+3; tile s+2 is in flight); P of tile s is written to Pw, P of
+  // tile s+4; tile s+3 is in flight); P of tile s is written to Pw, P of
   // tile s-1 read from Pr.
   // The two roles run separate loops (so that neither's registers are
   // shuffled at joins with the other's code); each step ends with the one
@@ -633,21 +634,29 @@ __global__ __launch_bounds__(2 * NPAIR * 64, 2) void bwd_dkdv_pair_kernel(BwdKPa
     for (int i = 0; i < 2 * DT; ++i) asm volatile("" : "+v"(toff[i]));
     asm volatile("" : "+v"(poff), "+v"(lhoff));
   };
-  // Tile s+2 has landed for every wave (this step's loads stay in flight:
-  // two, plus L or D for waves 0 and 1), P of tile s is visible to the dS
-  // waves, and the slot of tile s-2 may be refilled next step.
+  // Tile s+3 has landed for every wave (this step's loads stay in flight:
+  // two, plus L or D for waves 0 and 1); the slot of tile s-1 may be
+  // refilled next step.
   auto end_step = [&]() {
-    constexpr int kLgkm0 = 0x0F00;  // (lgkmcnt field cleared: wait for LDS ops)
     if (w < 2)
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm(3) & ~kLgkm0);
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(3));
     else
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm(2) & ~kLgkm0);
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(2));
     __builtin_amdgcn_s_barrier();
+  };
+  // The first AHEAD operand rows of a wave's next step are read at the end
+  // of this one, before the barrier: that step's tile has been in LDS for
+  // every wave since the previous barrier (tiles are fetched four steps
+  // ahead).
+  bf16x8 pre[AHEAD];
+  auto prefetch = [&](const __bf16* t) {
+#pragma unroll
+    for (int i = 0; i < AHEAD; ++i) pre[i] = rrow(t, i);
   };
   // P wave, step s < U: mask S of tile s, P = exp2(S s2 - L log2 e) (to Pw
   // and as the bf16 B operand), S of tile s+1, dV^T += dO^T P.
   auto pstep = [&](const __bf16* Oc, const float* Lc, const __bf16* Qnx, __bf16* Qf,
-                   __bf16* Of, float* Lf, float* Df, float* Pw) {
+                   __bf16* Of, float* Lf, float* Df, float* Pw, const __bf16* Qnext) {
     begin_step(Qf, Of, Lf, Df);
     const int i0 = ct * BQ;  // first query of tile s
     if (++ct == t_hi) ct = t_lo;
@@ -672,7 +681,7 @@ __global__ __launch_bounds__(2 * NPAIR * 64, 2) void bwd_dkdv_pair_kernel(BwdKPa
     bf16x8 aop[KS], top[2 * DT], pop[2];
     float pv[16];
 #pragma unroll
-    for (int i = 0; i < AHEAD; ++i) aop[i] = rrow(Qnx, i);
+    for (int i = 0; i < AHEAD; ++i) aop[i] = pre[i];
     __builtin_amdgcn_sched_barrier(0);
     // S of tile s+1, with two elements of P of tile s per bundle.
 #pragma unroll
@@ -701,12 +710,14 @@ __global__ __launch_bounds__(2 * NPAIR * 64, 2) void bwd_dkdv_pair_kernel(BwdKPa
       __builtin_amdgcn_sched_barrier(0);
     }
     cur = snext;
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): P of tile s is in LDS
+    prefetch(Qnext);
     end_step();
   };
   // dS wave, step s <= U: D - dP of tile s (from D, with -V), dS = P (dP - D)
   // of tile s-1 (negated; P from Pr), dK^T += Q^T dS of tile s-1.
   auto dstep = [&](const __bf16* Oc, const float* Dc, const __bf16* Qpv, __bf16* Qf,
-                   __bf16* Of, float* Lf, float* Df, const float* Pr) {
+                   __bf16* Of, float* Lf, float* Df, const float* Pr, const __bf16* Onext) {
     begin_step(Qf, Of, Lf, Df);
     f32x16 dpn;
 #pragma unroll
@@ -720,7 +731,7 @@ __global__ __launch_bounds__(2 * NPAIR * 64, 2) void bwd_dkdv_pair_kernel(BwdKPa
     for (int k = 0; k < 4; ++k) pp[k] = *(const f32x4*)((const char*)Pr + poff + 1024 * k);
     bf16x8 aop[KS], top[2 * DT], dsop[2];
 #pragma unroll
-    for (int i = 0; i < AHEAD; ++i) aop[i] = rrow(Oc, i);
+    for (int i = 0; i < AHEAD; ++i) aop[i] = pre[i];
     __builtin_amdgcn_sched_barrier(0);
     // D - dP of tile s, with two elements of dS of tile s-1 per bundle.
 #pragma unroll
@@ -743,44 +754,47 @@ __global__ __launch_bounds__(2 * NPAIR * 64, 2) void bwd_dkdv_pair_kernel(BwdKPa
       __builtin_amdgcn_sched_barrier(0);
     }
     cur = dpn;
+    prefetch(Onext);
     end_step();
   };
 
   // Step s uses slot s % 6 as c, (s+1) % 6 as nx, (s+5) % 6 as pv and fills
-  // (s+3) % 6; P buffer s % 2 is written and (s+1) % 2 read.  The P wave
+  // (s+4) % 6; P buffer s % 2 is written and (s+1) % 2 read.  The P wave
   // works on tiles 0 .. U-1 and then joins the last barrier; the dS wave on
   // tiles -1 .. U-1 (its dP products of tile U are never used).
   if (pwave) {
     int s = 0;
+    prefetch(sQ1);
     for (; s + 6 <= U; s += 6) {
-      pstep(sO0, sL0, sQ1, sQ3, sO3, sL3, sD3, sP0);
-      pstep(sO1, sL1, sQ2, sQ4, sO4, sL4, sD4, sP1);
-      pstep(sO2, sL2, sQ3, sQ5, sO5, sL5, sD5, sP0);
-      pstep(sO3, sL3, sQ4, sQ0, sO0, sL0, sD0, sP1);
-      pstep(sO4, sL4, sQ5, sQ1, sO1, sL1, sD1, sP0);
-      pstep(sO5, sL5, sQ0, sQ2, sO2, sL2, sD2, sP1);
+      pstep(sO0, sL0, sQ1, sQ4, sO4, sL4, sD4, sP0, sQ2);
+      pstep(sO1, sL1, sQ2, sQ5, sO5, sL5, sD5, sP1, sQ3);
+      pstep(sO2, sL2, sQ3, sQ0, sO0, sL0, sD0, sP0, sQ4);
+      pstep(sO3, sL3, sQ4, sQ1, sO1, sL1, sD1, sP1, sQ5);
+      pstep(sO4, sL4, sQ5, sQ2, sO2, sL2, sD2, sP0, sQ0);
+      pstep(sO5, sL5, sQ0, sQ3, sO3, sL3, sD3, sP1, sQ1);
     }
-    if (s < U) pstep(sO0, sL0, sQ1, sQ3, sO3, sL3, sD3, sP0);
-    if (s + 1 < U) pstep(sO1, sL1, sQ2, sQ4, sO4, sL4, sD4, sP1);
-    if (s + 2 < U) pstep(sO2, sL2, sQ3, sQ5, sO5, sL5, sD5, sP0);
-    if (s + 3 < U) pstep(sO3, sL3, sQ4, sQ0, sO0, sL0, sD0, sP1);
-    if (s + 4 < U) pstep(sO4, sL4, sQ5, sQ1, sO1, sL1, sD1, sP0);
+    if (s < U) pstep(sO0, sL0, sQ1, sQ4, sO4, sL4, sD4, sP0, sQ2);
+    if (s + 1 < U) pstep(sO1, sL1, sQ2, sQ5, sO5, sL5, sD5, sP1, sQ3);
+    if (s + 2 < U) pstep(sO2, sL2, sQ3, sQ0, sO0, sL0, sD0, sP0, sQ4);
+    if (s + 3 < U) pstep(sO3, sL3, sQ4, sQ1, sO1, sL1, sD1, sP1, sQ5);
+    if (s + 4 < U) pstep(sO4, sL4, sQ5, sQ2, sO2, sL2, sD2, sP0, sQ0);
     end_step();
   } else {
     int s = 0;
+    prefetch(sO0);
     for (; s + 6 <= U + 1; s += 6) {
-      dstep(sO0, sD0, sQ5, sQ3, sO3, sL3, sD3, sP1);
-      dstep(sO1, sD1, sQ0, sQ4, sO4, sL4, sD4, sP0);
-      dstep(sO2, sD2, sQ1, sQ5, sO5, sL5, sD5, sP1);
-      dstep(sO3, sD3, sQ2, sQ0, sO0, sL0, sD0, sP0);
-      dstep(sO4, sD4, sQ3, sQ1, sO1, sL1, sD1, sP1);
-      dstep(sO5, sD5, sQ4, sQ2, sO2, sL2, sD2, sP0);
+      dstep(sO0, sD0, sQ5, sQ4, sO4, sL4, sD4, sP1, sO1);
+      dstep(sO1, sD1, sQ0, sQ5, sO5, sL5, sD5, sP0, sO2);
+      dstep(sO2, sD2, sQ1, sQ0, sO0, sL0, sD0, sP1, sO3);
+      dstep(sO3, sD3, sQ2, sQ1, sO1, sL1, sD1, sP0, sO4);
+      dstep(sO4, sD4, sQ3, sQ2, sO2, sL2, sD2, sP1, sO5);
+      dstep(sO5, sD5, sQ4, sQ3, sO3, sL3, sD3, sP0, sO0);
     }
-    if (s <= U) dstep(sO0, sD0, sQ5, sQ3, sO3, sL3, sD3, sP1);
-    if (s + 1 <= U) dstep(sO1, sD1, sQ0, sQ4, sO4, sL4, sD4, sP0);
-    if (s + 2 <= U) dstep(sO2, sD2, sQ1, sQ5, sO5, sL5, sD5, sP1);
-    if (s + 3 <= U) dstep(sO3, sD3, sQ2, sQ0, sO0, sL0, sD0, sP0);
-    if (s + 4 <= U) dstep(sO4, sD4, sQ3, sQ1, sO1, sL1, sD1, sP1);
+    if (s <= U) dstep(sO0, sD0, sQ5, sQ4, sO4, sL4, sD4, sP1, sO1);
+    if (s + 1 <= U) dstep(sO1, sD1, sQ0, sQ5, sO5, sL5, sD5, sP0, sO2);
+    if (s + 2 <= U) dstep(sO2, sD2, sQ1, sQ0, sO0, sL0, sD0, sP1, sO3);
+    if (s + 3 <= U) dstep(sO3, sD3, sQ2, sQ1, sO1, sL1, sD1, sP0, sO4);
+    if (s + 4 <= U) dstep(sO4, sD4, sQ3, sQ2, sO2, sL2, sD2, sP1, sO5);
   }
   __builtin_amdgcn_s_waitcnt(0);  // no load may land after the workgroup ends
 
