@@ -817,6 +817,297 @@ __global__ __launch_bounds__(2 * NPAIR * 64, 2) void bwd_dkdv_pair_kernel(BwdKPa
   }
 }
 
+// --------------------------------------------------- dK, dV ping-pong (d = 64)
+// d = 64 without dropout or causal mask: workgroups of 8 waves (256 keys, 32 per wave, K^T
+// and -V^T resident), split into two groups one half-step apart as in the
+// ping-pong forward: M(u) issues the S and D - dP MFMAs of query tile u+1
+// and dV^T += dO_u^T P_u, dK^T += Q_u^T dS_u (16 MFMAs, the four kinds
+// alternating), V(u) masks and forms P and dS of tile u+1; a barrier ends
+// every half-step.  Query tiles of 32 rows (Q by waves 0-3, dO by waves 4-7,
+// L and D by waves 0 and 1) sit in slot j % 4 of their rings; tile u+3 is
+// fetched at half-step 2u, every half-step ends by waiting for the fetches of
+// two half-steps before, and a wave reads the first operands of its next M
+// in its V.  The walk over the group's query heads and the split into
+// shares are those of bwd_dkdv_kernel; values and accumulation order too.
+template <int D, int NG>
+__global__ __launch_bounds__(2 * NG * 64, 2) void bwd_dkdv_pp_kernel(BwdKParams p) {
+  constexpr int BQ = 32;
+  constexpr int NWV = 2 * NG;
+  constexpr int BKV = 32 * NWV;
+  constexpr int KS = D / 16, DT = D / 32;
+  static_assert(KS == (BQ / 16) * DT, "S, dP, dV and dK products alternate one to one");
+  constexpr int NM = 4 * KS;
+  constexpr int AHEAD = 3;
+  constexpr int LDROWS = 64;
+  __shared__ __attribute__((aligned(16))) __bf16 sQ0[BQ * D];
+  __shared__ __attribute__((aligned(16))) __bf16 sQ1[BQ * D];
+  __shared__ __attribute__((aligned(16))) __bf16 sQ2[BQ * D];
+  __shared__ __attribute__((aligned(16))) __bf16 sQ3[BQ * D];
+  __shared__ __attribute__((aligned(16))) __bf16 sO0[BQ * D];
+  __shared__ __attribute__((aligned(16))) __bf16 sO1[BQ * D];
+  __shared__ __attribute__((aligned(16))) __bf16 sO2[BQ * D];
+  __shared__ __attribute__((aligned(16))) __bf16 sO3[BQ * D];
+  __shared__ __attribute__((aligned(16))) float sL0[LDROWS], sL1[LDROWS], sL2[LDROWS], sL3[LDROWS];
+  __shared__ __attribute__((aligned(16))) float sD0[LDROWS], sD1[LDROWS], sD2[LDROWS], sD3[LDROWS];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, kept scalar
+  const bool lead = w < NG;
+  const int h = lane >> 5, n = lane & 31;
+  const TileId id =
+      tile_order(blockIdx.x, gridDim.x / p.n_tiles, p.n_tiles, p.causal, causal_group<D>());
+  const int bkv = id.bh / p.split;
+  const int share = id.bh % p.split;
+  const int kt = id.rank;
+  const int N = p.N, W = p.window;
+  const int G = p.H / p.Hkv / p.split;
+  const int bh0 = (bkv / p.Hkv) * p.H + (bkv % p.Hkv) * (p.H / p.Hkv) + share * G;
+  const int k0 = kt * BKV;
+  const int kw0 = k0 + 32 * w;
+  const int my_k = kw0 + n;
+  const size_t head = (size_t)bkv * N * D;
+  const uint32_t head_bytes = (uint32_t)N * D * 2;
+
+  // K^T and -V^T as B operands (lane = key); the dP MFMAs start from D_i
+  // and take -V, leaving D_i - dP_ij, and dS comes out negated.
+  bf16x8 kop[KS], vop[KS];
+  {
+    const auto rk = make_rsrc(p.k + head, head_bytes);
+    const auto rv = make_rsrc(p.v + head, head_bytes);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const uint32_t off = (uint32_t)(my_k * D + 16 * ks + 8 * h) * 2u;
+      kop[ks] = __builtin_bit_cast(bf16x8, buf_load16(rk, off));
+      vop[ks] = __builtin_bit_cast(bf16x8, buf_load16(rv, off) ^ 0x80008000u);
+    }
+  }
+  f32x16 dkacc[DT], dvacc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) dkacc[dt] = dvacc[dt] = (f32x16){};
+
+  const int k_last = min(k0 + BKV, N) - 1;
+  int q_lo = p.causal ? k0 : 0, q_hi = N;
+  int qmin = p.causal ? my_k : INT_MIN, qmax = INT_MAX;
+  if (W > 0) {
+    q_lo = max(q_lo, k0 - W + 1);
+    q_hi = min(q_hi, k_last + W);
+    if (!p.causal) qmin = my_k - W + 1;
+    qmax = my_k + W - 1;
+  }
+  const int t_lo = q_lo / BQ, t_hi = (q_hi + BQ - 1) / BQ;
+  const int T = G * (t_hi - t_lo);  // tiles in the walk (query head, tile)
+
+  const float s2 = p.scale * kLog2e;
+  const TrCoord trc(lane);
+  uint32_t roff[KS], toff[2 * DT];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) roff[ks] = (uint32_t)tile_off<D>(n, 2 * ks + h) * 2u;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      const int r = trc.row + 8 * x, col = 32 * dt + trc.col;
+      toff[2 * dt + x] = (uint32_t)(tile_off<D>(r, col >> 3) + (col & 7)) * 2u;
+    }
+  uint32_t lhoff = (uint32_t)(16 * h);
+  auto hide = [&]() {
+#pragma unroll
+    for (int i = 0; i < KS; ++i) asm volatile("" : "+v"(roff[i]));
+#pragma unroll
+    for (int i = 0; i < 2 * DT; ++i) asm volatile("" : "+v"(toff[i]));
+    asm volatile("" : "+v"(lhoff));
+  };
+  auto rrow = [&](const __bf16* t, int ks) {
+    return *(const bf16x8*)((const char*)t + roff[ks]);
+  };
+  auto rtr = [&](const __bf16* t, int j) {  // K-step j / DT, d-tile j % DT
+    const char* b = (const char*)t + 16 * (j / DT) * D * 2;
+    return cat4(lds_read_tr16(b + toff[2 * (j % DT)]), lds_read_tr16(b + toff[2 * (j % DT) + 1]));
+  };
+  auto rvec4 = [&](const float* t, int g) {  // rows 8g + 4h .. +3
+    return *(const f32x4*)((const char*)t + lhoff + 32 * g);
+  };
+
+  // Load cursor over the walk; past the last head it keeps reading the last
+  // head's rows (in bounds, never used).
+  int lj = 0, lt = t_lo, ct = t_lo;
+  auto load_tile = [&](__bf16* Qf, __bf16* Of, float* Lf, float* Df) {
+    const int bhq = bh0 + min(lj, G - 1);
+    const size_t qhead = (size_t)bhq * N * D;
+    if (lead)
+      tile_load_lds<D, BQ, NG>(p.q + qhead, head_bytes, lt * BQ, Qf, w, lane);
+    else
+      tile_load_lds<D, BQ, NG>(p.dout + qhead, head_bytes, lt * BQ, Of, w - NG, lane);
+    if (w == 0)
+      vec_load_lds<LDROWS>(make_rsrc(p.lse2 + (size_t)bhq * N, (uint32_t)N * 4), lt * BQ,
+                           Lf, lane);
+    if (w == 1)
+      vec_load_lds<LDROWS>(make_rsrc(p.delta + (size_t)bhq * N, (uint32_t)N * 4), lt * BQ,
+                           Df, lane);
+    if (++lt == t_hi) {
+      lt = t_lo;
+      ++lj;
+    }
+  };
+
+  f32x16 snx, dpnx;  // S and D - dP of the tile whose P and dS come next
+  bf16x8 pop[2], dsop[2];
+  // Mask (query tile starting at i0), P = exp2(S s2 - L log2 e) and dS (negated).
+  auto ds_step = [&](int i0, const float* Lc) {
+    bool need_mask = false;
+    if (p.causal) need_mask |= i0 < kw0 + 31;
+    if (W > 0) {
+      need_mask |= (i0 + BQ - 1) - kw0 >= W;
+      if (!p.causal) need_mask |= (kw0 + 31) - i0 >= W;
+    }
+    if (need_mask) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int q = i0 + 8 * (r >> 2) + 4 * h + (r & 3);
+        snx[r] = (q < qmin || q > qmax) ? -__builtin_inff() : snx[r];
+      }
+    }
+    f32x4 lb[4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) lb[g] = rvec4(Lc, g);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const float pv = fast_exp2(fmaf(snx[e], s2, -lb[e >> 2][e & 3]));
+      pop[e >> 3][e & 7] = (__bf16)pv;
+      dsop[e >> 3][e & 7] = (__bf16)(pv * dpnx[e]);
+    }
+  };
+  auto dp_init = [&](const float* Ds) {
+    f32x16 c;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const f32x4 v = rvec4(Ds, g);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) c[4 * g + i] = v[i];
+    }
+    return c;
+  };
+
+  // Prologue: tiles 0, 1, 2; S, D - dP, P and dS of tile 0.
+  load_tile(sQ0, sO0, sL0, sD0);
+  load_tile(sQ1, sO1, sL1, sD1);
+  load_tile(sQ2, sO2, sL2, sD2);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  hide();
+  snx = (f32x16){};
+  dpnx = dp_init(sD0);
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    snx = mfma32(tile_row8<D>(sQ0, n, 2 * ks + h), kop[ks], snx);
+    dpnx = mfma32(tile_row8<D>(sO0, n, 2 * ks + h), vop[ks], dpnx);
+  }
+  ds_step(ct * BQ, sL0);
+  if (++ct == t_hi) ct = t_lo;
+
+  auto end_half = [&]() {
+    if (w < 2)
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(2));
+    else
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(1));
+    __builtin_amdgcn_s_barrier();
+  };
+  auto fetch = [&](__bf16* Qf, __bf16* Of, float* Lf, float* Df) { load_tile(Qf, Of, Lf, Df); };
+  // M(u) operand i: by i % 4 a Q row (S of tile u+1), a dO row (dP of tile
+  // u+1), a transposed dO_u pair (dV) or a transposed Q_u pair (dK).
+  bf16x8 opd[NM];
+  auto issue = [&](int i, const __bf16* Qc, const __bf16* Oc, const __bf16* Qn,
+                   const __bf16* On) {
+    const int j = i / 4;
+    if (i % 4 == 0) opd[i] = rrow(Qn, j);
+    else if (i % 4 == 1) opd[i] = rrow(On, j);
+    else if (i % 4 == 2) opd[i] = rtr(Oc, j);
+    else opd[i] = rtr(Qc, j);
+  };
+  auto prefetch = [&](const __bf16* Qc, const __bf16* Oc, const __bf16* Qn, const __bf16* On) {
+    hide();
+#pragma unroll
+    for (int i = 0; i < AHEAD; ++i) issue(i, Qc, Oc, Qn, On);
+  };
+  auto mstep = [&](const __bf16* Qc, const __bf16* Oc, const __bf16* Qn, const __bf16* On,
+                   const float* Dn) {
+    hide();
+    f32x16 s = (f32x16){}, dp = dp_init(Dn);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < NM; ++i) {
+      if (i + AHEAD < NM) issue(i + AHEAD, Qc, Oc, Qn, On);
+      const int j = i / 4;
+      if (i % 4 == 0) s = mfma32(opd[i], kop[j], s);
+      else if (i % 4 == 1) dp = mfma32(opd[i], vop[j], dp);
+      else if (i % 4 == 2) dvacc[j % DT] = mfma32(opd[i], pop[j / DT], dvacc[j % DT]);
+      else dkacc[j % DT] = mfma32(opd[i], dsop[j / DT], dkacc[j % DT]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    snx = s;
+    dpnx = dp;
+  };
+  auto vstep = [&](int u, const float* Ln) {
+    if (u >= 0 && u + 1 < T) {
+      hide();
+      ds_step(ct * BQ, Ln);
+      if (++ct == t_hi) ct = t_lo;
+    }
+  };
+
+  // Half-steps 0 .. 2T: the lead group runs M(u) at 2u and V(u) at 2u+1,
+  // the other V(u-1) at 2u and M(u) at 2u+1; both end with one more.
+  int u = 0;
+  if (lead) {
+    prefetch(sQ0, sO0, sQ1, sO1);
+    for (; u + 4 <= T; u += 4) {
+      fetch(sQ3, sO3, sL3, sD3); mstep(sQ0, sO0, sQ1, sO1, sD1); end_half(); vstep(u, sL1); prefetch(sQ1, sO1, sQ2, sO2); end_half();
+      fetch(sQ0, sO0, sL0, sD0); mstep(sQ1, sO1, sQ2, sO2, sD2); end_half(); vstep(u + 1, sL2); prefetch(sQ2, sO2, sQ3, sO3); end_half();
+      fetch(sQ1, sO1, sL1, sD1); mstep(sQ2, sO2, sQ3, sO3, sD3); end_half(); vstep(u + 2, sL3); prefetch(sQ3, sO3, sQ0, sO0); end_half();
+      fetch(sQ2, sO2, sL2, sD2); mstep(sQ3, sO3, sQ0, sO0, sD0); end_half(); vstep(u + 3, sL0); prefetch(sQ0, sO0, sQ1, sO1); end_half();
+    }
+    if (u < T) { fetch(sQ3, sO3, sL3, sD3); mstep(sQ0, sO0, sQ1, sO1, sD1); end_half(); vstep(u, sL1); prefetch(sQ1, sO1, sQ2, sO2); end_half(); }
+    if (u + 1 < T) { fetch(sQ0, sO0, sL0, sD0); mstep(sQ1, sO1, sQ2, sO2, sD2); end_half(); vstep(u + 1, sL2); prefetch(sQ2, sO2, sQ3, sO3); end_half(); }
+    if (u + 2 < T) { fetch(sQ1, sO1, sL1, sD1); mstep(sQ2, sO2, sQ3, sO3, sD3); end_half(); vstep(u + 2, sL3); prefetch(sQ3, sO3, sQ0, sO0); end_half(); }
+    end_half();
+  } else {
+    for (; u + 4 <= T; u += 4) {
+      fetch(sQ3, sO3, sL3, sD3); vstep(u - 1, sL0); prefetch(sQ0, sO0, sQ1, sO1); end_half(); mstep(sQ0, sO0, sQ1, sO1, sD1); end_half();
+      fetch(sQ0, sO0, sL0, sD0); vstep(u, sL1); prefetch(sQ1, sO1, sQ2, sO2); end_half(); mstep(sQ1, sO1, sQ2, sO2, sD2); end_half();
+      fetch(sQ1, sO1, sL1, sD1); vstep(u + 1, sL2); prefetch(sQ2, sO2, sQ3, sO3); end_half(); mstep(sQ2, sO2, sQ3, sO3, sD3); end_half();
+      fetch(sQ2, sO2, sL2, sD2); vstep(u + 2, sL3); prefetch(sQ3, sO3, sQ0, sO0); end_half(); mstep(sQ3, sO3, sQ0, sO0, sD0); end_half();
+    }
+    if (u < T) { fetch(sQ3, sO3, sL3, sD3); vstep(u - 1, sL0); prefetch(sQ0, sO0, sQ1, sO1); end_half(); mstep(sQ0, sO0, sQ1, sO1, sD1); end_half(); }
+    if (u + 1 < T) { fetch(sQ0, sO0, sL0, sD0); vstep(u, sL1); prefetch(sQ1, sO1, sQ2, sO2); end_half(); mstep(sQ1, sO1, sQ2, sO2, sD2); end_half(); }
+    if (u + 2 < T) { fetch(sQ1, sO1, sL1, sD1); vstep(u + 1, sL2); prefetch(sQ2, sO2, sQ3, sO3); end_half(); mstep(sQ2, sO2, sQ3, sO3, sD3); end_half(); }
+    end_half();
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // no load may land after the workgroup ends
+
+  float* dk_out = p.dk;
+  float* dv_out = p.dv;
+  if (p.split > 1) {
+    const size_t part = (size_t)(gridDim.x / p.n_tiles / p.split) * N * D;
+    dk_out = p.dk_part + share * part;
+    dv_out = p.dv_part + share * part;
+  }
+  if (my_k < N) {
+    const size_t row = head + (size_t)my_k * D;
+    const float ks_ = -p.scale;  // (dS negated)
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = 32 * dt + 8 * g + 4 * h;
+        *(f32x4*)(dk_out + row + d0) =
+            (f32x4){dkacc[dt][4 * g] * ks_, dkacc[dt][4 * g + 1] * ks_,
+                    dkacc[dt][4 * g + 2] * ks_, dkacc[dt][4 * g + 3] * ks_};
+        *(f32x4*)(dv_out + row + d0) = (f32x4){dvacc[dt][4 * g], dvacc[dt][4 * g + 1],
+                                               dvacc[dt][4 * g + 2], dvacc[dt][4 * g + 3]};
+      }
+  }
+}
+
 // out = sum over `split` partial arrays of n4 float4 each (stride n4 apart),
 // in share order, so the result does not depend on scheduling.
 __global__ __launch_bounds__(256) void bwd_share_sum_kernel(const f32x4* part, f32x4* out,
@@ -1375,9 +1666,21 @@ hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream) {
   else if (drop)
     hipLaunchKernelGGL((bwd_dkdv_kernel<64, kBwdWaves, kDropQTile, true>), grid, block, 0,
                        stream, p);
-  else
+  else if (a.causal)
     hipLaunchKernelGGL((bwd_dkdv_kernel<64, kBwdWaves, dkdv_qtile<64>(), false>), grid,
                        block, 0, stream, p);
+  else {
+    // d = 64 without dropout or causal mask: the ping-pong kernel, 256 keys
+    // per workgroup (the same shares of the group, so the same workspace).
+    // Under the causal mask its second group would compute four query tiles
+    // its keys cannot see (measured 0.5-1.5 % slower), so causal launches keep
+    // the kernel above.
+    BwdKParams pp = bwd_params(a, 64 * kBwdWaves);
+    pp.split = p.split;
+    hipLaunchKernelGGL((bwd_dkdv_pp_kernel<64, kBwdWaves>),
+                       dim3((unsigned)(BHkv * pp.n_tiles * pp.split)), dim3(2 * 64 * kBwdWaves), 0,
+                       stream, pp);
+  }
   if (p.split > 1) {
     const size_t n4 = (size_t)BHkv * a.N * a.d / 4;
     const unsigned sum_grid = (unsigned)std::min<size_t>((n4 + 255) / 256, 8192);
