@@ -11,7 +11,7 @@ import pytest
 import torch
 
 import oracle
-from helpers import BF16_MAX, BF16_MEAN, assert_close, bf16_case, log
+from helpers import BF16_MAX, BF16_MEAN, LSE_MAX, assert_close, bf16_case, log
 
 pytestmark = pytest.mark.gpu
 
@@ -65,6 +65,25 @@ def test_dkdv_tile_walk_lengths(ea, N, causal):
     d = 128
     log(f"case: bwd B1 H2 N{N} d{d} causal={causal} (dK/dV walk lengths)")
     dev, ref = bf16_case(470 + N, 1, 2, N, d, with_dout=True)
+    got = fwd_bwd(ea, dev, causal, 0)
+    want = oracle.bwd(ref["q"], ref["k"], ref["v"], ref["do"], 1 / math.sqrt(d), causal, 0)[:3]
+    for name, g, r in zip(("dQ", "dK", "dV"), got, want):
+        assert_close(g, r, BF16_MAX, BF16_MEAN, name)
+
+
+# At d = 64 the forward walks 64-key tiles (a loop unrolled three steps deep)
+# and the non-causal dK/dV pass 32-row query tiles (four deep): N = 64 .. 512
+# covers walks of 1 to 8 and 2 to 16 tiles; causal at N = 576 exercises the
+# forward's first group stopping early.
+@pytest.mark.parametrize("N,causal", [(64 * u, False) for u in range(1, 9)] + [(576, True)])
+def test_d64_tile_walk_lengths(ea, N, causal):
+    d = 64
+    log(f"case: bwd B1 H2 N{N} d{d} causal={causal} (d = 64 walk lengths)")
+    dev, ref = bf16_case(490 + N, 1, 2, N, d, with_dout=True)
+    o, lse = ea.attn_fwd(dev["q"], dev["k"], dev["v"], causal=causal)
+    o_ref, lse_ref = oracle.fwd(ref["q"], ref["k"], ref["v"], 1 / math.sqrt(d), causal)
+    assert_close(o.float().cpu().numpy().astype(np.float64), o_ref, BF16_MAX, BF16_MEAN, "O")
+    assert_close(lse.cpu().numpy().astype(np.float64), lse_ref, LSE_MAX, None, "LSE")
     got = fwd_bwd(ea, dev, causal, 0)
     want = oracle.bwd(ref["q"], ref["k"], ref["v"], ref["do"], 1 / math.sqrt(d), causal, 0)[:3]
     for name, g, r in zip(("dQ", "dK", "dV"), got, want):
