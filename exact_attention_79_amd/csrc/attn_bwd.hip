@@ -8,17 +8,19 @@
 // dS_ij = P_ij (dP_ij - D_i) with D_i = sum_k dO_ik O_ik, and the scale s of
 // S = s Q K^T gives dQ = s dS K and dK = s dS^T Q.
 //
-// Two launches on the caller's stream:
+// Two launches on the caller's stream (which kernel serves which head dim
+// and mask: without dropout, bwd_dq_pp_kernel at d = 128, bwd_dkdv_pair_kernel
+// at d = 128 and bwd_dkdv_pp_kernel at d = 64 non-causal; the single-wave
+// kernels otherwise):
 //  1. bwd_dq_kernel: one workgroup per query block, Q_i, dO_i, L_i, D_i
 //     resident, looping over the K/V blocks it sees; dQ_i accumulates in
 //     VGPRs and is written once.  Each lane owns one query row, so it forms
 //     D_i = rowsum(dO_i * O_i) itself (one read of O_i) and also leaves D_i
 //     and L_i log2(e) in the workspace for the second launch;
-//  2. bwd_dkdv_kernel (bwd_dkdv_pair_kernel at d = 128 without dropout): one
-//     workgroup per K/V block (the page's column-block partition of the
-//     backward), K_j and V_j resident in VGPRs, looping over the query blocks
-//     that can see them; dK_j and dV_j accumulate in VGPRs and are written
-//     once.
+//  2. bwd_dkdv_kernel: one workgroup per K/V block (the page's column-block
+//     partition of the backward), K_j and V_j resident in VGPRs, looping over
+//     the query blocks that can see them; dK_j and dV_j accumulate in VGPRs
+//     and are written once.
 // bwd_delta_kernel writes the same two workspace arrays on its own (for
 // callers that run the dK/dV pass without the dQ pass).
 // Splitting dQ into its own pass recomputes S and dP there (two extra
@@ -1061,25 +1063,107 @@ __global__ __launch_bounds__(2 * NG * 64, 2) void bwd_dkdv_pp_kernel(BwdKParams 
   if (lead) {
     prefetch(sQ0, sO0, sQ1, sO1);
     for (; u + 4 <= T; u += 4) {
-      fetch(sQ3, sO3, sL3, sD3); mstep(sQ0, sO0, sQ1, sO1, sD1); end_half(); vstep(u, sL1); prefetch(sQ1, sO1, sQ2, sO2); end_half();
-      fetch(sQ0, sO0, sL0, sD0); mstep(sQ1, sO1, sQ2, sO2, sD2); end_half(); vstep(u + 1, sL2); prefetch(sQ2, sO2, sQ3, sO3); end_half();
-      fetch(sQ1, sO1, sL1, sD1); mstep(sQ2, sO2, sQ3, sO3, sD3); end_half(); vstep(u + 2, sL3); prefetch(sQ3, sO3, sQ0, sO0); end_half();
-      fetch(sQ2, sO2, sL2, sD2); mstep(sQ3, sO3, sQ0, sO0, sD0); end_half(); vstep(u + 3, sL0); prefetch(sQ0, sO0, sQ1, sO1); end_half();
+      fetch(sQ3, sO3, sL3, sD3);
+      mstep(sQ0, sO0, sQ1, sO1, sD1);
+      end_half();
+      vstep(u, sL1);
+      prefetch(sQ1, sO1, sQ2, sO2);
+      end_half();
+      fetch(sQ0, sO0, sL0, sD0);
+      mstep(sQ1, sO1, sQ2, sO2, sD2);
+      end_half();
+      vstep(u + 1, sL2);
+      prefetch(sQ2, sO2, sQ3, sO3);
+      end_half();
+      fetch(sQ1, sO1, sL1, sD1);
+      mstep(sQ2, sO2, sQ3, sO3, sD3);
+      end_half();
+      vstep(u + 2, sL3);
+      prefetch(sQ3, sO3, sQ0, sO0);
+      end_half();
+      fetch(sQ2, sO2, sL2, sD2);
+      mstep(sQ3, sO3, sQ0, sO0, sD0);
+      end_half();
+      vstep(u + 3, sL0);
+      prefetch(sQ0, sO0, sQ1, sO1);
+      end_half();
     }
-    if (u < T) { fetch(sQ3, sO3, sL3, sD3); mstep(sQ0, sO0, sQ1, sO1, sD1); end_half(); vstep(u, sL1); prefetch(sQ1, sO1, sQ2, sO2); end_half(); }
-    if (u + 1 < T) { fetch(sQ0, sO0, sL0, sD0); mstep(sQ1, sO1, sQ2, sO2, sD2); end_half(); vstep(u + 1, sL2); prefetch(sQ2, sO2, sQ3, sO3); end_half(); }
-    if (u + 2 < T) { fetch(sQ1, sO1, sL1, sD1); mstep(sQ2, sO2, sQ3, sO3, sD3); end_half(); vstep(u + 2, sL3); prefetch(sQ3, sO3, sQ0, sO0); end_half(); }
+    if (u < T) {
+      fetch(sQ3, sO3, sL3, sD3);
+      mstep(sQ0, sO0, sQ1, sO1, sD1);
+      end_half();
+      vstep(u, sL1);
+      prefetch(sQ1, sO1, sQ2, sO2);
+      end_half();
+    }
+    if (u + 1 < T) {
+      fetch(sQ0, sO0, sL0, sD0);
+      mstep(sQ1, sO1, sQ2, sO2, sD2);
+      end_half();
+      vstep(u + 1, sL2);
+      prefetch(sQ2, sO2, sQ3, sO3);
+      end_half();
+    }
+    if (u + 2 < T) {
+      fetch(sQ1, sO1, sL1, sD1);
+      mstep(sQ2, sO2, sQ3, sO3, sD3);
+      end_half();
+      vstep(u + 2, sL3);
+      prefetch(sQ3, sO3, sQ0, sO0);
+      end_half();
+    }
     end_half();
   } else {
     for (; u + 4 <= T; u += 4) {
-      fetch(sQ3, sO3, sL3, sD3); vstep(u - 1, sL0); prefetch(sQ0, sO0, sQ1, sO1); end_half(); mstep(sQ0, sO0, sQ1, sO1, sD1); end_half();
-      fetch(sQ0, sO0, sL0, sD0); vstep(u, sL1); prefetch(sQ1, sO1, sQ2, sO2); end_half(); mstep(sQ1, sO1, sQ2, sO2, sD2); end_half();
-      fetch(sQ1, sO1, sL1, sD1); vstep(u + 1, sL2); prefetch(sQ2, sO2, sQ3, sO3); end_half(); mstep(sQ2, sO2, sQ3, sO3, sD3); end_half();
-      fetch(sQ2, sO2, sL2, sD2); vstep(u + 2, sL3); prefetch(sQ3, sO3, sQ0, sO0); end_half(); mstep(sQ3, sO3, sQ0, sO0, sD0); end_half();
+      fetch(sQ3, sO3, sL3, sD3);
+      vstep(u - 1, sL0);
+      prefetch(sQ0, sO0, sQ1, sO1);
+      end_half();
+      mstep(sQ0, sO0, sQ1, sO1, sD1);
+      end_half();
+      fetch(sQ0, sO0, sL0, sD0);
+      vstep(u, sL1);
+      prefetch(sQ1, sO1, sQ2, sO2);
+      end_half();
+      mstep(sQ1, sO1, sQ2, sO2, sD2);
+      end_half();
+      fetch(sQ1, sO1, sL1, sD1);
+      vstep(u + 1, sL2);
+      prefetch(sQ2, sO2, sQ3, sO3);
+      end_half();
+      mstep(sQ2, sO2, sQ3, sO3, sD3);
+      end_half();
+      fetch(sQ2, sO2, sL2, sD2);
+      vstep(u + 2, sL3);
+      prefetch(sQ3, sO3, sQ0, sO0);
+      end_half();
+      mstep(sQ3, sO3, sQ0, sO0, sD0);
+      end_half();
     }
-    if (u < T) { fetch(sQ3, sO3, sL3, sD3); vstep(u - 1, sL0); prefetch(sQ0, sO0, sQ1, sO1); end_half(); mstep(sQ0, sO0, sQ1, sO1, sD1); end_half(); }
-    if (u + 1 < T) { fetch(sQ0, sO0, sL0, sD0); vstep(u, sL1); prefetch(sQ1, sO1, sQ2, sO2); end_half(); mstep(sQ1, sO1, sQ2, sO2, sD2); end_half(); }
-    if (u + 2 < T) { fetch(sQ1, sO1, sL1, sD1); vstep(u + 1, sL2); prefetch(sQ2, sO2, sQ3, sO3); end_half(); mstep(sQ2, sO2, sQ3, sO3, sD3); end_half(); }
+    if (u < T) {
+      fetch(sQ3, sO3, sL3, sD3);
+      vstep(u - 1, sL0);
+      prefetch(sQ0, sO0, sQ1, sO1);
+      end_half();
+      mstep(sQ0, sO0, sQ1, sO1, sD1);
+      end_half();
+    }
+    if (u + 1 < T) {
+      fetch(sQ0, sO0, sL0, sD0);
+      vstep(u, sL1);
+      prefetch(sQ1, sO1, sQ2, sO2);
+      end_half();
+      mstep(sQ1, sO1, sQ2, sO2, sD2);
+      end_half();
+    }
+    if (u + 2 < T) {
+      fetch(sQ1, sO1, sL1, sD1);
+      vstep(u + 1, sL2);
+      prefetch(sQ2, sO2, sQ3, sO3);
+      end_half();
+      mstep(sQ2, sO2, sQ3, sO3, sD3);
+      end_half();
+    }
     end_half();
   }
   __builtin_amdgcn_s_waitcnt(0);  // no load may land after the workgroup ends
@@ -1555,14 +1639,55 @@ __global__ __launch_bounds__(2 * NG * 64, 2) void bwd_dq_pp_kernel(BwdKParams p)
     const int Tg = p.causal ? min(T, (q0 + 32 * NG - 1) / BC - t_lo + 1) : T;
     prefetch(sK0, sK1, sV1);
     for (; u + 4 <= Tg; u += 4) {
-      fetch(u, sK3, sV3); mstep(sK0, sK1, sV1); end_half(); vstep(u, Tg); prefetch(sK1, sK2, sV2); end_half();
-      fetch(u + 1, sK0, sV0); mstep(sK1, sK2, sV2); end_half(); vstep(u + 1, Tg); prefetch(sK2, sK3, sV3); end_half();
-      fetch(u + 2, sK1, sV1); mstep(sK2, sK3, sV3); end_half(); vstep(u + 2, Tg); prefetch(sK3, sK0, sV0); end_half();
-      fetch(u + 3, sK2, sV2); mstep(sK3, sK0, sV0); end_half(); vstep(u + 3, Tg); prefetch(sK0, sK1, sV1); end_half();
+      fetch(u, sK3, sV3);
+      mstep(sK0, sK1, sV1);
+      end_half();
+      vstep(u, Tg);
+      prefetch(sK1, sK2, sV2);
+      end_half();
+      fetch(u + 1, sK0, sV0);
+      mstep(sK1, sK2, sV2);
+      end_half();
+      vstep(u + 1, Tg);
+      prefetch(sK2, sK3, sV3);
+      end_half();
+      fetch(u + 2, sK1, sV1);
+      mstep(sK2, sK3, sV3);
+      end_half();
+      vstep(u + 2, Tg);
+      prefetch(sK3, sK0, sV0);
+      end_half();
+      fetch(u + 3, sK2, sV2);
+      mstep(sK3, sK0, sV0);
+      end_half();
+      vstep(u + 3, Tg);
+      prefetch(sK0, sK1, sV1);
+      end_half();
     }
-    if (u < Tg) { fetch(u, sK3, sV3); mstep(sK0, sK1, sV1); end_half(); vstep(u, Tg); prefetch(sK1, sK2, sV2); end_half(); }
-    if (u + 1 < Tg) { fetch(u + 1, sK0, sV0); mstep(sK1, sK2, sV2); end_half(); vstep(u + 1, Tg); prefetch(sK2, sK3, sV3); end_half(); }
-    if (u + 2 < Tg) { fetch(u + 2, sK1, sV1); mstep(sK2, sK3, sV3); end_half(); vstep(u + 2, Tg); prefetch(sK3, sK0, sV0); end_half(); }
+    if (u < Tg) {
+      fetch(u, sK3, sV3);
+      mstep(sK0, sK1, sV1);
+      end_half();
+      vstep(u, Tg);
+      prefetch(sK1, sK2, sV2);
+      end_half();
+    }
+    if (u + 1 < Tg) {
+      fetch(u + 1, sK0, sV0);
+      mstep(sK1, sK2, sV2);
+      end_half();
+      vstep(u + 1, Tg);
+      prefetch(sK2, sK3, sV3);
+      end_half();
+    }
+    if (u + 2 < Tg) {
+      fetch(u + 2, sK1, sV1);
+      mstep(sK2, sK3, sV3);
+      end_half();
+      vstep(u + 2, Tg);
+      prefetch(sK3, sK0, sV0);
+      end_half();
+    }
     for (u += (u < Tg) + (u + 1 < Tg) + (u + 2 < Tg); u < T; ++u) {
       if (u % 4 == 0) fetch(u, sK3, sV3);
       else if (u % 4 == 1) fetch(u, sK0, sV0);
@@ -1574,14 +1699,55 @@ __global__ __launch_bounds__(2 * NG * 64, 2) void bwd_dq_pp_kernel(BwdKParams p)
     end_half();
   } else {
     for (; u + 4 <= T; u += 4) {
-      fetch(u, sK3, sV3); vstep(u - 1, T); prefetch(sK0, sK1, sV1); end_half(); mstep(sK0, sK1, sV1); end_half();
-      fetch(u + 1, sK0, sV0); vstep(u, T); prefetch(sK1, sK2, sV2); end_half(); mstep(sK1, sK2, sV2); end_half();
-      fetch(u + 2, sK1, sV1); vstep(u + 1, T); prefetch(sK2, sK3, sV3); end_half(); mstep(sK2, sK3, sV3); end_half();
-      fetch(u + 3, sK2, sV2); vstep(u + 2, T); prefetch(sK3, sK0, sV0); end_half(); mstep(sK3, sK0, sV0); end_half();
+      fetch(u, sK3, sV3);
+      vstep(u - 1, T);
+      prefetch(sK0, sK1, sV1);
+      end_half();
+      mstep(sK0, sK1, sV1);
+      end_half();
+      fetch(u + 1, sK0, sV0);
+      vstep(u, T);
+      prefetch(sK1, sK2, sV2);
+      end_half();
+      mstep(sK1, sK2, sV2);
+      end_half();
+      fetch(u + 2, sK1, sV1);
+      vstep(u + 1, T);
+      prefetch(sK2, sK3, sV3);
+      end_half();
+      mstep(sK2, sK3, sV3);
+      end_half();
+      fetch(u + 3, sK2, sV2);
+      vstep(u + 2, T);
+      prefetch(sK3, sK0, sV0);
+      end_half();
+      mstep(sK3, sK0, sV0);
+      end_half();
     }
-    if (u < T) { fetch(u, sK3, sV3); vstep(u - 1, T); prefetch(sK0, sK1, sV1); end_half(); mstep(sK0, sK1, sV1); end_half(); }
-    if (u + 1 < T) { fetch(u + 1, sK0, sV0); vstep(u, T); prefetch(sK1, sK2, sV2); end_half(); mstep(sK1, sK2, sV2); end_half(); }
-    if (u + 2 < T) { fetch(u + 2, sK1, sV1); vstep(u + 1, T); prefetch(sK2, sK3, sV3); end_half(); mstep(sK2, sK3, sV3); end_half(); }
+    if (u < T) {
+      fetch(u, sK3, sV3);
+      vstep(u - 1, T);
+      prefetch(sK0, sK1, sV1);
+      end_half();
+      mstep(sK0, sK1, sV1);
+      end_half();
+    }
+    if (u + 1 < T) {
+      fetch(u + 1, sK0, sV0);
+      vstep(u, T);
+      prefetch(sK1, sK2, sV2);
+      end_half();
+      mstep(sK1, sK2, sV2);
+      end_half();
+    }
+    if (u + 2 < T) {
+      fetch(u + 2, sK1, sV1);
+      vstep(u + 1, T);
+      prefetch(sK2, sK3, sV3);
+      end_half();
+      mstep(sK2, sK3, sV3);
+      end_half();
+    }
     end_half();
   }
   __builtin_amdgcn_s_waitcnt(0);  // no fetch may land after the workgroup ends

@@ -586,12 +586,41 @@ __global__ __launch_bounds__(2 * NG * 64, 2) void fwd_pp_kernel(FwdKParams p) {
     const int Tg = p.causal ? min(T, (q0 + 32 * NG - 1) / BC - t_lo + 1) : T;
     prefetch(sK1, sV0);
     for (; u + 3 <= Tg; u += 3) {
-      fetch(u, sK0, sV2); mstep(sK1, sV0); end_half(); vstep(u, Tg); prefetch(sK2, sV1); end_half();
-      fetch(u + 1, sK1, sV0); mstep(sK2, sV1); end_half(); vstep(u + 1, Tg); prefetch(sK0, sV2); end_half();
-      fetch(u + 2, sK2, sV1); mstep(sK0, sV2); end_half(); vstep(u + 2, Tg); prefetch(sK1, sV0); end_half();
+      fetch(u, sK0, sV2);
+      mstep(sK1, sV0);
+      end_half();
+      vstep(u, Tg);
+      prefetch(sK2, sV1);
+      end_half();
+      fetch(u + 1, sK1, sV0);
+      mstep(sK2, sV1);
+      end_half();
+      vstep(u + 1, Tg);
+      prefetch(sK0, sV2);
+      end_half();
+      fetch(u + 2, sK2, sV1);
+      mstep(sK0, sV2);
+      end_half();
+      vstep(u + 2, Tg);
+      prefetch(sK1, sV0);
+      end_half();
     }
-    if (u < Tg) { fetch(u, sK0, sV2); mstep(sK1, sV0); end_half(); vstep(u, Tg); prefetch(sK2, sV1); end_half(); }
-    if (u + 1 < Tg) { fetch(u + 1, sK1, sV0); mstep(sK2, sV1); end_half(); vstep(u + 1, Tg); prefetch(sK0, sV2); end_half(); }
+    if (u < Tg) {
+      fetch(u, sK0, sV2);
+      mstep(sK1, sV0);
+      end_half();
+      vstep(u, Tg);
+      prefetch(sK2, sV1);
+      end_half();
+    }
+    if (u + 1 < Tg) {
+      fetch(u + 1, sK1, sV0);
+      mstep(sK2, sV1);
+      end_half();
+      vstep(u + 1, Tg);
+      prefetch(sK0, sV2);
+      end_half();
+    }
     for (u += (u < Tg) + (u + 1 < Tg); u < T; ++u) {
       if (u % 3 == 0) fetch(u, sK0, sV2);
       else if (u % 3 == 1) fetch(u, sK1, sV0);
@@ -602,12 +631,41 @@ __global__ __launch_bounds__(2 * NG * 64, 2) void fwd_pp_kernel(FwdKParams p) {
     end_half();
   } else {
     for (; u + 3 <= T; u += 3) {
-      fetch(u, sK0, sV2); vstep(u - 1, T); prefetch(sK1, sV0); end_half(); mstep(sK1, sV0); end_half();
-      fetch(u + 1, sK1, sV0); vstep(u, T); prefetch(sK2, sV1); end_half(); mstep(sK2, sV1); end_half();
-      fetch(u + 2, sK2, sV1); vstep(u + 1, T); prefetch(sK0, sV2); end_half(); mstep(sK0, sV2); end_half();
+      fetch(u, sK0, sV2);
+      vstep(u - 1, T);
+      prefetch(sK1, sV0);
+      end_half();
+      mstep(sK1, sV0);
+      end_half();
+      fetch(u + 1, sK1, sV0);
+      vstep(u, T);
+      prefetch(sK2, sV1);
+      end_half();
+      mstep(sK2, sV1);
+      end_half();
+      fetch(u + 2, sK2, sV1);
+      vstep(u + 1, T);
+      prefetch(sK0, sV2);
+      end_half();
+      mstep(sK0, sV2);
+      end_half();
     }
-    if (u < T) { fetch(u, sK0, sV2); vstep(u - 1, T); prefetch(sK1, sV0); end_half(); mstep(sK1, sV0); end_half(); }
-    if (u + 1 < T) { fetch(u + 1, sK1, sV0); vstep(u, T); prefetch(sK2, sV1); end_half(); mstep(sK2, sV1); end_half(); }
+    if (u < T) {
+      fetch(u, sK0, sV2);
+      vstep(u - 1, T);
+      prefetch(sK1, sV0);
+      end_half();
+      mstep(sK1, sV0);
+      end_half();
+    }
+    if (u + 1 < T) {
+      fetch(u + 1, sK1, sV0);
+      vstep(u, T);
+      prefetch(sK2, sV1);
+      end_half();
+      mstep(sK2, sV1);
+      end_half();
+    }
     end_half();
   }
   __builtin_amdgcn_s_waitcnt(0);  // no fetch may land after the workgroup ends
