@@ -34,8 +34,8 @@
 //  * Workgroups are renumbered per XCD (whole heads per XCD, sharing K/V in
 //    that XCD's L2) and, with the causal mask, the longest query blocks run
 //    first.
-// fwd_bf16_kernel serves dropout; without dropout the forward runs
-// fwd_pp_kernel below, which keeps this mapping but separates each wave's
+// fwd_bf16_kernel serves dropout and grids of fewer than four 256-query
+// workgroups; otherwise the forward runs fwd_pp_kernel below, which keeps this mapping but separates each wave's
 // matrix and vector work into alternating half-steps (ping-pong).
 #include "attn_device.hpp"
 #include "attn_kernels.hpp"
@@ -737,6 +737,13 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream) {
   if (a.drop.thresh > 0) {
     if (a.d == 128) return launch_fwd_cfg<128, 4, 32, true>(a, stream);
     return launch_fwd_cfg<64, 4, 64, true>(a, stream);
+  }
+  // Grids of fewer than four 256-query workgroups (one short head, say):
+  // 128-query workgroups give twice the parallelism, and such a launch is
+  // bound by latency, not by the matrix cores.
+  if (a.BH * ((a.N + 255) / 256) < 4) {
+    if (a.d == 128) return launch_fwd_cfg<128, 4, 32, false>(a, stream);
+    return launch_fwd_cfg<64, 4, 64, false>(a, stream);
   }
   if (a.d == 128) return launch_fwd_pp<128, 32>(a, stream);
   return launch_fwd_pp<64, 64>(a, stream);

@@ -127,6 +127,19 @@ def test_long_context_causal_sampled(ea, window):
     assert np.isfinite(o).all() and np.isfinite(lse).all()
 
 
+@pytest.mark.parametrize("N,d", [(600, 128), (700, 64)])
+def test_small_grid_single_head(ea, N, d):
+    """One head short enough for fewer than four 256-query workgroups: the
+    forward then runs 128-query workgroups (causal, ragged tail)."""
+    log(f"case: B1 H1 N{N} d{d} causal (small grid)")
+    dev, ref = bf16_case(520 + N, 1, 1, N, d)
+    o, lse = ea.attn_fwd(dev["q"], dev["k"], dev["v"], causal=True)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.fwd(ref["q"], ref["k"], ref["v"], 1 / math.sqrt(d), True)
+    assert_close(o.float().cpu().numpy().astype(np.float64), o_ref, BF16_MAX, BF16_MEAN, "O")
+    assert_close(lse.cpu().numpy().astype(np.float64), lse_ref, LSE_MAX, None, "LSE")
+
+
 @pytest.mark.parametrize("d", [64, 128])
 def test_closed_form_invariants(ea, d):
     """Constant V -> O = V; window 1 -> O = V; identical keys -> running mean of
