@@ -14,10 +14,10 @@
   same indicators, fp64 central finite differences of sum(O * dO), and
   D_i = sum_k dO_ik O_ik.
 
-The 4x32 multipliers (0xD2511F53, 0xCD9E8D57) are the generator's published
-constants; the numpy pin covers the round structure and key schedule they
-run through, not their values.  The HIP side types them independently, so a
-wrong value in either copy fails the GPU parity tests.
+The 32-bit instance itself -- its multipliers, Weyl constants and word
+layout -- is pinned word for word against rocRAND's Philox-4x32-10 engine in
+test_oracle_philox_rocrand.py; the GPU parity tests then compare the
+kernels' keep bytes with the oracle's.
 """
 import math
 
