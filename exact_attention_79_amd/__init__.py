@@ -20,12 +20,13 @@ LIB_PATH = os.path.join(_HERE, "libattn.so")
 
 ATTN_OK, ATTN_EINVAL, ATTN_EUNSUPPORTED, ATTN_EHIP = 0, 1, 2, 3
 ATTN_OUT_BF16, ATTN_OUT_F32 = 0, 1
+STAGE_FWD, STAGE_BWD_DQ, STAGE_BWD_DKDV, STAGE_FWD_FP8 = 0, 1, 2, 3
 
 # Entry points declared in include/attn.h.
 EXPORTS = ("attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_bwd_preprocess",
            "attn_bwd_dkdv", "attn_bwd_dq", "attn_fwd_fp8", "attn_decode_workspace_bytes",
            "attn_fwd_decode", "attn_fwd_fp8_blocks", "attn_fwd_dropout", "attn_bwd_dropout",
-           "attn_status_str")
+           "attn_status_str", "attn_kernel_name")
 
 
 class AttnDesc(ctypes.Structure):
@@ -87,6 +88,8 @@ def _load():
     L.attn_fwd_dropout.restype = ctypes.c_int
     L.attn_bwd_dropout.argtypes = [dp, drp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.attn_bwd_dropout.restype = ctypes.c_int
+    L.attn_kernel_name.argtypes = [dp, i32, f32]
+    L.attn_kernel_name.restype = ctypes.c_char_p
     L.attn_status_str.argtypes = [ctypes.c_int]
     L.attn_status_str.restype = ctypes.c_char_p
     return L
@@ -97,6 +100,18 @@ lib = _load()
 
 def status_str(status: int) -> str:
     return lib.attn_status_str(int(status)).decode()
+
+
+def kernel_name(stage: int, B: int, H: int, N: int, d: int, causal: bool = False,
+                window: int = 0, H_kv: int = 0, dropout_p: float = 0.0) -> str:
+    """Symbol of the main kernel that an entry point launches for this shape
+    (stage: STAGE_FWD, STAGE_BWD_DQ, STAGE_BWD_DKDV or STAGE_FWD_FP8), as
+    profilers list it; nothing is launched."""
+    desc = make_desc(B, H, N, d, 1.0 / math.sqrt(d), causal, window, H_kv)
+    name = lib.attn_kernel_name(ctypes.byref(desc), int(stage), float(dropout_p))
+    if name is None:
+        raise ValueError("invalid shape, stage or dropout probability")
+    return name.decode()
 
 
 def make_desc(B: int, H: int, N: int, d: int, scale: float, causal: bool,
@@ -145,9 +160,7 @@ def _fwd_prep(q, k, v, scale, causal, window, out_dtype, return_lse, out, lse):
     _check_like(q, out_dtype, out=o)
     if return_lse and lse is None:
         lse = torch.empty((B, H, N), device=q.device, dtype=torch.float32)
-    if lse is not None and (not lse.is_cuda or lse.dtype != torch.float32
-                            or lse.shape != (B, H, N) or not lse.is_contiguous()):
-        raise ValueError("lse must be a contiguous fp32 device tensor [B, H, N]")
+    _check_lse(lse, (B, H, N))
     desc = make_desc(B, H, N, d, scale, causal, window, k.shape[1])
     od = ATTN_OUT_F32 if out_dtype == torch.float32 else ATTN_OUT_BF16
     return desc, o, lse, od
@@ -255,11 +268,18 @@ def _check_like(ref, dtype, **tensors):
                              f"of shape {tuple(ref.shape)}")
 
 
+def _check_lse(lse, shape):
+    """lse, when given, must be a contiguous fp32 device tensor of `shape`
+    (the kernels write every element of it)."""
+    if lse is not None and (not lse.is_cuda or lse.dtype != torch.float32
+                            or tuple(lse.shape) != tuple(shape) or not lse.is_contiguous()):
+        dims = ", ".join(str(x) for x in shape)
+        raise ValueError(f"lse must be a contiguous fp32 device tensor of shape [{dims}]")
+
+
 def _check_lse_ws(q, lse, workspace, desc):
     B, H, N, _ = q.shape
-    if (lse is not None and (not lse.is_cuda or lse.dtype != torch.float32
-                             or lse.shape != (B, H, N) or not lse.is_contiguous())):
-        raise ValueError("lse must be a contiguous fp32 device tensor [B, H, N]")
+    _check_lse(lse, (B, H, N))
     need = int(lib.attn_bwd_workspace_bytes(ctypes.byref(desc)))
     if workspace.numel() * workspace.element_size() < need or not workspace.is_cuda:
         raise ValueError(f"workspace must be a device tensor of >= {need} bytes")
@@ -345,9 +365,7 @@ def attn_fwd_fp8(q8, k8, v8, q_descale: float, k_descale: float, v_descale: floa
     _check_like(q8, out_dtype, out=o)
     if return_lse and lse is None:
         lse = torch.empty((B, H, N), device=q8.device, dtype=torch.float32)
-    if lse is not None and (not lse.is_cuda or lse.dtype != torch.float32
-                            or lse.shape != (B, H, N) or not lse.is_contiguous()):
-        raise ValueError("lse must be a contiguous fp32 device tensor [B, H, N]")
+    _check_lse(lse, (B, H, N))
     desc = make_desc(B, H, N, d, scale, causal, window, k8.shape[1])
     od = ATTN_OUT_F32 if out_dtype == torch.float32 else ATTN_OUT_BF16
     _check(lib.attn_fwd_fp8(ctypes.byref(desc), _ptr(q8), _ptr(k8), _ptr(v8),
@@ -389,9 +407,7 @@ def attn_fwd_decode(q, k, v, scale: float | None = None, causal: bool = False,
     _check_like(q, out_dtype, out=o)
     if return_lse and lse is None:
         lse = torch.empty((B, H, Nq), device=q.device, dtype=torch.float32)
-    if lse is not None and (not lse.is_cuda or lse.dtype != torch.float32
-                            or lse.shape != (B, H, Nq) or not lse.is_contiguous()):
-        raise ValueError("lse must be a contiguous fp32 device tensor [B, H, N_q]")
+    _check_lse(lse, (B, H, Nq))
     desc = make_decode_desc(B, H, Hkv, Nq, Nk, d, scale, causal, window)
     need = int(lib.attn_decode_workspace_bytes(ctypes.byref(desc)))
     if workspace is None:
@@ -428,6 +444,7 @@ def attn_fwd_fp8_blocks(q8, k8, v8, q_descales, k_descales, v_descales,
     _check_like(q8, out_dtype, out=o)
     if return_lse and lse is None:
         lse = torch.empty((B, H, N), device=q8.device, dtype=torch.float32)
+    _check_lse(lse, (B, H, N))
     desc = make_desc(B, H, N, d, scale, causal, window, Hkv)
     od = ATTN_OUT_F32 if out_dtype == torch.float32 else ATTN_OUT_BF16
     _check(lib.attn_fwd_fp8_blocks(ctypes.byref(desc), _ptr(q8), _ptr(k8), _ptr(v8),

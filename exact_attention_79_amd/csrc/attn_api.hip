@@ -333,6 +333,32 @@ attn_status attn_fwd_decode(const attn_decode_desc* desc, const void* q, const v
   return from_hip(attn::launch_decode(a, (hipStream_t)stream));
 }
 
+const char* attn_kernel_name(const attn_desc* desc, int32_t stage, float dropout_p) {
+  if (check_desc(desc) != ATTN_OK) return nullptr;
+  attn::DropoutArgs drop{0u, 0u, 0ull};
+  if (dropout_p != 0.f) {
+    const attn_dropout dd{dropout_p, 0u, 0ull};
+    if (dropout_args(&dd, &drop) != ATTN_OK || stage == ATTN_STAGE_FWD_FP8) return nullptr;
+  }
+  // Any aligned non-null stand-in: nothing is launched or dereferenced.
+  void* x = (void*)(uintptr_t)256;
+  const char* name = nullptr;
+  hipError_t e = hipErrorInvalidValue;
+  if (stage == ATTN_STAGE_FWD || stage == ATTN_STAGE_FWD_FP8) {
+    attn::FwdArgs a = fwd_args(desc, x, x, x, x, ATTN_OUT_BF16, nullptr);
+    a.drop = drop;
+    e = stage == ATTN_STAGE_FWD ? attn::launch_fwd_bf16(a, nullptr, &name)
+                                : attn::launch_fwd_fp8(a, nullptr, &name);
+  } else if (stage == ATTN_STAGE_BWD_DQ || stage == ATTN_STAGE_BWD_DKDV) {
+    attn::BwdArgs a = bwd_args(desc, x, x, x, x, x, (const float*)x, (float*)x, (float*)x,
+                               (float*)x, x);
+    a.drop = drop;
+    e = stage == ATTN_STAGE_BWD_DQ ? attn::launch_bwd_dq(a, nullptr, &name)
+                                   : attn::launch_bwd_dkdv(a, nullptr, &name);
+  }
+  return e == hipSuccess ? name : nullptr;
+}
+
 const char* attn_status_str(attn_status s) {
   switch (s) {
     case ATTN_OK:

@@ -1816,37 +1816,41 @@ hipError_t launch_bwd_preprocess(const BwdArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream) {
+hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream, const char** name) {
   BwdKParams p = bwd_params(a, 32 * kBwdWaves);
   // One workgroup per key block of every key/value head and share of its group.
   const int BHkv = a.BH / a.H * a.Hkv;
   p.split = dkdv_split(BHkv, a.H / a.Hkv, a.N, a.d, a.causal);
   const dim3 grid((unsigned)(BHkv * p.n_tiles * p.split)), block(64 * kBwdWaves);
   const bool drop = a.drop.thresh > 0;
+  constexpr int W = kBwdWaves;
+  hipError_t e;
   if (a.d == 128 && drop)
-    hipLaunchKernelGGL((bwd_dkdv_kernel<128, kBwdWaves, kDropQTile, true>), grid, block, 0,
-                       stream, p);
+    e = go<bwd_dkdv_kernel<128, W, kDropQTile, true>>(
+        name, kname("attn::bwd_dkdv_kernel", 128, W, kDropQTile, true), grid, block, stream, p);
   else if (a.d == 128)
-    hipLaunchKernelGGL((bwd_dkdv_pair_kernel<128, kBwdWaves>), grid, dim3(2 * 64 * kBwdWaves),
-                       0, stream, p);
+    e = go<bwd_dkdv_pair_kernel<128, W>>(name, kname("attn::bwd_dkdv_pair_kernel", 128, W),
+                                         grid, dim3(2 * 64 * W), stream, p);
   else if (drop)
-    hipLaunchKernelGGL((bwd_dkdv_kernel<64, kBwdWaves, kDropQTile, true>), grid, block, 0,
-                       stream, p);
+    e = go<bwd_dkdv_kernel<64, W, kDropQTile, true>>(
+        name, kname("attn::bwd_dkdv_kernel", 64, W, kDropQTile, true), grid, block, stream, p);
   else if (a.causal)
-    hipLaunchKernelGGL((bwd_dkdv_kernel<64, kBwdWaves, dkdv_qtile<64>(), false>), grid,
-                       block, 0, stream, p);
+    e = go<bwd_dkdv_kernel<64, W, dkdv_qtile<64>(), false>>(
+        name, kname("attn::bwd_dkdv_kernel", 64, W, dkdv_qtile<64>(), false), grid, block,
+        stream, p);
   else {
     // d = 64 without dropout or causal mask: the ping-pong kernel, 256 keys
     // per workgroup (the same shares of the group, so the same workspace).
     // Under the causal mask its second group would compute four query tiles
     // its keys cannot see (measured 0.5-1.5 % slower), so causal launches keep
     // the kernel above.
-    BwdKParams pp = bwd_params(a, 64 * kBwdWaves);
+    BwdKParams pp = bwd_params(a, 64 * W);
     pp.split = p.split;
-    hipLaunchKernelGGL((bwd_dkdv_pp_kernel<64, kBwdWaves>),
-                       dim3((unsigned)(BHkv * pp.n_tiles * pp.split)), dim3(2 * 64 * kBwdWaves), 0,
-                       stream, pp);
+    e = go<bwd_dkdv_pp_kernel<64, W>>(name, kname("attn::bwd_dkdv_pp_kernel", 64, W),
+                                      dim3((unsigned)(BHkv * pp.n_tiles * pp.split)),
+                                      dim3(2 * 64 * W), stream, pp);
   }
+  if (name || e != hipSuccess) return e;
   if (p.split > 1) {
     const size_t n4 = (size_t)BHkv * a.N * a.d / 4;
     const unsigned sum_grid = (unsigned)std::min<size_t>((n4 + 255) / 256, 8192);
@@ -1858,23 +1862,25 @@ hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream) {
+hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream, const char** name) {
   const BwdKParams p = bwd_params(a, 32 * kBwdWaves);
   const dim3 grid((unsigned)(a.BH * p.n_tiles)), block(64 * kBwdWaves);
   const bool drop = a.drop.thresh > 0;
+  constexpr int W = kBwdWaves;
   if (a.d == 128 && drop)
-    hipLaunchKernelGGL((bwd_dq_kernel<128, kBwdWaves, 32, true>), grid, block, 0, stream, p);
-  else if (a.d == 128) {
-    const BwdKParams pp = bwd_params(a, 64 * kBwdWaves);
-    hipLaunchKernelGGL((bwd_dq_pp_kernel<128, kBwdWaves>), dim3((unsigned)(a.BH * pp.n_tiles)),
-                       dim3(2 * 64 * kBwdWaves), 0, stream, pp);
+    return go<bwd_dq_kernel<128, W, 32, true>>(name, kname("attn::bwd_dq_kernel", 128, W, 32, true),
+                                               grid, block, stream, p);
+  if (a.d == 128) {
+    const BwdKParams pp = bwd_params(a, 64 * W);
+    return go<bwd_dq_pp_kernel<128, W>>(name, kname("attn::bwd_dq_pp_kernel", 128, W),
+                                        dim3((unsigned)(a.BH * pp.n_tiles)), dim3(2 * 64 * W),
+                                        stream, pp);
   }
-  else if (drop)
-    hipLaunchKernelGGL((bwd_dq_kernel<64, kBwdWaves, 64, true>), grid, block, 0, stream, p);
-  else
-    hipLaunchKernelGGL((bwd_dq_kernel<64, kBwdWaves, 64, false>), grid, block, 0, stream,
-                       p);
-  return hipGetLastError();
+  if (drop)
+    return go<bwd_dq_kernel<64, W, 64, true>>(name, kname("attn::bwd_dq_kernel", 64, W, 64, true),
+                                              grid, block, stream, p);
+  return go<bwd_dq_kernel<64, W, 64, false>>(name, kname("attn::bwd_dq_kernel", 64, W, 64, false),
+                                             grid, block, stream, p);
 }
 
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {

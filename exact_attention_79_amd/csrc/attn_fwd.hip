@@ -714,39 +714,38 @@ static FwdKParams fwd_params(const FwdArgs& a, int rows) {
 }
 
 template <int D, int NW, int BC, bool DROP>
-static hipError_t launch_fwd_cfg(const FwdArgs& a, hipStream_t stream) {
+static hipError_t launch_fwd_cfg(const FwdArgs& a, hipStream_t stream, const char** name) {
   const FwdKParams p = fwd_params(a, 32 * NW);
   const unsigned grid = (unsigned)(a.BH * p.n_qtiles);
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, BC, DROP>), dim3(grid), dim3(NW * 64), 0,
-                     stream, p);
-  return hipGetLastError();
+  return go<fwd_bf16_kernel<D, NW, BC, DROP>>(name, kname("attn::fwd_bf16_kernel", D, NW, BC, DROP),
+                                              dim3(grid), dim3(NW * 64), stream, p);
 }
 
 // Without dropout: the ping-pong kernel (two groups of 4 waves), 32-key tiles
 // at d = 128 and 64-key tiles at d = 64.
 template <int D, int BC>
-static hipError_t launch_fwd_pp(const FwdArgs& a, hipStream_t stream) {
+static hipError_t launch_fwd_pp(const FwdArgs& a, hipStream_t stream, const char** name) {
   constexpr int NG = 4;
   const FwdKParams p = fwd_params(a, 64 * NG);
-  hipLaunchKernelGGL((fwd_pp_kernel<D, NG, BC>), dim3((unsigned)(a.BH * p.n_qtiles)),
-                     dim3(2 * NG * 64), 0, stream, p);
-  return hipGetLastError();
+  return go<fwd_pp_kernel<D, NG, BC>>(name, kname("attn::fwd_pp_kernel", D, NG, BC),
+                                      dim3((unsigned)(a.BH * p.n_qtiles)), dim3(2 * NG * 64),
+                                      stream, p);
 }
 
-hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream) {
+hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream, const char** name) {
   if (a.drop.thresh > 0) {
-    if (a.d == 128) return launch_fwd_cfg<128, 4, 32, true>(a, stream);
-    return launch_fwd_cfg<64, 4, 64, true>(a, stream);
+    if (a.d == 128) return launch_fwd_cfg<128, 4, 32, true>(a, stream, name);
+    return launch_fwd_cfg<64, 4, 64, true>(a, stream, name);
   }
   // Grids of fewer than four 256-query workgroups (one short head, say):
   // 128-query workgroups give twice the parallelism, and such a launch is
   // bound by latency, not by the matrix cores.
   if (a.BH * ((a.N + 255) / 256) < 4) {
-    if (a.d == 128) return launch_fwd_cfg<128, 4, 32, false>(a, stream);
-    return launch_fwd_cfg<64, 4, 64, false>(a, stream);
+    if (a.d == 128) return launch_fwd_cfg<128, 4, 32, false>(a, stream, name);
+    return launch_fwd_cfg<64, 4, 64, false>(a, stream, name);
   }
-  if (a.d == 128) return launch_fwd_pp<128, 32>(a, stream);
-  return launch_fwd_pp<64, 64>(a, stream);
+  if (a.d == 128) return launch_fwd_pp<128, 32>(a, stream, name);
+  return launch_fwd_pp<64, 64>(a, stream, name);
 }
 
 }  // namespace attn

@@ -433,7 +433,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8_kernel(FwdFp8Params p) {
 }
 
 template <int D>
-static hipError_t launch_fp8_d(const FwdArgs& a, hipStream_t stream) {
+static hipError_t launch_fp8_d(const FwdArgs& a, hipStream_t stream, const char** name) {
   constexpr int NW = 4;
   FwdFp8Params p;
   p.q = (const uint8_t*)a.q;
@@ -457,16 +457,15 @@ static hipError_t launch_fp8_d(const FwdArgs& a, hipStream_t stream) {
   p.out_f32 = a.out_f32;
   const unsigned grid = (unsigned)(a.BH * p.n_qtiles);
   if (a.q_scales)
-    hipLaunchKernelGGL((fwd_fp8_kernel<D, NW, true>), dim3(grid), dim3(NW * 64), 0, stream, p);
-  else
-    hipLaunchKernelGGL((fwd_fp8_kernel<D, NW, false>), dim3(grid), dim3(NW * 64), 0, stream,
-                       p);
-  return hipGetLastError();
+    return go<fwd_fp8_kernel<D, NW, true>>(name, kname("attn::fwd_fp8_kernel", D, NW, true),
+                                           dim3(grid), dim3(NW * 64), stream, p);
+  return go<fwd_fp8_kernel<D, NW, false>>(name, kname("attn::fwd_fp8_kernel", D, NW, false),
+                                          dim3(grid), dim3(NW * 64), stream, p);
 }
 
-hipError_t launch_fwd_fp8(const FwdArgs& a, hipStream_t stream) {
-  if (a.d == 128) return launch_fp8_d<128>(a, stream);
-  return launch_fp8_d<64>(a, stream);
+hipError_t launch_fwd_fp8(const FwdArgs& a, hipStream_t stream, const char** name) {
+  if (a.d == 128) return launch_fp8_d<128>(a, stream, name);
+  return launch_fp8_d<64>(a, stream, name);
 }
 
 }  // namespace attn

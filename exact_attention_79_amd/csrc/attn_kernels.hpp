@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <string>
+
 namespace attn {
 
 // Dropout on P for the bf16 forward and backward (thresh = 0: none).
@@ -91,14 +93,59 @@ inline int dkdv_split(int BHkv, int G, int N, int d, int causal) {
   return G;
 }
 
-hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream);
+// The symbol of a kernel instance as profilers list it, "attn::name<a, b>".
+struct KName {
+  const char* base;
+  int n;
+  int v[4];
+  bool is_bool[4];
+};
+inline void kname_put(KName& k, int v) { k.is_bool[k.n] = false, k.v[k.n++] = v; }
+inline void kname_put(KName& k, bool v) { k.is_bool[k.n] = true, k.v[k.n++] = v; }
+template <typename... T>
+inline KName kname(const char* base, T... t) {
+  static_assert(sizeof...(T) <= 4, "at most four template arguments");
+  KName k{base, 0, {}, {}};
+  (kname_put(k, t), ...);
+  return k;
+}
+inline std::string kname_str(const KName& k) {
+  std::string s = k.base;
+  s += '<';
+  for (int i = 0; i < k.n; ++i) {
+    if (i) s += ", ";
+    s += k.is_bool[i] ? (k.v[i] ? "true" : "false") : std::to_string(k.v[i]);
+  }
+  return s + '>';
+}
+
+// Launches kernel K, or, when `name` is not null, launches nothing and
+// returns the kernel's symbol there instead (static storage).  Each launch
+// site states its kernel's template arguments once more in `sym`, on the
+// same line as K.
+template <auto K, typename... Args>
+hipError_t go(const char** name, const KName& sym, dim3 grid, dim3 block, hipStream_t stream,
+              Args... args) {
+  if (name) {
+    static const std::string s = kname_str(sym);
+    *name = s.c_str();
+    return hipSuccess;
+  }
+  hipLaunchKernelGGL(K, grid, block, 0, stream, args...);
+  return hipGetLastError();
+}
+
+// Every launch function enqueues its kernels on `stream`; with `name` set it
+// only reports the symbol of its main kernel (the one that does the
+// attention arithmetic) for these arguments.
+hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream, const char** name = nullptr);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
-hipError_t launch_fwd_fp8(const FwdArgs& a, hipStream_t stream);
+hipError_t launch_fwd_fp8(const FwdArgs& a, hipStream_t stream, const char** name = nullptr);
 // The backward stages; launch_bwd = dq (which also fills the workspace),
 // then dkdv.  preprocess fills the workspace on its own.
 hipError_t launch_bwd_preprocess(const BwdArgs& a, hipStream_t stream);
-hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream);
-hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream);
+hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream, const char** name = nullptr);
+hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream, const char** name = nullptr);
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream);
 
 }  // namespace attn

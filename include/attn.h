@@ -248,6 +248,24 @@ attn_status attn_bwd_dropout(const attn_desc* desc, const attn_dropout* drop,
                              float* dv, void* workspace, size_t workspace_bytes,
                              void* stream);
 
+/* Which kernel an entry point runs (for matching profiler traces).  Returns
+ * the symbol of the main kernel -- the one that does the attention
+ * arithmetic -- that the entry point of `stage` launches for `desc`, as
+ * profilers list it (for example "attn::fwd_pp_kernel<128, 4, 32>"):
+ *   ATTN_STAGE_FWD      attn_fwd (dropout_p = 0) or attn_fwd_dropout
+ *   ATTN_STAGE_BWD_DQ   attn_bwd_dq, the dQ pass of attn_bwd / attn_bwd_dropout
+ *   ATTN_STAGE_BWD_DKDV attn_bwd_dkdv, the dK/dV pass of the same
+ *   ATTN_STAGE_FWD_FP8  attn_fwd_fp8 (dropout_p must be 0)
+ * Nothing is launched.  Static storage, valid until the process ends; NULL
+ * for an invalid desc, stage or dropout_p (rules as the entry points). */
+typedef enum {
+  ATTN_STAGE_FWD = 0,
+  ATTN_STAGE_BWD_DQ = 1,
+  ATTN_STAGE_BWD_DKDV = 2,
+  ATTN_STAGE_FWD_FP8 = 3
+} attn_stage;
+const char* attn_kernel_name(const attn_desc* desc, int32_t stage, float dropout_p);
+
 /* Static, human-readable text for a status code. */
 const char* attn_status_str(attn_status status);
 

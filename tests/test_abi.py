@@ -29,7 +29,7 @@ def test_header_declares_the_boundary():
         ["attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_bwd_preprocess",
          "attn_bwd_dkdv", "attn_bwd_dq", "attn_fwd_fp8", "attn_decode_workspace_bytes",
          "attn_fwd_decode", "attn_fwd_fp8_blocks", "attn_fwd_dropout", "attn_bwd_dropout",
-         "attn_status_str"])
+         "attn_status_str", "attn_kernel_name"])
 
 
 def test_library_exports_every_declared_symbol(ea):
@@ -227,3 +227,62 @@ def test_decode_rejects_small_workspace_and_null_pointers(ea):
                                   None) == ea.ATTN_EINVAL
     assert ea.lib.attn_fwd_decode(ctypes.byref(desc), f, f, f, f, 5, None, f, ws,
                                   None) == ea.ATTN_EINVAL
+
+
+@pytest.mark.parametrize("stage,B,H,N,d,causal,p,expect", [
+    (0, 4, 16, 2048, 128, False, 0.0, "attn::fwd_pp_kernel<128, 4, 32>"),
+    (0, 4, 16, 2048, 64, True, 0.0, "attn::fwd_pp_kernel<64, 4, 64>"),
+    (0, 1, 1, 256, 64, False, 0.0, "attn::fwd_bf16_kernel<64, 4, 64, false>"),
+    (0, 4, 16, 2048, 128, False, 0.1, "attn::fwd_bf16_kernel<128, 4, 32, true>"),
+    (1, 4, 16, 2048, 128, True, 0.0, "attn::bwd_dq_pp_kernel<128, 4>"),
+    (1, 4, 16, 2048, 64, True, 0.0, "attn::bwd_dq_kernel<64, 4, 64, false>"),
+    (1, 4, 16, 2048, 64, True, 0.1, "attn::bwd_dq_kernel<64, 4, 64, true>"),
+    (2, 4, 16, 2048, 128, False, 0.0, "attn::bwd_dkdv_pair_kernel<128, 4>"),
+    (2, 4, 16, 2048, 64, False, 0.0, "attn::bwd_dkdv_pp_kernel<64, 4>"),
+    (2, 4, 16, 2048, 64, True, 0.0, "attn::bwd_dkdv_kernel<64, 4, 32, false>"),
+    (2, 4, 16, 2048, 128, True, 0.1, "attn::bwd_dkdv_kernel<128, 4, 32, true>"),
+    (3, 2, 32, 8192, 128, False, 0.0, "attn::fwd_fp8_kernel<128, 4, false>"),
+])
+def test_kernel_name_follows_the_dispatch(ea, stage, B, H, N, d, causal, p, expect):
+    """The name query walks the same dispatch as the launch, without launching."""
+    assert ea.kernel_name(stage, B, H, N, d, causal, dropout_p=p) == expect
+
+
+def test_kernel_name_rejects_invalid_queries(ea):
+    with pytest.raises(ValueError):
+        ea.kernel_name(0, 1, 1, 64, 96)             # unsupported head dim
+    with pytest.raises(ValueError):
+        ea.kernel_name(7, 1, 1, 64, 64)             # no such stage
+    with pytest.raises(ValueError):
+        ea.kernel_name(3, 1, 1, 64, 128, dropout_p=0.1)  # fp8 has no dropout
+    with pytest.raises(ValueError):
+        ea.kernel_name(0, 1, 1, 64, 64, dropout_p=2.0)
+
+
+class _FakeDeviceTensor:
+    """Metadata-only stand-in for a device tensor (no GPU needed)."""
+
+    def __init__(self, shape, dtype, contiguous=True):
+        self.shape, self.dtype, self._c, self.is_cuda = tuple(shape), dtype, contiguous, True
+
+    def is_contiguous(self):
+        return self._c
+
+
+def test_lse_check_shared_by_every_forward(ea):
+    """Every forward entry (bf16, fp8, fp8 blocks, decode, and the backward's
+    lse argument) goes through one lse check: shape, dtype and layout."""
+    import inspect
+    import torch
+    ok = _FakeDeviceTensor((2, 3, 100), torch.float32)
+    ea._check_lse(ok, (2, 3, 100))
+    ea._check_lse(None, (2, 3, 100))
+    for bad in (_FakeDeviceTensor((2, 3, 99), torch.float32),
+                _FakeDeviceTensor((2, 3, 100), torch.bfloat16),
+                _FakeDeviceTensor((2, 3, 100), torch.float32, contiguous=False),
+                _FakeDeviceTensor((6, 100), torch.float32)):
+        with pytest.raises(ValueError):
+            ea._check_lse(bad, (2, 3, 100))
+    for fn in (ea._fwd_prep, ea.attn_fwd_fp8, ea.attn_fwd_fp8_blocks, ea.attn_fwd_decode,
+               ea._check_lse_ws):
+        assert "_check_lse(lse" in inspect.getsource(fn), fn.__name__
