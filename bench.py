@@ -1,25 +1,27 @@
 #!/usr/bin/env python3
 """Throughput of the exact-attention hot path on one MI355X.
 
-One step = every entry point of the library once over one batch of seeded
-synthetic inputs of the B=4, H=16, N=2048 sweep: for d in {64, 128} and for
-non-causal and causal masks, the bf16 forward (attn_fwd) and the two
-backward stages that attn_bwd enqueues (attn_bwd_dq, attn_bwd_dkdv), plus the
-fp8 forward (attn_fwd_fp8) at d=128 non-causal.  Inputs are resident in HBM
-before timing starts; outputs are preallocated.
+One step = the bf16 forward and backward of the long-context workload
+B=1, H=32, N=16384, d=128 with the causal mask and without it: for each
+mask, attn_fwd and the two backward stages that attn_bwd enqueues
+(attn_bwd_dq, then attn_bwd_dkdv).  Inputs are seeded synthetic N(0,1)
+values rounded to bf16, resident in HBM before timing starts; outputs are
+preallocated.
 
-value = credited FLOPs per step / step time, with the usual convention:
-forward 4*B*H*N^2*d (halved for causal), backward 2.5x the forward, fp8
-forward 4*B*H*N^2*d.  Each kernel launch is bracketed by HIP events on the
-stream it runs on; the dominant kernel (most GPU time per step) is reported
-against its roofline.  The fp64 CPU oracle is timed on a bounded sample of
-the same workload as a reference point (rank 0 only).
+value = credited FLOPs per step / step time, with the metric's convention:
+forward 4*B*H*N^2*d (halved for causal), backward 2.5x the forward.  Each
+kernel launch is bracketed by HIP events on the stream it runs on; the
+dominant kernel (most GPU time per step) is reported against its roofline
+(credited FLOPs per launch over its average launch time).  Launch labels
+name the kernel each entry point runs, as the library reports it
+(attn_kernel_name).  The fp64 CPU oracle is timed on a bounded sample of the
+same workload as a reference point.
 
 After the timed step, with their own HIP-event timing and outside `value`:
-grouped-query attention (`gqa`), decode (`decode`, against HBM), dropout
-(`dropout`, beside the same calls without it) and every workload of the
-metric (`configs`: single head, long-context causal and window, the
-N >= 4096 forward/backward points, fp8); --no-extra-paths skips them.
+the fp8 forward (`fp8`, against the fp8 peak), grouped-query attention
+(`gqa`), decode (`decode`, against HBM), dropout (`dropout`, beside the same
+calls without it) and every other workload of the metric (`configs`);
+--no-extra-paths skips them.
 
 The roofline's "traffic" (HBM bytes per launch of the dominant kernel) is
 read from the rocprofv3 counter summary committed under profiles/, and only
@@ -43,15 +45,16 @@ import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(ROOT, "exact_attention_79_amd", "csrc")
-TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "hbm_traffic_B4H16N2048.md")
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "hbm_traffic_B1H32N16384.md")
 
 METRIC = "attention fwd/bwd TFLOPS (bf16, causal & non-causal) and % of MFMA peak"
 # MI355X dense peaks: 256 CUs x 2.4 GHz x (4096 bf16 | 8192 fp8) flop/clk/CU.
 PEAK_BF16_TFLOPS = 2516.6
 PEAK_FP8_TFLOPS = 5033.2
 HBM_GBPS = 8000.0
-# The fp8 forward joins the step once its kernel is built into the library.
-INCLUDE_FP8 = True
+# The timed workload: long-context, d = 128 (the targets are stated for
+# N >= 4096, d = 128); seeds of the long-context workload (number 3).
+STEP_B, STEP_H, STEP_N, STEP_D, STEP_SEEDS = 1, 32, 16384, 128, 3
 
 
 def visible_pairs(N: int, causal: bool, window: int) -> int:
@@ -76,11 +79,12 @@ def parse_args():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra-paths", action="store_true",
-                    help="skip the grouped-query, decode and dropout measurements that follow the "
-                         "timed step (for profiler runs that should see the step only)")
+                    help="skip the fp8, grouped-query, decode, dropout and per-workload "
+                         "measurements that follow the timed step (for profiler runs "
+                         "that should see the step only)")
     ap.add_argument("--hbm-copy-mib", type=int, default=0,
                     help="after timing, one fp32 -> bf16 copy of this many MiB of "
                          "fp32 (counter calibration for rocprofv3 --pmc runs)")
@@ -126,70 +130,56 @@ class Launch:
 
 def build_step(ea, torch, attn_synth):
     """All launches of one step, with inputs resident on the device."""
-    B, H, N = 4, 16, 2048
+    import numpy as np
+    B, H, N, d = STEP_B, STEP_H, STEP_N, STEP_D
     BH = B * H
     launches = []
 
     def dev_bf16(bits):
-        import numpy as np
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(
             torch.bfloat16).cuda()
 
-    for d in (64, 128):
-        bits = attn_synth.bf16_attention_inputs(2, B, H, N, d, with_dout=True)
-        q, k, v, do = (dev_bf16(bits[n]) for n in ("q", "k", "v", "do"))
-        for causal in (False, True):
-            tag = f"d{d} {'causal' if causal else 'non-causal'}"
-            t = dict(q=q, k=k, v=v, do=do, causal=causal,
-                     o=torch.empty_like(q),
-                     lse=torch.empty((B, H, N), device="cuda", dtype=torch.float32),
-                     dq=torch.empty(q.shape, device="cuda", dtype=torch.float32),
-                     dk=torch.empty(q.shape, device="cuda", dtype=torch.float32),
-                     dv=torch.empty(q.shape, device="cuda", dtype=torch.float32),
-                     ws=torch.empty(ea.attn_bwd_workspace_bytes(B, H, N, d),
-                                    device="cuda", dtype=torch.uint8))
-            # Every launch reads only the tensors bound in its own dict `t`; the
-            # binding derives the descriptor from their shapes.
-            def fwd(t=t):
-                ea.attn_fwd(t["q"], t["k"], t["v"], causal=t["causal"], out=t["o"],
-                            lse=t["lse"])
+    bits = attn_synth.bf16_attention_inputs(STEP_SEEDS, B, H, N, d, with_dout=True)
+    q, k, v, do = (dev_bf16(bits[n]) for n in ("q", "k", "v", "do"))
+    del bits
+    ws = torch.empty(ea.attn_bwd_workspace_bytes(B, H, N, d), device="cuda", dtype=torch.uint8)
+    dq = torch.empty(q.shape, device="cuda", dtype=torch.float32)
+    dk = torch.empty(q.shape, device="cuda", dtype=torch.float32)
+    dv = torch.empty(q.shape, device="cuda", dtype=torch.float32)
+    for causal in (False, True):
+        tag = "causal" if causal else "non-causal"
+        t = dict(q=q, k=k, v=v, do=do, causal=causal, o=torch.empty_like(q),
+                 lse=torch.empty((B, H, N), device="cuda", dtype=torch.float32),
+                 dq=dq, dk=dk, dv=dv, ws=ws)
 
-            def dq(t=t):
-                ea.attn_bwd_dq(t["q"], t["k"], t["v"], t["o"], t["do"], t["lse"],
-                               t["ws"], t["dq"], causal=t["causal"])
+        # Every launch reads the tensors bound in its own dict `t`; the
+        # binding derives the descriptor from their shapes.
+        def fwd(t=t):
+            ea.attn_fwd(t["q"], t["k"], t["v"], causal=t["causal"], out=t["o"], lse=t["lse"])
 
-            def dkdv(t=t):
-                ea.attn_bwd_dkdv(t["q"], t["k"], t["v"], t["do"], t["ws"], t["dk"],
-                                 t["dv"], causal=t["causal"])
+        def bwd_dq(t=t):
+            ea.attn_bwd_dq(t["q"], t["k"], t["v"], t["o"], t["do"], t["lse"], t["ws"], t["dq"],
+                           causal=t["causal"])
 
-            fwd()  # O and L for the backward launches
-            f = credited_fwd_flops(BH, N, d, causal, 0)
-            # Backward credit (2.5x fwd) is split over the five products:
-            # dK/dV kernel S, dP, dV, dK (4/5 of it), dQ kernel dQ (1/5); the
-            # dQ kernel also recomputes S and dP (executed, not credited).
-            bwd = 2.5 * f
-            launches.append(Launch(f"attn_fwd {tag}", f"fwd_bf16_kernel<d{d}>", fwd,
-                                   f, f, PEAK_BF16_TFLOPS))
-            # The dQ pass runs first: it also forms D = rowsum(dO * O) and
-            # leaves D and L log2(e) in the workspace for the dK/dV pass.
-            launches.append(Launch(f"attn_bwd_dq {tag}", f"bwd_dq_kernel<d{d}>", dq,
-                                   0.2 * bwd, 0.6 * bwd, PEAK_BF16_TFLOPS))
-            # (At d = 128 the dK/dV pass is the paired-wave kernel.)
-            dkdv_name = "bwd_dkdv_pair_kernel" if d == 128 else "bwd_dkdv_kernel"
-            launches.append(Launch(f"attn_bwd_dkdv {tag}", f"{dkdv_name}<d{d}>", dkdv,
-                                   0.8 * bwd, 0.8 * bwd, PEAK_BF16_TFLOPS))
-    if INCLUDE_FP8:
-        d = 128
-        f8 = attn_synth.fp8_attention_inputs(5, B, H, N, d)
-        q8, k8, v8 = (torch.from_numpy(f8[n]).cuda() for n in ("q", "k", "v"))
-        o8 = torch.empty((B, H, N, d), device="cuda", dtype=torch.bfloat16)
-        l8 = torch.empty((B, H, N), device="cuda", dtype=torch.float32)
-        f = credited_fwd_flops(BH, N, d, False, 0)
-        launches.append(Launch(
-            "attn_fwd_fp8 d128 non-causal", "fwd_fp8_kernel<d128>",
-            (lambda: ea.attn_fwd_fp8(q8, k8, v8, f8["q_descale"], f8["k_descale"],
-                                     f8["v_descale"], out=o8, lse=l8)),
-            f, f, PEAK_FP8_TFLOPS))
+        def bwd_dkdv(t=t):
+            ea.attn_bwd_dkdv(t["q"], t["k"], t["v"], t["do"], t["ws"], t["dk"], t["dv"],
+                             causal=t["causal"])
+
+        fwd()  # O and L for the backward launches
+        f = credited_fwd_flops(BH, N, d, causal, 0)
+        # Backward credit (2.5x fwd) is split over the five products: the
+        # dK/dV pass computes S, dP, dV, dK (4/5 of it), the dQ pass dQ
+        # (1/5) and also recomputes S and dP (executed, not credited).
+        bwd = 2.5 * f
+        name = lambda stage: ea.kernel_name(stage, B, H, N, d, causal)
+        launches.append(Launch(f"attn_fwd {tag}", name(ea.STAGE_FWD), fwd, f, f,
+                               PEAK_BF16_TFLOPS))
+        # The dQ pass runs first: it also forms D = rowsum(dO * O) and leaves
+        # D and L log2(e) in the workspace for the dK/dV pass.
+        launches.append(Launch(f"attn_bwd_dq {tag}", name(ea.STAGE_BWD_DQ), bwd_dq, 0.2 * bwd,
+                               0.6 * bwd, PEAK_BF16_TFLOPS))
+        launches.append(Launch(f"attn_bwd_dkdv {tag}", name(ea.STAGE_BWD_DKDV), bwd_dkdv,
+                               0.8 * bwd, 0.8 * bwd, PEAK_BF16_TFLOPS))
     return launches
 
 
@@ -321,15 +311,15 @@ def _time_ms(torch, fn, reps):
 
 
 def measure_configs(ea, torch, reps=10):
-    """Every workload of the metric beside the timed step: the single-head
-    forward (latency and HBM rate), the long-context causal and window
-    forwards, the B4 H16 N4096 causal backward, the fp8 forward, and the
-    N >= 4096, d = 128 points at which the forward and backward targets are
-    stated.  Inputs are N(0,1) draws of torch's seeded device generator (the
-    same distributions as the tests' inputs, drawn on the device because the
-    host generator needs tens of seconds at these sizes); the fp8 inputs get
-    the outlier channel (x10) and per-tensor e4m3 scales on the device too.
-    Measured after the timed step; none of it enters `value`."""
+    """Every other workload of the metric beside the timed step: the
+    single-head forward (latency and HBM rate), the B4 H16 N2048 sweep
+    (d 64 and 128, both masks), the long-context causal window, the
+    B4 H16 N4096 causal backward and the other N >= 4096, d = 128 points at
+    which the forward and backward targets are stated.  Inputs are N(0,1)
+    draws of torch's seeded device generator (the same distributions as the
+    tests' inputs, drawn on the device because the host generator needs tens
+    of seconds at these sizes).  Measured after the timed step; none of it
+    enters `value`."""
     gen = torch.Generator(device="cuda").manual_seed(79)
 
     def randn(*shape):
@@ -348,22 +338,22 @@ def measure_configs(ea, torch, reps=10):
     nbytes = 3 * 256 * 64 * 2 + 256 * 64 * 4 + 256 * 4
     out["fwd B1 H1 N256 d64 fp32-out"] = {"us": round(ms * 1e3, 2),
                                           "gbps": round(nbytes / (ms * 1e-3) / 1e9, 1)}
-    # Long context, causal and causal window 4096.
+    # Long context, causal window 4096 (exact visible-pair FLOPs).
     B, H, N, d = 1, 32, 16384, 128
     q, k, v = randn(B, H, N, d), randn(B, H, N, d), randn(B, H, N, d)
     o, lse = ea.attn_fwd(q, k, v, causal=True)
-    for window in (0, 4096):
-        f = credited_fwd_flops(B * H, N, d, True, window)
-        ms = _time_ms(torch, lambda: ea.attn_fwd(q, k, v, causal=True, window=window,
-                                                 out=o, lse=lse), reps)
-        tf = f / (ms * 1e-3) / 1e12
-        out[f"fwd B1 H32 N16384 d128 causal window={window}"] = {
-            "ms": round(ms, 4), "tflops": round(tf, 1), "pct_peak": pct(tf)}
+    f = credited_fwd_flops(B * H, N, d, True, 4096)
+    ms = _time_ms(torch, lambda: ea.attn_fwd(q, k, v, causal=True, window=4096, out=o,
+                                             lse=lse), reps)
+    tf = f / (ms * 1e-3) / 1e12
+    out["fwd B1 H32 N16384 d128 causal window=4096"] = {
+        "ms": round(ms, 4), "tflops": round(tf, 1), "pct_peak": pct(tf)}
     del q, k, v, o, lse
-    # The forward and backward targets (N >= 4096, d = 128) and the causal backward.
-    for B, H, N, causal in ((4, 16, 4096, True), (4, 16, 4096, False), (2, 32, 8192, False),
-                            (2, 32, 8192, True)):
-        d = 128
+    # The B4 H16 N2048 sweep, the N >= 4096, d = 128 points and the causal backward.
+    shapes = [(4, 16, 2048, 64, False), (4, 16, 2048, 64, True), (4, 16, 2048, 128, False),
+              (4, 16, 2048, 128, True), (4, 16, 4096, 128, True), (4, 16, 4096, 128, False),
+              (2, 32, 8192, 128, False), (2, 32, 8192, 128, True)]
+    for B, H, N, d, causal in shapes:
         q, k, v, do = (randn(B, H, N, d) for _ in range(4))
         o, lse = ea.attn_fwd(q, k, v, causal=causal)
         ws = torch.empty(ea.attn_bwd_workspace_bytes(B, H, N, d), device="cuda",
@@ -380,7 +370,17 @@ def measure_configs(ea, torch, reps=10):
             "fwd": {"ms": round(ms_f, 4), "tflops": round(tf_f, 1), "pct_peak": pct(tf_f)},
             "bwd": {"ms": round(ms_b, 4), "tflops": round(tf_b, 1), "pct_peak": pct(tf_b)}}
         del q, k, v, do, o, lse, ws, grads
-    # fp8 forward with one x10 outlier channel and per-tensor e4m3 scales.
+    return out
+
+
+def measure_fp8(ea, torch, reps=10):
+    """The fp8 forward at B2 H32 N8192 d128, non-causal: N(0,1) inputs of
+    torch's seeded device generator with one x10 outlier channel, quantised
+    per tensor to e4m3 on the device.  Credited FLOPs 4*B*H*N^2*d against the
+    fp8 peak; executed FLOPs count both e4m3 terms of the probabilities in
+    the P V product (6*d per visible pair instead of 4*d).  Measured after
+    the timed step; it does not enter `value`."""
+    gen = torch.Generator(device="cuda").manual_seed(80)
     B, H, N, d = 2, 32, 8192, 128
     codes, descales = [], []
     for _ in range(3):
@@ -394,11 +394,19 @@ def measure_configs(ea, torch, reps=10):
     lse = torch.empty((B, H, N), device="cuda", dtype=torch.float32)
     f = credited_fwd_flops(B * H, N, d, False, 0)
     ms = _time_ms(torch, lambda: ea.attn_fwd_fp8(*codes, *descales, out=o, lse=lse), reps)
+    ms_bf16 = None
+    qb, kb, vb = (torch.randn((B, H, N, d), device="cuda", generator=gen).bfloat16()
+                  for _ in range(3))
+    ob = torch.empty_like(qb)
+    ms_bf16 = _time_ms(torch, lambda: ea.attn_fwd(qb, kb, vb, out=ob, lse=lse), reps)
     tf = f / (ms * 1e-3) / 1e12
-    out["fp8 fwd B2 H32 N8192 d128 non-causal"] = {
-        "ms": round(ms, 4), "tflops": round(tf, 1), "pct_fp8_peak": pct(tf, PEAK_FP8_TFLOPS),
-        "pct_bf16_peak": pct(tf)}
-    return out
+    return {"workload": f"B{B} H{H} N{N} d{d} non-causal, e4m3 per-tensor, bf16 O",
+            "kernel": ea.kernel_name(ea.STAGE_FWD_FP8, B, H, N, d),
+            "ms": round(ms, 4), "tflops": round(tf, 1),
+            "pct_fp8_peak": round(100.0 * tf / PEAK_FP8_TFLOPS, 1),
+            "executed_tflops": round(1.5 * tf, 1),
+            "bf16_fwd_same_shape_ms": round(ms_bf16, 4),
+            "speedup_vs_bf16": round(ms_bf16 / ms, 3)}
 
 
 def measure_decode(ea, torch, attn_synth, reps=20):
@@ -435,43 +443,62 @@ def measure_decode(ea, torch, attn_synth, reps=20):
             "gbps": round(gbps, 1), "frac_of_hbm": round(gbps / HBM_GBPS, 4)}
 
 
-def cpu_baseline(attn_synth, seconds_budget=16.0):
-    """The fp64 oracle, as it stands, on a bounded sample of the same workload:
-    for each of the four variants, forward + backward of heads (0,0), (0,1), ...
-    until that variant's share of the budget is spent."""
+def cpu_model() -> str:
+    """The host CPU's model name from /proc/cpuinfo (empty if unreadable)."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return ""
+
+
+def cpu_baseline(attn_synth, seconds_budget=20.0):
+    """The fp64 oracle, as it stands, on a bounded sample of the timed
+    workload: forward + backward of whole heads (0, 0), (0, 1), ... of the
+    causal and then the non-causal variant, until that variant's share of
+    the budget is spent (at least one head each); credited FLOPs as for the
+    GPU."""
     import oracle
-    B, H, N = 4, 16, 2048
+    import numpy as np
+    B, H, N, d = STEP_B, STEP_H, STEP_N, STEP_D
     threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or os.cpu_count()
-    per_variant = seconds_budget / 4
+    s = 1.0 / math.sqrt(d)
     done_flops, t_total, parts = 0.0, 0.0, []
-    for d in (64, 128):
-        bits = attn_synth.bf16_attention_inputs(2, B, H, N, d, with_dout=True)
-        s = 1.0 / math.sqrt(d)
-        for causal in (False, True):
-            t_var, heads = 0.0, 0
-            while t_var < per_variant and heads < B * H:
-                b, h = divmod(heads, H)
-                ref = {k: oracle.decode_bf16(v[b, h]) for k, v in bits.items()}
-                t0 = time.perf_counter()
-                oracle.fwd(ref["q"], ref["k"], ref["v"], s, causal, 0, nthreads=threads)
-                oracle.bwd(ref["q"], ref["k"], ref["v"], ref["do"], s, causal, 0,
-                           nthreads=threads)
-                t_var += time.perf_counter() - t0
-                heads += 1
-                done_flops += 3.5 * credited_fwd_flops(1, N, d, causal, 0)
-            t_total += t_var
-            parts.append(f"d{d} {'causal' if causal else 'non-causal'}: {heads} heads")
-    whole = all(p.endswith(f": {B * H} heads") for p in parts)
-    which = "all heads" if whole else "the first heads"
+    for causal in (True, False):
+        t_var, heads = 0.0, 0
+        while heads == 0 or (t_var < seconds_budget / 2 and heads < B * H):
+            b, h = divmod(heads, H)
+            # Head (b, h) of the step's inputs: the generator's draws for one
+            # head are the slice [b, h] of the full tensor, so draw the full
+            # tensors' first heads only.
+            bits = attn_synth.bf16_attention_inputs(STEP_SEEDS, 1, b * H + h + 1, N, d,
+                                                    with_dout=True)
+            ref = {k: oracle.decode_bf16(np.ascontiguousarray(v[0, -1])) for k, v in bits.items()}
+            t0 = time.perf_counter()
+            oracle.fwd(ref["q"], ref["k"], ref["v"], s, causal, 0, nthreads=threads)
+            oracle.bwd(ref["q"], ref["k"], ref["v"], ref["do"], s, causal, 0, nthreads=threads)
+            t_var += time.perf_counter() - t0
+            heads += 1
+            done_flops += 3.5 * credited_fwd_flops(1, N, d, causal, 0)
+        t_total += t_var
+        parts.append(f"{'causal' if causal else 'non-causal'}: {heads} of {B * H} heads")
     return {
         "value": done_flops / t_total / 1e12,
         "unit": "TFLOP/s",
         "cores": threads,
+        "cpu_model": cpu_model(),
         "kind": "oracle",
-        "sample": (f"fp64 oracle forward + backward on {which} of the B4 H16 "
-                   f"N2048 workload ({'; '.join(parts)}), {t_total:.1f} s; credited "
-                   f"FLOPs as for the GPU"),
+        "sample": (f"fp64 oracle forward + backward of whole heads of the B{B} H{H} N{N} "
+                   f"d{d} step ({'; '.join(parts)}), {t_total:.1f} s of oracle time; "
+                   f"credited FLOPs as for the GPU"),
     }
+
+
+def progress(msg: str):
+    """A progress line on stderr (stdout carries only the result line)."""
+    print(f"bench: {msg}", file=sys.stderr, flush=True)
 
 
 def main():
@@ -486,6 +513,7 @@ def main():
     import exact_attention_79_amd as ea
 
     launches = build_step(ea, torch, attn_synth)
+    progress("inputs resident")
     for _ in range(args.warmup):
         run_step(launches, torch, record=False)
     torch.cuda.synchronize()
@@ -520,6 +548,21 @@ def main():
             row["gbps"] = round(L.bytes / (t * 1e-3) / 1e9, 1)
         breakdown.append(row)
 
+    # The forward and the backward (both passes) of each mask, as fractions
+    # of the bf16 peak: the targets are stated for them separately.
+    phases = {}
+    for L in launches:
+        mask = L.name.split()[-1]
+        ph = "fwd" if L.name.startswith("attn_fwd") else "bwd"
+        row = phases.setdefault(f"{ph} {mask}", {"ms": 0.0, "credited": 0.0})
+        row["ms"] += sum(L.times_ms) / len(L.times_ms)
+        row["credited"] += L.credited
+    phases = {k: {"ms": round(v["ms"], 4),
+                  "tflops": round(v["credited"] / (v["ms"] * 1e-3) / 1e12, 1),
+                  "pct_peak": round(100 * v["credited"] / (v["ms"] * 1e-3) / 1e12
+                                    / PEAK_BF16_TFLOPS, 1)}
+              for k, v in phases.items()}
+
     # Dominant kernel: the kernel symbol with the most GPU time per step.
     per_kernel = {}
     for L in launches:
@@ -553,20 +596,24 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": ("B4 H16 N2048 sweep: d in {64,128} x {non-causal, causal}, "
-                         "bf16 forward + backward; fp8 (e4m3) forward at d128 "
-                         "non-causal" + ("" if INCLUDE_FP8 else " (not yet built)")),
-            "global_batch": 4, "heads": 16, "seq_len": 2048, "head_dims": [64, 128],
+            "workload": (f"B{STEP_B} H{STEP_H} N{STEP_N} d{STEP_D} bf16 forward + backward "
+                         "(attn_fwd, attn_bwd_dq, attn_bwd_dkdv), causal and non-causal"),
+            "global_batch": STEP_B, "heads": STEP_H, "seq_len": STEP_N, "head_dim": STEP_D,
             "parallelism": "none (1 GPU)",
         },
         "roofline": roofline,
+        "phases": phases,
         "breakdown": breakdown,
     }
+    progress(f"timed step: {ms_per_step:.3f} ms, {value:.1f} TFLOP/s")
     if not args.no_extra_paths:
-        out["gqa"] = measure_gqa(ea, torch, attn_synth)
-        out["decode"] = measure_decode(ea, torch, attn_synth)
-        out["dropout"] = measure_dropout(ea, torch, attn_synth)
-        out["configs"] = measure_configs(ea, torch)
+        for key, fn in (("fp8", lambda: measure_fp8(ea, torch)),
+                        ("gqa", lambda: measure_gqa(ea, torch, attn_synth)),
+                        ("decode", lambda: measure_decode(ea, torch, attn_synth)),
+                        ("dropout", lambda: measure_dropout(ea, torch, attn_synth)),
+                        ("configs", lambda: measure_configs(ea, torch))):
+            out[key] = fn()
+            progress(f"measured {key}")
     if args.hbm_copy_mib > 0:
         # fp32 -> bf16, so that the copy runs as an elementwise kernel (a
         # same-dtype copy may go to a DMA engine that the counters miss).
@@ -580,6 +627,7 @@ def main():
         del src, dst
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(attn_synth)
+        progress("timed the CPU oracle")
     print(json.dumps(out), flush=True)
     return 0
 
