@@ -18,7 +18,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libattn.so")
 
-ATTN_OK, ATTN_EINVAL, ATTN_EUNSUPPORTED, ATTN_EHIP = 0, 1, 2, 3
+ATTN_OK, ATTN_EINVAL, ATTN_EUNSUPPORTED, ATTN_EHIP, ATTN_ESCRATCH = 0, 1, 2, 3, 4
 ATTN_OUT_BF16, ATTN_OUT_F32 = 0, 1
 STAGE_FWD, STAGE_BWD_DQ, STAGE_BWD_DKDV, STAGE_FWD_FP8 = 0, 1, 2, 3
 
@@ -26,7 +26,8 @@ STAGE_FWD, STAGE_BWD_DQ, STAGE_BWD_DKDV, STAGE_FWD_FP8 = 0, 1, 2, 3
 EXPORTS = ("attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_bwd_preprocess",
            "attn_bwd_dkdv", "attn_bwd_dq", "attn_fwd_fp8", "attn_decode_workspace_bytes",
            "attn_fwd_decode", "attn_fwd_fp8_blocks", "attn_fwd_dropout", "attn_bwd_dropout",
-           "attn_status_str", "attn_kernel_name")
+           "attn_status_str", "attn_kernel_name", "attn_bwd_noalloc",
+           "attn_bwd_noalloc_scratch_bytes")
 
 
 class AttnDesc(ctypes.Structure):
@@ -68,6 +69,10 @@ def _load():
     L.attn_bwd_workspace_bytes.restype = sz
     L.attn_bwd.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.attn_bwd.restype = ctypes.c_int
+    L.attn_bwd_noalloc.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    L.attn_bwd_noalloc.restype = ctypes.c_int
+    L.attn_bwd_noalloc_scratch_bytes.argtypes = [dp]
+    L.attn_bwd_noalloc_scratch_bytes.restype = sz
     L.attn_bwd_preprocess.argtypes = [dp, vp, vp, vp, vp, sz, vp]
     L.attn_bwd_preprocess.restype = ctypes.c_int
     L.attn_bwd_dq.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp]
@@ -230,6 +235,25 @@ def attn_bwd(q, k, v, o, dout, lse, scale: float | None = None,
     _check(lib.attn_bwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
                         _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
                         _ptr(workspace), _ws_bytes(workspace), _stream()), "attn_bwd")
+    return dq, dk, dv
+
+
+def attn_bwd_noalloc(q, k, v, o, dout, lse, grads, scale: float | None = None,
+                     causal: bool = False, window: int = 0):
+    """attn_bwd without a workspace: the library's static device scratch holds
+    D and L log2(e) (include/attn.h); the caller passes the fp32 gradient
+    tensors (dq, dk, dv), so nothing is allocated."""
+    _check_qkv(q, k, v, (torch.bfloat16,))
+    _check_like(q, torch.bfloat16, o=o, dout=dout)
+    dq, dk, dv = grads
+    _check_like(q, torch.float32, dq=dq)
+    _check_like(k, torch.float32, dk=dk, dv=dv)
+    B, H, N, _ = q.shape
+    _check_lse(lse, (B, H, N))
+    desc = _bwd_desc(q, k, scale, causal, window)
+    _check(lib.attn_bwd_noalloc(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
+                                _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
+                                _stream()), "attn_bwd_noalloc")
     return dq, dk, dv
 
 

@@ -4,8 +4,18 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "attn.h"
 #include "attn_kernels.hpp"
+
+// Device memory for callers that cannot allocate (attn_bwd_noalloc): the
+// backward's D and L log2(e) arrays live here instead of in a caller's
+// workspace.  Each GPU the library runs on holds its own copy until the
+// process ends.  Host code never uses the name `scratch` as an address (on
+// the host it is only a stand-in for the symbol): the device address comes
+// from hipGetSymbolAddress, once per device, in scratch_address below.
+static __device__ __align__(256) unsigned char scratch[ATTN_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -104,6 +114,7 @@ attn::BwdArgs bwd_args(const attn_desc* d, const void* q, const void* k,
   a.causal = d->causal;
   a.window = d->window;
   a.drop = attn::DropoutArgs{0u, 0u, 0ull};
+  a.no_split = 0;
   return a;
 }
 
@@ -115,6 +126,25 @@ attn_status dropout_args(const attn_dropout* drop, attn::DropoutArgs* out) {
   out->thresh = (uint32_t)t;
   out->offset = drop->offset;
   out->seed = drop->seed;
+  return ATTN_OK;
+}
+
+// The device address of `scratch` on the current device, looked up with that
+// device current on the first call there and kept per device.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+attn_status scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return ATTN_EHIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return ATTN_EHIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
   return ATTN_OK;
 }
 
@@ -152,6 +182,29 @@ attn_status attn_bwd(const attn_desc* desc, const void* q, const void* k,
   return from_hip(attn::launch_bwd(
       bwd_args(desc, q, k, v, o, dout, lse, dq, dk, dv, workspace),
       (hipStream_t)stream));
+}
+
+size_t attn_bwd_noalloc_scratch_bytes(const attn_desc* desc) {
+  if (check_desc(desc) != ATTN_OK) return 0;
+  return 2 * ws_array_bytes(desc);
+}
+
+attn_status attn_bwd_noalloc(const attn_desc* desc, const void* q, const void* k,
+                             const void* v, const void* o, const void* dout,
+                             const float* lse, float* dq, float* dk, float* dv,
+                             void* stream) {
+  attn_status st = check_desc(desc);
+  if (st != ATTN_OK) return st;
+  st = check_ptrs({q, k, v, o, dout, lse, dq, dk, dv}, {});
+  if (st != ATTN_OK) return st;
+  if (attn_bwd_noalloc_scratch_bytes(desc) > (size_t)ATTN_NOALLOC_SCRATCH_BYTES)
+    return ATTN_ESCRATCH;
+  void* ws = nullptr;
+  st = scratch_address(&ws);
+  if (st != ATTN_OK) return st;
+  attn::BwdArgs a = bwd_args(desc, q, k, v, o, dout, lse, dq, dk, dv, ws);
+  a.no_split = 1;  // no partial dK/dV arrays: the scratch holds D and L log2(e) only
+  return from_hip(attn::launch_bwd(a, (hipStream_t)stream));
 }
 
 attn_status attn_bwd_preprocess(const attn_desc* desc, const void* o,
@@ -369,6 +422,9 @@ const char* attn_status_str(attn_status s) {
       return "unsupported shape (head dim must be 64 or 128; B*H*N*d < 2^31)";
     case ATTN_EHIP:
       return "HIP runtime error at launch";
+    case ATTN_ESCRATCH:
+      return "problem too large for the no-allocation entry point's static scratch "
+             "(B*H*N above its limit)";
   }
   return "unknown status";
 }

@@ -1820,7 +1820,7 @@ hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream, const char** na
   BwdKParams p = bwd_params(a, 32 * kBwdWaves);
   // One workgroup per key block of every key/value head and share of its group.
   const int BHkv = a.BH / a.H * a.Hkv;
-  p.split = dkdv_split(BHkv, a.H / a.Hkv, a.N, a.d, a.causal);
+  p.split = a.no_split ? 1 : dkdv_split(BHkv, a.H / a.Hkv, a.N, a.d, a.causal);
   const dim3 grid((unsigned)(BHkv * p.n_tiles * p.split)), block(64 * kBwdWaves);
   const bool drop = a.drop.thresh > 0;
   constexpr int W = kBwdWaves;

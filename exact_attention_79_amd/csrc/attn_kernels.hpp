@@ -53,6 +53,7 @@ struct BwdArgs {
   float scale;
   int causal, window;
   DropoutArgs drop;
+  int no_split;        // 1: the dK/dV pass never splits a group (no partials)
 };
 
 // A block of Nq queries (the last Nq positions) against Nk keys, split over

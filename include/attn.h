@@ -71,7 +71,8 @@ typedef enum {
   ATTN_OK = 0,
   ATTN_EINVAL = 1,
   ATTN_EUNSUPPORTED = 2,
-  ATTN_EHIP = 3
+  ATTN_EHIP = 3,
+  ATTN_ESCRATCH = 4 /* attn_bwd_noalloc only: the problem exceeds its static scratch */
 } attn_status;
 
 typedef enum { ATTN_OUT_BF16 = 0, ATTN_OUT_F32 = 1 } attn_out_dtype;
@@ -122,6 +123,31 @@ attn_status attn_bwd(const attn_desc* desc, const void* q, const void* k,
                      const void* v, const void* o, const void* dout,
                      const float* lse, float* dq, float* dk, float* dv,
                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* The backward for callers that cannot allocate memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): attn_bwd
+ * without a workspace argument.  Its D and L log2(e) arrays live in a static
+ * device array of the library, ATTN_NOALLOC_SCRATCH_BYTES bytes on every GPU
+ * the library runs on, held until the process ends; the call allocates
+ * nothing and calls no allocating routine.  The scratch holds
+ * attn_bwd_noalloc_scratch_bytes(desc) bytes (8 bytes per query row, each
+ * array padded to 256 bytes), so B*H*N may be at most about 2^21; larger
+ * problems return ATTN_ESCRATCH before anything is launched.  Grouped-query
+ * backwards never split a group here (no partial dK/dV arrays), so small
+ * grouped-query grids may run slower than with attn_bwd.
+ *   The scratch is shared by every call on a GPU and keeps the last call's
+ * contents (each call writes all of what it reads first, so nothing needs
+ * clearing); calls that overlap on one GPU (for example on two streams) race
+ * on it and must be serialised by the caller.  The scratch's device address
+ * is looked up once per device, on the first call with that device current;
+ * `stream` must belong to the current device.  Other arguments, results and
+ * errors as attn_bwd. */
+#define ATTN_NOALLOC_SCRATCH_BYTES (16u << 20)
+size_t attn_bwd_noalloc_scratch_bytes(const attn_desc* desc);
+attn_status attn_bwd_noalloc(const attn_desc* desc, const void* q, const void* k,
+                             const void* v, const void* o, const void* dout,
+                             const float* lse, float* dq, float* dk, float* dv,
+                             void* stream);
 
 /* The backward as separately launchable stages.  attn_bwd enqueues
  * attn_bwd_dq and then attn_bwd_dkdv on one stream; a caller may issue them

@@ -29,7 +29,8 @@ def test_header_declares_the_boundary():
         ["attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_bwd_preprocess",
          "attn_bwd_dkdv", "attn_bwd_dq", "attn_fwd_fp8", "attn_decode_workspace_bytes",
          "attn_fwd_decode", "attn_fwd_fp8_blocks", "attn_fwd_dropout", "attn_bwd_dropout",
-         "attn_status_str", "attn_kernel_name"])
+         "attn_status_str", "attn_kernel_name", "attn_bwd_noalloc",
+         "attn_bwd_noalloc_scratch_bytes"])
 
 
 def test_library_exports_every_declared_symbol(ea):
@@ -39,8 +40,8 @@ def test_library_exports_every_declared_symbol(ea):
 
 
 def test_status_strings(ea):
-    for s in range(4):
-        assert ea.status_str(s)
+    for s in range(5):
+        assert ea.status_str(s) and ea.status_str(s) != "unknown status"
     assert ea.status_str(99) == "unknown status"
 
 
@@ -286,3 +287,26 @@ def test_lse_check_shared_by_every_forward(ea):
     for fn in (ea._fwd_prep, ea.attn_fwd_fp8, ea.attn_fwd_fp8_blocks, ea.attn_fwd_decode,
                ea._check_lse_ws):
         assert "_check_lse(lse" in inspect.getsource(fn), fn.__name__
+
+
+def test_noalloc_backward_rejects_before_launching(ea):
+    """The no-allocation backward checks its arguments like attn_bwd and
+    refuses problems whose D and L log2(e) arrays exceed its static scratch
+    (ATTN_ESCRATCH), all before any HIP call."""
+    vp = ctypes.c_void_p
+    f = vp(FAKE)
+    limit = 16 << 20
+    ok = ea.make_desc(4, 16, 4096, 128, 0.1, True, 0)
+    need = ea.lib.attn_bwd_noalloc_scratch_bytes(ctypes.byref(ok))
+    assert need == 2 * 4 * 16 * 4096 * 4 and need <= limit
+    big = ea.make_desc(1, 64, 65536, 64, 0.1, True, 0)  # 2^22 rows: 32 MiB
+    assert ea.lib.attn_bwd_noalloc_scratch_bytes(ctypes.byref(big)) > limit
+    assert ea.lib.attn_bwd_noalloc(ctypes.byref(big), *([f] * 9), None) == ea.ATTN_ESCRATCH
+    assert ea.lib.attn_bwd_noalloc(ctypes.byref(ok), f, f, f, f, f, None, f, f, f,
+                                   None) == ea.ATTN_EINVAL
+    assert ea.lib.attn_bwd_noalloc(ctypes.byref(ok), f, f, f, f, f, f, f, f, vp(FAKE + 4),
+                                   None) == ea.ATTN_EINVAL
+    bad = ea.make_desc(1, 2, 64, 80, 0.1, False, 0)
+    assert ea.lib.attn_bwd_noalloc_scratch_bytes(ctypes.byref(bad)) == 0
+    assert ea.lib.attn_bwd_noalloc(ctypes.byref(bad), *([f] * 9), None) == \
+        ea.ATTN_EUNSUPPORTED
