@@ -85,6 +85,10 @@ def parse_args():
                     help="skip the fp8, grouped-query, decode, dropout and per-workload "
                          "measurements that follow the timed step (for profiler runs "
                          "that should see the step only)")
+    ap.add_argument("--workload", choices=sorted(WORKLOADS), default="step",
+                    help="time another workload in place of the step (for profiler runs: "
+                         "bwd4096 = B4 H16 N4096 d128 causal forward + backward, fp8 = the "
+                         "B2 H32 N8192 d128 fp8 forward); the result line then describes it")
     ap.add_argument("--hbm-copy-mib", type=int, default=0,
                     help="after timing, one fp32 -> bf16 copy of this many MiB of "
                          "fp32 (counter calibration for rocprofv3 --pmc runs)")
@@ -128,10 +132,38 @@ class Launch:
         self.times_ms = []
 
 
-def build_step(ea, torch, attn_synth):
+# Workloads a profiler run can time in place of the step (--workload): the
+# causal backward workload B4 H16 N4096 and the fp8 forward B2 H32 N8192.
+# Each keeps the seeds of its workload number.
+WORKLOADS = {
+    "step": dict(B=STEP_B, H=STEP_H, N=STEP_N, d=STEP_D, masks=(False, True), seeds=STEP_SEEDS),
+    "bwd4096": dict(B=4, H=16, N=4096, d=128, masks=(True,), seeds=4),
+    "fp8": dict(B=2, H=32, N=8192, d=128, masks=(False,), seeds=5),
+}
+
+
+def build_fp8_step(ea, torch, attn_synth, w):
+    """The fp8 forward as a step: inputs with one x10 outlier channel,
+    quantised per tensor to e4m3 on the host (attn_synth)."""
+    B, H, N, d = w["B"], w["H"], w["N"], w["d"]
+    f8 = attn_synth.fp8_attention_inputs(w["seeds"], B, H, N, d)
+    q8, k8, v8 = (torch.from_numpy(f8[n]).cuda() for n in ("q", "k", "v"))
+    o = torch.empty((B, H, N, d), device="cuda", dtype=torch.bfloat16)
+    lse = torch.empty((B, H, N), device="cuda", dtype=torch.float32)
+    f = credited_fwd_flops(B * H, N, d, False, 0)
+    fn = lambda: ea.attn_fwd_fp8(q8, k8, v8, f8["q_descale"], f8["k_descale"],
+                                 f8["v_descale"], out=o, lse=lse)
+    return [Launch("attn_fwd_fp8 non-causal", ea.kernel_name(ea.STAGE_FWD_FP8, B, H, N, d), fn,
+                   f, 1.5 * f, PEAK_FP8_TFLOPS)]
+
+
+def build_step(ea, torch, attn_synth, workload="step"):
     """All launches of one step, with inputs resident on the device."""
     import numpy as np
-    B, H, N, d = STEP_B, STEP_H, STEP_N, STEP_D
+    w = WORKLOADS[workload]
+    if workload == "fp8":
+        return build_fp8_step(ea, torch, attn_synth, w)
+    B, H, N, d = w["B"], w["H"], w["N"], w["d"]
     BH = B * H
     launches = []
 
@@ -139,14 +171,14 @@ def build_step(ea, torch, attn_synth):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(
             torch.bfloat16).cuda()
 
-    bits = attn_synth.bf16_attention_inputs(STEP_SEEDS, B, H, N, d, with_dout=True)
+    bits = attn_synth.bf16_attention_inputs(w["seeds"], B, H, N, d, with_dout=True)
     q, k, v, do = (dev_bf16(bits[n]) for n in ("q", "k", "v", "do"))
     del bits
     ws = torch.empty(ea.attn_bwd_workspace_bytes(B, H, N, d), device="cuda", dtype=torch.uint8)
     dq = torch.empty(q.shape, device="cuda", dtype=torch.float32)
     dk = torch.empty(q.shape, device="cuda", dtype=torch.float32)
     dv = torch.empty(q.shape, device="cuda", dtype=torch.float32)
-    for causal in (False, True):
+    for causal in w["masks"]:
         tag = "causal" if causal else "non-causal"
         t = dict(q=q, k=k, v=v, do=do, causal=causal, o=torch.empty_like(q),
                  lse=torch.empty((B, H, N), device="cuda", dtype=torch.float32),
@@ -496,6 +528,16 @@ def cpu_baseline(attn_synth, seconds_budget=20.0):
     }
 
 
+def workload_config(name: str) -> dict:
+    w = WORKLOADS[name]
+    shape = f"B{w['B']} H{w['H']} N{w['N']} d{w['d']}"
+    masks = " and ".join("causal" if m else "non-causal" for m in w["masks"])
+    what = ("fp8 (e4m3) forward (attn_fwd_fp8), " if name == "fp8" else
+            "bf16 forward + backward (attn_fwd, attn_bwd_dq, attn_bwd_dkdv), ")
+    return {"workload": f"{shape} {what}{masks}", "global_batch": w["B"], "heads": w["H"],
+            "seq_len": w["N"], "head_dim": w["d"], "parallelism": "none (1 GPU)"}
+
+
 def progress(msg: str):
     """A progress line on stderr (stdout carries only the result line)."""
     print(f"bench: {msg}", file=sys.stderr, flush=True)
@@ -512,7 +554,7 @@ def main():
     import attn_synth
     import exact_attention_79_amd as ea
 
-    launches = build_step(ea, torch, attn_synth)
+    launches = build_step(ea, torch, attn_synth, args.workload)
     progress("inputs resident")
     for _ in range(args.warmup):
         run_step(launches, torch, record=False)
@@ -554,13 +596,13 @@ def main():
     for L in launches:
         mask = L.name.split()[-1]
         ph = "fwd" if L.name.startswith("attn_fwd") else "bwd"
-        row = phases.setdefault(f"{ph} {mask}", {"ms": 0.0, "credited": 0.0})
+        row = phases.setdefault(f"{ph} {mask}", {"ms": 0.0, "credited": 0.0, "peak": L.peak})
         row["ms"] += sum(L.times_ms) / len(L.times_ms)
         row["credited"] += L.credited
     phases = {k: {"ms": round(v["ms"], 4),
                   "tflops": round(v["credited"] / (v["ms"] * 1e-3) / 1e12, 1),
                   "pct_peak": round(100 * v["credited"] / (v["ms"] * 1e-3) / 1e12
-                                    / PEAK_BF16_TFLOPS, 1)}
+                                    / v["peak"], 1)}
               for k, v in phases.items()}
 
     # Dominant kernel: the kernel symbol with the most GPU time per step.
@@ -593,14 +635,9 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "fp8" if args.workload == "fp8" else "bf16",
         "data": "synthetic",
-        "config": {
-            "workload": (f"B{STEP_B} H{STEP_H} N{STEP_N} d{STEP_D} bf16 forward + backward "
-                         "(attn_fwd, attn_bwd_dq, attn_bwd_dkdv), causal and non-causal"),
-            "global_batch": STEP_B, "heads": STEP_H, "seq_len": STEP_N, "head_dim": STEP_D,
-            "parallelism": "none (1 GPU)",
-        },
+        "config": workload_config(args.workload),
         "roofline": roofline,
         "phases": phases,
         "breakdown": breakdown,

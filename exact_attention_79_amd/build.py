@@ -35,10 +35,27 @@ def _compile(src: str) -> str:
     return obj
 
 
+# Measurement programs (not part of the library): source -> executable.
+PROBES = {os.path.join(HERE, "probes", "dq_atomic_adds.hip"):
+          os.path.join(HERE, "probes", "dq_atomic_adds")}
+
+
+def _build_probe(src: str, exe: str):
+    cmd = [HIPCC, "--offload-arch=gfx950", "-O3", "-munsafe-fp-atomics",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           "-Wno-unused-command-line-argument", src, "-o", exe]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
+
+
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
     with ThreadPoolExecutor(max_workers=min(4, len(SOURCES))) as ex:
         objs = list(ex.map(_compile, SOURCES))
+        probes = [ex.submit(_build_probe, s, e) for s, e in PROBES.items()]
+        for pr in probes:
+            pr.result()
     tmp = LIB + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
