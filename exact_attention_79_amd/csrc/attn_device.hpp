@@ -68,17 +68,19 @@ __device__ __forceinline__ bf16x8 cat4(bf16x4 a, bf16x4 b) {
 }
 
 // Combine a value with the one held by lane l ^ 32 (the other half of the
-// wave).  The lower-half value is always the left operand, so both halves
-// compute the identical rounded result.
-__device__ __forceinline__ float other_half(float x) {
-  return __shfl_xor(x, 32, 64);
-}
+// wave) without going through LDS: v_permlane32_swap on two copies of x
+// leaves one copy holding the lower half's values in every lane and the
+// other the upper half's, and both halves then compute the identical
+// rounded result (max and sum are taken of the same two operands).
 __device__ __forceinline__ float halves_max(float x) {
-  return fmaxf(x, other_half(x));
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x),
+                                                  __builtin_bit_cast(unsigned, x), false, false);
+  return fmaxf(__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1]));
 }
 __device__ __forceinline__ float halves_sum(float x) {
-  const float y = other_half(x);
-  return (threadIdx.x & 32) ? y + x : x + y;
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x),
+                                                  __builtin_bit_cast(unsigned, x), false, false);
+  return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
 }
 
 __device__ __forceinline__ float fast_exp2(float x) {
