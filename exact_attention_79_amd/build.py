@@ -37,7 +37,9 @@ def _compile(src: str) -> str:
 
 # Measurement programs (not part of the library): source -> executable.
 PROBES = {os.path.join(HERE, "probes", "dq_atomic_adds.hip"):
-          os.path.join(HERE, "probes", "dq_atomic_adds")}
+          os.path.join(HERE, "probes", "dq_atomic_adds"),
+          os.path.join(HERE, "probes", "valu_rates.hip"):
+          os.path.join(HERE, "probes", "valu_rates")}
 
 
 def _build_probe(src: str, exe: str):
