@@ -342,6 +342,29 @@ def _time_ms(torch, fn, reps):
     return e0.elapsed_time(e1) / reps
 
 
+def _time_each_us(torch, fn, reps, flush=None):
+    """GPU time of single calls, in microseconds: each call is enqueued behind
+    a ~1 ms device-side spin (torch.cuda._sleep), so the events around it
+    measure the device's work for the call and not the host's time to issue
+    it; `flush`, when given, runs before the spin (untimed).  Returns
+    (median, min) over `reps` calls after one untimed call."""
+    fn()
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        if flush is not None:
+            flush()
+        torch.cuda._sleep(2_000_000)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1) * 1e3)
+    ts.sort()
+    return ts[len(ts) // 2], ts[0]
+
+
 def measure_configs(ea, torch, reps=10):
     """Every other workload of the metric beside the timed step: the
     single-head forward (latency and HBM rate), the B4 H16 N2048 sweep
@@ -365,11 +388,21 @@ def measure_configs(ea, torch, reps=10):
     q, k, v = randn(1, 1, 256, 64), randn(1, 1, 256, 64), randn(1, 1, 256, 64)
     o = torch.empty(q.shape, device="cuda", dtype=torch.float32)
     lse = torch.empty((1, 1, 256), device="cuda", dtype=torch.float32)
-    ms = _time_ms(torch, lambda: ea.attn_fwd(q, k, v, out_dtype=torch.float32, out=o,
-                                             lse=lse), 50)
+    call = lambda: ea.attn_fwd(q, k, v, out_dtype=torch.float32, out=o, lse=lse)
+    ms = _time_ms(torch, call, 50)
     nbytes = 3 * 256 * 64 * 2 + 256 * 64 * 4 + 256 * 4
-    out["fwd B1 H1 N256 d64 fp32-out"] = {"us": round(ms * 1e3, 2),
-                                          "gbps": round(nbytes / (ms * 1e-3) / 1e9, 1)}
+    # Device time of one call with warm caches, and after 512 MiB have been
+    # written (more than the L2s and the 256 MB MALL hold): median and min.
+    flush_buf = torch.empty(512 << 20, device="cuda", dtype=torch.uint8)
+    warm = _time_each_us(torch, call, 50)
+    cold = _time_each_us(torch, call, 50, flush=lambda: flush_buf.zero_())
+    del flush_buf
+    gbps = lambda us: round(nbytes / (us * 1e-6) / 1e9, 1)
+    out["fwd B1 H1 N256 d64 fp32-out"] = {
+        "us": round(ms * 1e3, 2), "gbps": gbps(ms * 1e3),
+        "device_us_warm_median": round(warm[0], 2), "device_us_warm_min": round(warm[1], 2),
+        "device_us_cold_median": round(cold[0], 2), "device_us_cold_min": round(cold[1], 2),
+        "gbps_warm": gbps(warm[0]), "gbps_cold": gbps(cold[0])}
     # Long context, causal window 4096 (exact visible-pair FLOPs).
     B, H, N, d = 1, 32, 16384, 128
     q, k, v = randn(B, H, N, d), randn(B, H, N, d), randn(B, H, N, d)
