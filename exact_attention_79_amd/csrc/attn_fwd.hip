@@ -354,7 +354,10 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdKParams p) {
 // V_j sit in slot j % 3 of their rings; at every even half-step 2u the waves
 // fetch K_{u+3} and V_{u+2}, and every half-step ends by waiting for the
 // fetches issued two half-steps earlier, so that the operands of a wave's
-// next M are in LDS during its V and the first of them are read there.
+// next M are in LDS during its V and the first of them are read there, at
+// its start (issued before the exponentials, the reads are back before the
+// other group's operand reads fill the LDS queue; about 1 % faster than at
+// its end).
 // Under the causal mask the first group (the workgroup's first 128 queries)
 // stops computing after the last tile its queries see and from then on only
 // fetches its share of the tiles and joins the barriers.
@@ -589,36 +592,36 @@ __global__ __launch_bounds__(2 * NG * 64, 2) void fwd_pp_kernel(FwdKParams p) {
       fetch(u, sK0, sV2);
       mstep(sK1, sV0);
       end_half();
-      vstep(u, Tg);
       prefetch(sK2, sV1);
+      vstep(u, Tg);
       end_half();
       fetch(u + 1, sK1, sV0);
       mstep(sK2, sV1);
       end_half();
-      vstep(u + 1, Tg);
       prefetch(sK0, sV2);
+      vstep(u + 1, Tg);
       end_half();
       fetch(u + 2, sK2, sV1);
       mstep(sK0, sV2);
       end_half();
-      vstep(u + 2, Tg);
       prefetch(sK1, sV0);
+      vstep(u + 2, Tg);
       end_half();
     }
     if (u < Tg) {
       fetch(u, sK0, sV2);
       mstep(sK1, sV0);
       end_half();
-      vstep(u, Tg);
       prefetch(sK2, sV1);
+      vstep(u, Tg);
       end_half();
     }
     if (u + 1 < Tg) {
       fetch(u + 1, sK1, sV0);
       mstep(sK2, sV1);
       end_half();
-      vstep(u + 1, Tg);
       prefetch(sK0, sV2);
+      vstep(u + 1, Tg);
       end_half();
     }
     for (u += (u < Tg) + (u + 1 < Tg); u < T; ++u) {
@@ -632,36 +635,36 @@ __global__ __launch_bounds__(2 * NG * 64, 2) void fwd_pp_kernel(FwdKParams p) {
   } else {
     for (; u + 3 <= T; u += 3) {
       fetch(u, sK0, sV2);
-      vstep(u - 1, T);
       prefetch(sK1, sV0);
+      vstep(u - 1, T);
       end_half();
       mstep(sK1, sV0);
       end_half();
       fetch(u + 1, sK1, sV0);
-      vstep(u, T);
       prefetch(sK2, sV1);
+      vstep(u, T);
       end_half();
       mstep(sK2, sV1);
       end_half();
       fetch(u + 2, sK2, sV1);
-      vstep(u + 1, T);
       prefetch(sK0, sV2);
+      vstep(u + 1, T);
       end_half();
       mstep(sK0, sV2);
       end_half();
     }
     if (u < T) {
       fetch(u, sK0, sV2);
-      vstep(u - 1, T);
       prefetch(sK1, sV0);
+      vstep(u - 1, T);
       end_half();
       mstep(sK1, sV0);
       end_half();
     }
     if (u + 1 < T) {
       fetch(u + 1, sK1, sV0);
-      vstep(u, T);
       prefetch(sK2, sV1);
+      vstep(u, T);
       end_half();
       mstep(sK2, sV1);
       end_half();
