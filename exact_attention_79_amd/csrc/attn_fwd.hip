@@ -355,9 +355,8 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdKParams p) {
 // fetch K_{u+3} and V_{u+2}, and every half-step ends by waiting for the
 // fetches issued two half-steps earlier, so that the operands of a wave's
 // next M are in LDS during its V and the first of them are read there, at
-// its start (issued before the exponentials, the reads are back before the
-// other group's operand reads fill the LDS queue; about 1 % faster than at
-// its end).
+// its start, before the exponentials (measured about 1 % faster than at its
+// end).
 // Under the causal mask the first group (the workgroup's first 128 queries)
 // stops computing after the last tile its queries see and from then on only
 // fetches its share of the tiles and joins the barriers.
