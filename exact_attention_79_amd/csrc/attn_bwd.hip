@@ -1066,100 +1066,100 @@ __global__ __launch_bounds__(2 * NG * 64, 2) void bwd_dkdv_pp_kernel(BwdKParams 
       fetch(sQ3, sO3, sL3, sD3);
       mstep(sQ0, sO0, sQ1, sO1, sD1);
       end_half();
-      vstep(u, sL1);
       prefetch(sQ1, sO1, sQ2, sO2);
+      vstep(u, sL1);
       end_half();
       fetch(sQ0, sO0, sL0, sD0);
       mstep(sQ1, sO1, sQ2, sO2, sD2);
       end_half();
-      vstep(u + 1, sL2);
       prefetch(sQ2, sO2, sQ3, sO3);
+      vstep(u + 1, sL2);
       end_half();
       fetch(sQ1, sO1, sL1, sD1);
       mstep(sQ2, sO2, sQ3, sO3, sD3);
       end_half();
-      vstep(u + 2, sL3);
       prefetch(sQ3, sO3, sQ0, sO0);
+      vstep(u + 2, sL3);
       end_half();
       fetch(sQ2, sO2, sL2, sD2);
       mstep(sQ3, sO3, sQ0, sO0, sD0);
       end_half();
-      vstep(u + 3, sL0);
       prefetch(sQ0, sO0, sQ1, sO1);
+      vstep(u + 3, sL0);
       end_half();
     }
     if (u < T) {
       fetch(sQ3, sO3, sL3, sD3);
       mstep(sQ0, sO0, sQ1, sO1, sD1);
       end_half();
-      vstep(u, sL1);
       prefetch(sQ1, sO1, sQ2, sO2);
+      vstep(u, sL1);
       end_half();
     }
     if (u + 1 < T) {
       fetch(sQ0, sO0, sL0, sD0);
       mstep(sQ1, sO1, sQ2, sO2, sD2);
       end_half();
-      vstep(u + 1, sL2);
       prefetch(sQ2, sO2, sQ3, sO3);
+      vstep(u + 1, sL2);
       end_half();
     }
     if (u + 2 < T) {
       fetch(sQ1, sO1, sL1, sD1);
       mstep(sQ2, sO2, sQ3, sO3, sD3);
       end_half();
-      vstep(u + 2, sL3);
       prefetch(sQ3, sO3, sQ0, sO0);
+      vstep(u + 2, sL3);
       end_half();
     }
     end_half();
   } else {
     for (; u + 4 <= T; u += 4) {
       fetch(sQ3, sO3, sL3, sD3);
-      vstep(u - 1, sL0);
       prefetch(sQ0, sO0, sQ1, sO1);
+      vstep(u - 1, sL0);
       end_half();
       mstep(sQ0, sO0, sQ1, sO1, sD1);
       end_half();
       fetch(sQ0, sO0, sL0, sD0);
-      vstep(u, sL1);
       prefetch(sQ1, sO1, sQ2, sO2);
+      vstep(u, sL1);
       end_half();
       mstep(sQ1, sO1, sQ2, sO2, sD2);
       end_half();
       fetch(sQ1, sO1, sL1, sD1);
-      vstep(u + 1, sL2);
       prefetch(sQ2, sO2, sQ3, sO3);
+      vstep(u + 1, sL2);
       end_half();
       mstep(sQ2, sO2, sQ3, sO3, sD3);
       end_half();
       fetch(sQ2, sO2, sL2, sD2);
-      vstep(u + 2, sL3);
       prefetch(sQ3, sO3, sQ0, sO0);
+      vstep(u + 2, sL3);
       end_half();
       mstep(sQ3, sO3, sQ0, sO0, sD0);
       end_half();
     }
     if (u < T) {
       fetch(sQ3, sO3, sL3, sD3);
-      vstep(u - 1, sL0);
       prefetch(sQ0, sO0, sQ1, sO1);
+      vstep(u - 1, sL0);
       end_half();
       mstep(sQ0, sO0, sQ1, sO1, sD1);
       end_half();
     }
     if (u + 1 < T) {
       fetch(sQ0, sO0, sL0, sD0);
-      vstep(u, sL1);
       prefetch(sQ1, sO1, sQ2, sO2);
+      vstep(u, sL1);
       end_half();
       mstep(sQ1, sO1, sQ2, sO2, sD2);
       end_half();
     }
     if (u + 2 < T) {
       fetch(sQ1, sO1, sL1, sD1);
-      vstep(u + 1, sL2);
       prefetch(sQ2, sO2, sQ3, sO3);
+      vstep(u + 1, sL2);
       end_half();
       mstep(sQ2, sO2, sQ3, sO3, sD3);
       end_half();
@@ -1642,50 +1642,50 @@ __global__ __launch_bounds__(2 * NG * 64, 2) void bwd_dq_pp_kernel(BwdKParams p)
       fetch(u, sK3, sV3);
       mstep(sK0, sK1, sV1);
       end_half();
-      vstep(u, Tg);
       prefetch(sK1, sK2, sV2);
+      vstep(u, Tg);
       end_half();
       fetch(u + 1, sK0, sV0);
       mstep(sK1, sK2, sV2);
       end_half();
-      vstep(u + 1, Tg);
       prefetch(sK2, sK3, sV3);
+      vstep(u + 1, Tg);
       end_half();
       fetch(u + 2, sK1, sV1);
       mstep(sK2, sK3, sV3);
       end_half();
-      vstep(u + 2, Tg);
       prefetch(sK3, sK0, sV0);
+      vstep(u + 2, Tg);
       end_half();
       fetch(u + 3, sK2, sV2);
       mstep(sK3, sK0, sV0);
       end_half();
-      vstep(u + 3, Tg);
       prefetch(sK0, sK1, sV1);
+      vstep(u + 3, Tg);
       end_half();
     }
     if (u < Tg) {
       fetch(u, sK3, sV3);
       mstep(sK0, sK1, sV1);
       end_half();
-      vstep(u, Tg);
       prefetch(sK1, sK2, sV2);
+      vstep(u, Tg);
       end_half();
     }
     if (u + 1 < Tg) {
       fetch(u + 1, sK0, sV0);
       mstep(sK1, sK2, sV2);
       end_half();
-      vstep(u + 1, Tg);
       prefetch(sK2, sK3, sV3);
+      vstep(u + 1, Tg);
       end_half();
     }
     if (u + 2 < Tg) {
       fetch(u + 2, sK1, sV1);
       mstep(sK2, sK3, sV3);
       end_half();
-      vstep(u + 2, Tg);
       prefetch(sK3, sK0, sV0);
+      vstep(u + 2, Tg);
       end_half();
     }
     for (u += (u < Tg) + (u + 1 < Tg) + (u + 2 < Tg); u < T; ++u) {
@@ -1700,50 +1700,50 @@ __global__ __launch_bounds__(2 * NG * 64, 2) void bwd_dq_pp_kernel(BwdKParams p)
   } else {
     for (; u + 4 <= T; u += 4) {
       fetch(u, sK3, sV3);
-      vstep(u - 1, T);
       prefetch(sK0, sK1, sV1);
+      vstep(u - 1, T);
       end_half();
       mstep(sK0, sK1, sV1);
       end_half();
       fetch(u + 1, sK0, sV0);
-      vstep(u, T);
       prefetch(sK1, sK2, sV2);
+      vstep(u, T);
       end_half();
       mstep(sK1, sK2, sV2);
       end_half();
       fetch(u + 2, sK1, sV1);
-      vstep(u + 1, T);
       prefetch(sK2, sK3, sV3);
+      vstep(u + 1, T);
       end_half();
       mstep(sK2, sK3, sV3);
       end_half();
       fetch(u + 3, sK2, sV2);
-      vstep(u + 2, T);
       prefetch(sK3, sK0, sV0);
+      vstep(u + 2, T);
       end_half();
       mstep(sK3, sK0, sV0);
       end_half();
     }
     if (u < T) {
       fetch(u, sK3, sV3);
-      vstep(u - 1, T);
       prefetch(sK0, sK1, sV1);
+      vstep(u - 1, T);
       end_half();
       mstep(sK0, sK1, sV1);
       end_half();
     }
     if (u + 1 < T) {
       fetch(u + 1, sK0, sV0);
-      vstep(u, T);
       prefetch(sK1, sK2, sV2);
+      vstep(u, T);
       end_half();
       mstep(sK1, sK2, sV2);
       end_half();
     }
     if (u + 2 < T) {
       fetch(u + 2, sK1, sV1);
-      vstep(u + 1, T);
       prefetch(sK2, sK3, sV3);
+      vstep(u + 1, T);
       end_half();
       mstep(sK2, sK3, sV3);
       end_half();
