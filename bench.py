@@ -85,6 +85,9 @@ def parse_args():
                     help="skip the fp8, grouped-query, decode, dropout and per-workload "
                          "measurements that follow the timed step (for profiler runs "
                          "that should see the step only)")
+    ap.add_argument("--paths", default="fp8,gqa,decode,dropout,configs",
+                    help="comma-separated extra measurements to run after the timed "
+                         "step (a subset of the default; for profiler runs of one path)")
     ap.add_argument("--workload", choices=sorted(WORKLOADS), default="step",
                     help="time another workload in place of the step (for profiler runs: "
                          "bwd4096 = B4 H16 N4096 d128 causal forward + backward, fp8 = the "
@@ -677,11 +680,14 @@ def main():
     }
     progress(f"timed step: {ms_per_step:.3f} ms, {value:.1f} TFLOP/s")
     if not args.no_extra_paths:
+        wanted = set(args.paths.split(","))
         for key, fn in (("fp8", lambda: measure_fp8(ea, torch)),
                         ("gqa", lambda: measure_gqa(ea, torch, attn_synth)),
                         ("decode", lambda: measure_decode(ea, torch, attn_synth)),
                         ("dropout", lambda: measure_dropout(ea, torch, attn_synth)),
                         ("configs", lambda: measure_configs(ea, torch))):
+            if key not in wanted:
+                continue
             out[key] = fn()
             progress(f"measured {key}")
     if args.hbm_copy_mib > 0:
