@@ -512,14 +512,28 @@ def measure_decode(ea, torch, attn_synth, reps=20):
 
 
 def cpu_model() -> str:
-    """The host CPU's model name from /proc/cpuinfo (empty if unreadable)."""
+    """The host CPU from /proc/cpuinfo: model name, family and model numbers
+    (a virtual machine may report only a generic name), the nominal clock
+    implied by BogoMIPS (twice the TSC rate on x86) and whether a hypervisor
+    is present; empty if unreadable."""
+    info = {}
     try:
         for line in open("/proc/cpuinfo"):
-            if line.startswith("model name"):
-                return line.split(":", 1)[1].strip()
+            if ":" in line:
+                k, v = (x.strip() for x in line.split(":", 1))
+                info.setdefault(k, v)
     except OSError:
+        return ""
+    out = info.get("model name", "")
+    if "cpu family" in info and "model" in info:
+        out += f" (cpu family {info['cpu family']}, model {info['model']})"
+    try:
+        out += f", {float(info['bogomips']) / 2000:.2f} GHz nominal"
+    except (KeyError, ValueError):
         pass
-    return ""
+    if "hypervisor" in info.get("flags", "").split():
+        out += ", virtual machine"
+    return out
 
 
 def cpu_baseline(attn_synth, seconds_budget=20.0):
