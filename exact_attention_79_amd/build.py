@@ -17,8 +17,7 @@ LIB = os.path.join(HERE, "libattn.so")
 BUILD_DIR = os.path.join(HERE, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["attn_api.hip", "attn_fwd.hip", "attn_bwd.hip", "attn_fwd_fp8.hip",
-           "attn_decode.hip"]
+SOURCES = ["attn_api.hip", "attn_fwd.hip", "attn_bwd.hip", "attn_decode.hip"]
 
 # Packed-fp32 VALU instructions are disabled for all device code.
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -243,6 +243,53 @@ __device__ __forceinline__ void vec_load_lds(__amdgpu_buffer_rsrc_t rs, int row0
                                            0);
 }
 
+// ---- e4m3 inputs widened to bf16 ----
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Eight e4m3 codes (the bytes of x0, then those of x1) widened to bf16, which
+// holds every e4m3 value exactly.  Q and K go through this same routine, so
+// the order it gives the eight values in is the same on both sides of a dot
+// product.
+__device__ __forceinline__ bf16x8 e4m3x8_to_bf16(uint32_t x0, uint32_t x1) {
+  const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)x0, 1.f, false);
+  const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)x0, 1.f, true);
+  const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)x1, 1.f, false);
+  const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)x1, 1.f, true);
+  return (bf16x8){a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+// The same widening to fp16 (which also holds every e4m3 value exactly).
+__device__ __forceinline__ f16x8 e4m3x8_to_f16(uint32_t x0, uint32_t x1) {
+  const f16x2 a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)x0, 1.f, false);
+  const f16x2 b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)x0, 1.f, true);
+  const f16x2 c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)x1, 1.f, false);
+  const f16x2 d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)x1, 1.f, true);
+  return (f16x8){a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+// Global -> LDS copy of rows row0 .. row0+ROWS-1 of an e4m3 [rows][D] head
+// by NW waves, unswizzled: LDS chunk c of the tile holds the tile's 16-byte
+// chunk c (row c / (D/16)), so each wave instruction moves 1 KB of
+// consecutive bytes.  Rows past the head's end read as zero.
+template <int D, int ROWS, int NW>
+__device__ __forceinline__ void tile_stage_lds8(const uint8_t* head, uint32_t head_bytes,
+                                                int row0, uint8_t* t, int w, int lane) {
+  constexpr int ROUNDS = ROWS * D / 16 / (64 * NW);
+  static_assert(ROUNDS >= 1 && (ROWS * D / 16) % (64 * NW) == 0, "tile split");
+  const uint32_t rows = head_bytes / D, r0 = (uint32_t)row0;
+  const auto rs = make_rsrc(head + (size_t)r0 * D, r0 < rows ? head_bytes - r0 * D : 0u);
+#pragma unroll
+  for (int i = 0; i < ROUNDS; ++i) {
+    const int base = (i * NW + w) * 64;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS_AS void*)(t + base * 16), 16,
+                                             (int)((uint32_t)(base + lane) * 16u), 0, 0, 0);
+  }
+}
+
 // s_waitcnt immediate that waits until at most `n` vector-memory operations
 // of this wave are outstanding (LDS and export counters not waited on).
 __host__ __device__ constexpr int waitcnt_vm(int n) {

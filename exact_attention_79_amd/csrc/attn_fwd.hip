@@ -1,4 +1,4 @@
-// attn_fwd.hip -- bf16 forward kernel for gfx950.
+// attn_fwd.hip -- bf16 and fp8-input forward kernels for gfx950.
 //
 // Method (FLASH-ATTN page, FlashAttention-2 section): one workgroup owns a
 // block of B_r queries and walks the K/V blocks of its head in order, keeping
@@ -35,8 +35,11 @@
 //    that XCD's L2) and, with the causal mask, the longest query blocks run
 //    first.
 // fwd_bf16_kernel serves dropout and grids of fewer than four 256-query
-// workgroups; otherwise the forward runs fwd_pp_kernel below, which keeps this mapping but separates each wave's
-// matrix and vector work into alternating half-steps (ping-pong).
+// workgroups; otherwise the forward runs fwd_pp_kernel below, which keeps
+// this mapping but separates each wave's matrix and vector work into
+// alternating half-steps (ping-pong).  fwd_fp8_pp_kernel is the same kernel
+// for e4m3 inputs (the FlashAttention-3 summary's "Low-precision with FP8"
+// part), which it widens in LDS.
 #include "attn_device.hpp"
 #include "attn_kernels.hpp"
 
@@ -54,6 +57,13 @@ struct FwdKParams {
   float scale;
   int causal, window, out_f32;
   Dropout drop;
+  // e4m3 inputs (fwd_pp_kernel with IN > 0; q, k, v then point at codes):
+  // descales per tensor, or per block (IN = 2): qs [BH][ceil(N/128)], ks and
+  // vs [B*Hkv][ceil(N/64)].
+  float q_descale, k_descale, v_descale;
+  const float* qs;
+  const float* ks;
+  const float* vs;
 };
 
 // DROP: dropout on P (the keep bytes of attn_device.hpp); l and L stay those
@@ -360,8 +370,25 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdKParams p) {
 // Under the causal mask the first group (the workgroup's first 128 queries)
 // stops computing after the last tile its queries see and from then on only
 // fetches its share of the tiles and joins the barriers.
-template <int D, int NG, int BC>
-__global__ __launch_bounds__(2 * NG * 64, 2) void fwd_pp_kernel(FwdKParams p) {
+// IN: 0 = bf16 inputs; 1 = e4m3 codes with one descale per tensor; 2 = e4m3
+// codes with one descale per block.  With e4m3 inputs the products run on
+// the 16-bit MFMAs, S = K Q^T in bf16 and O~ += V^T P^T in fp16, both of
+// which hold every e4m3 value exactly.  The fp8 MFMA's sum of 64 products
+// keeps too few bits below its largest product for the scores of inputs with
+// outlier channels (their error then reaches the output amplified by the
+// outlier channels of V), and an accurate fp8 P V needs P as two e4m3 terms,
+// i.e. as many MFMA cycles as a 16-bit P V and more vector work.  P is fp16
+// rather than bf16 because its rounding error reaches O multiplied by |V|,
+// which the outlier channels make large.  Each K and V tile is copied to LDS
+// as e4m3 (a staging ring of three slots) and widened there to the bf16 tile
+// layout by one wave group during its matrix half-step, so that the rest of
+// the kernel is the bf16 one.  The descales fold into the score scale and the
+// output scale (per tensor), or into each tile's score scale and weights (per
+// block; the weights then carry the value descale, which must stay below
+// 2^8 so that they stay inside the fp16 range).
+template <int D, int NG, int BC, int IN>
+__device__ __forceinline__ void fwd_pp_body(const FwdKParams& p) {
+  constexpr bool F8 = IN != 0, BLOCKS = IN == 2;
   constexpr int MT = BC / 32;          // score tiles of 32 keys per K/V tile
   constexpr int NWV = 2 * NG;          // waves
   constexpr int BR = 32 * NWV;         // queries per workgroup
@@ -375,6 +402,11 @@ __global__ __launch_bounds__(2 * NG * 64, 2) void fwd_pp_kernel(FwdKParams p) {
   __shared__ __attribute__((aligned(16))) __bf16 sV0[BC * D];
   __shared__ __attribute__((aligned(16))) __bf16 sV1[BC * D];
   __shared__ __attribute__((aligned(16))) __bf16 sV2[BC * D];
+  // e4m3 staging slots: the K tile, then the V tile, of one fetch.
+  constexpr int SS = F8 ? 2 * BC * D : 16;
+  __shared__ __attribute__((aligned(16))) uint8_t sS0[SS];
+  __shared__ __attribute__((aligned(16))) uint8_t sS1[SS];
+  __shared__ __attribute__((aligned(16))) uint8_t sS2[SS];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, kept scalar
@@ -394,12 +426,26 @@ __global__ __launch_bounds__(2 * NG * 64, 2) void fwd_pp_kernel(FwdKParams p) {
   const auto rq = make_rsrc(p.q + head, head_bytes);
   const __bf16* kh = p.k + kv_off;
   const __bf16* vh = p.v + kv_off;
+  // e4m3 heads: one byte per element.
+  const uint32_t head_bytes8 = (uint32_t)N * D;
+  const uint8_t* kh8 = (const uint8_t*)p.k + kv_off;
+  const uint8_t* vh8 = (const uint8_t*)p.v + kv_off;
 
   bf16x8 qop[KS];
+  if constexpr (F8) {
+    // Channels 16 ks + 8 h .. +7 of the query, widened.
+    const auto rq8 = make_rsrc((const uint8_t*)p.q + head, head_bytes8);
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks)
-    qop[ks] = __builtin_bit_cast(
-        bf16x8, buf_load16(rq, (uint32_t)(my_q * D + 16 * ks + 8 * h) * 2u));
+    for (int ks = 0; ks < KS; ++ks) {
+      const u32x4 x = buf_load16(rq8, (uint32_t)(my_q * D + 16 * ks));
+      qop[ks] = e4m3x8_to_bf16(h ? x[2] : x[0], h ? x[3] : x[1]);
+    }
+  } else {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      qop[ks] = __builtin_bit_cast(
+          bf16x8, buf_load16(rq, (uint32_t)(my_q * D + 16 * ks + 8 * h) * 2u));
+  }
 
   const int q_last = min(q0 + BR, N) - 1;
   int kv_lo = 0, kv_hi = N;
@@ -418,6 +464,32 @@ __global__ __launch_bounds__(2 * NG * 64, 2) void fwd_pp_kernel(FwdKParams p) {
   const float s2 = p.scale * kLog2e;
   const float tau = 8.0f / s2;
   const TrCoord trc(lane);
+  // e4m3 inputs: the running max is kept in base-2 logit units (so that
+  // tiles with different key descales compare directly); tile t's code
+  // products are scaled by st(t), and with block descales log2 of its value
+  // descale, lv(t), is folded into its weights.
+  const int kvh = kv_head(bh, p.H, p.Hkv);
+  const int n_kb = (N + 63) / 64;
+  float s2q = 0.f, s2k = 0.f;
+  if constexpr (F8) {
+    s2q = s2 * (BLOCKS ? p.qs[(size_t)bh * ((N + 127) / 128) + (q0 + (lead ? 0 : 32 * NG)) / 128]
+                       : p.q_descale);
+    s2k = s2q * p.k_descale;
+  }
+  // Block descales: fetch(u) loads those of tile t_lo + u + 2 into set
+  // u % 3, which V(u+1) reads.  They are read through the constant address
+  // space, which makes them scalar loads (vector loads would join the
+  // staging loads' in-order wait count); nothing writes them while the
+  // kernel runs.
+  typedef const __attribute__((address_space(4))) float* ConstF;
+  float dks[3] = {1.f, 1.f, 1.f}, dvs[3] = {1.f, 1.f, 1.f};
+  auto load_scales = [&](int t, int set) {
+    if constexpr (BLOCKS) {
+      const int i = kvh * n_kb + min(t * BC / 64, n_kb - 1);
+      dks[set] = ((ConstF)p.ks)[i];
+      dvs[set] = ((ConstF)p.vs)[i];
+    }
+  };
 
   int hi_key = N - 1, lo_key = 0;
   if (p.causal) hi_key = min(hi_key, my_q);
@@ -478,6 +550,46 @@ __global__ __launch_bounds__(2 * NG * 64, 2) void fwd_pp_kernel(FwdKParams p) {
   bf16x8 pop[BC / 16];
   // Row max of snx (masked), running max moved past it, O~ and l rescaled,
   // then the probabilities of snx into pop and their sum into l.
+  // set: the descale set holding this tile's block descales.
+  // Block descales: the score scale, log2 of the value descale and its
+  // inverse for the next softmax step, formed from descale set `set` during
+  // the matrix half-step before it (where the vector units have time).
+  float tsc = 0.f, tlv = 0.f, trl = 1.f;
+  auto tile_consts = [&](int set) {
+    if constexpr (BLOCKS) {
+      tsc = s2q * dks[set];
+      tlv = __builtin_amdgcn_logf(dvs[set]);
+      trl = fast_exp2(-tlv);
+    }
+  };
+  auto softmax_step_f8 = [&]() {
+    float mx = snx[0][0];
+#pragma unroll
+    for (int e = 1; e < 16 * MT; ++e) mx = fmaxf(mx, snx[e >> 4][e & 15]);
+    const float sc = BLOCKS ? tsc : s2k, lvt = BLOCKS ? tlv : 0.f;
+    mx = halves_max(mx) * sc;
+    const float m_new = (mx > m_run + 8.f) ? mx : m_run;
+    const float alpha = fast_exp2(m_run - m_new);
+    m_run = m_new;
+    if (__ballot(alpha != 1.f)) {
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
+    }
+    const float mb = m_run - lvt;
+    float lsum;
+#pragma unroll
+    for (int e = 0; e < 16 * MT; e += 2) {  // fp16 weights, two per convert
+      const float x0 = fast_exp2(fmaf(snx[e >> 4][e & 15], sc, -mb));
+      const float x1 = fast_exp2(fmaf(snx[e >> 4][(e & 15) + 1], sc, -mb));
+      lsum = e == 0 ? x0 + x1 : lsum + x0 + x1;
+      const auto hb = __builtin_bit_cast(bf16x2, (f16x2){(_Float16)x0, (_Float16)x1});
+      pop[e >> 3][e & 7] = hb[0];
+      pop[e >> 3][(e & 7) + 1] = hb[1];
+    }
+    // The weights carry the value descale; l sums them without it.
+    l_run += BLOCKS ? lsum * trl : lsum;
+  };
   auto softmax_step = [&]() {
     float mx = snx[0][0];
 #pragma unroll
@@ -502,15 +614,59 @@ __global__ __launch_bounds__(2 * NG * 64, 2) void fwd_pp_kernel(FwdKParams p) {
     l_run += lsum;
   };
 
+  // e4m3 tiles: the first group stages and widens the K tiles, the second
+  // the V tiles; each lane widens one 16-byte chunk (16 codes) of a tile.
+  const int wg = lead ? w : w - NG;  // wave index inside its group
+  static_assert(!F8 || (BC * D / 16 == 64 * NG && 32 * NG == 128), "e4m3 tile split");
+  const int wpc = wg * 64 + lane;  // the chunk this lane widens
+  const int wrow = wpc / (D / 16), wch = 2 * (wpc % (D / 16));
+  const int woff0 = tile_off<D>(wrow, wch), woff1 = tile_off<D>(wrow, wch + 1);
+  auto stage = [&](int t, uint8_t* slot) {  // this group's tile t into a staging slot
+    if (lead) tile_stage_lds8<D, BC, NG>(kh8, head_bytes8, t * BC, slot, wg, lane);
+    else tile_stage_lds8<D, BC, NG>(vh8, head_bytes8, t * BC, slot + BC * D, wg, lane);
+  };
+  // K is widened to bf16, V to fp16 (stored in the same 16-bit tile layout).
+  auto widen8 = [&](uint32_t x0, uint32_t x1) {
+    return lead ? e4m3x8_to_bf16(x0, x1) : __builtin_bit_cast(bf16x8, e4m3x8_to_f16(x0, x1));
+  };
+  auto widen = [&](const uint8_t* slot, __bf16* dst) {  // this group's half of a slot
+    const u32x4 x = *(const u32x4*)&slot[(lead ? 0 : BC * D) + wpc * 16];
+    *(bf16x8*)&dst[woff0] = widen8(x[0], x[1]);
+    *(bf16x8*)&dst[woff1] = widen8(x[2], x[3]);
+  };
+
   // Prologue: K_0, K_1, K_2, V_0, V_1 (tile j = t_lo + j); S of tile 0 and
-  // its probabilities.
-  tile_load_lds<D, BC, NWV>(kh, head_bytes, t_lo * BC, sK0, w, lane);
-  tile_load_lds<D, BC, NWV>(vh, head_bytes, t_lo * BC, sV0, w, lane);
-  tile_load_lds<D, BC, NWV>(kh, head_bytes, (t_lo + 1) * BC, sK1, w, lane);
-  tile_load_lds<D, BC, NWV>(vh, head_bytes, (t_lo + 1) * BC, sV1, w, lane);
-  tile_load_lds<D, BC, NWV>(kh, head_bytes, (t_lo + 2) * BC, sK2, w, lane);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
+  // its probabilities.  e4m3: K_0, K_1, V_0, V_1 staged and widened here (K_1
+  // staged in K_2's bf16 slot, which is free until K_2 is widened), K_2 and
+  // V_1 staged in slot 1, K_3 and V_2 in slot 2.
+  if constexpr (F8) {
+    stage(t_lo, sS0);
+    load_scales(t_lo, 0);
+    load_scales(t_lo + 1, 2);
+    if (lead) stage(t_lo + 1, (uint8_t*)sK2);
+    stage(t_lo + 2, lead ? sS1 : sS2);  // K_2 / V_2
+    stage(t_lo + (lead ? 3 : 1), lead ? sS2 : sS1);  // K_3 / V_1
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    widen(sS0, lead ? sK0 : sV0);
+    if (lead) {
+      const u32x4 x = *(const u32x4*)&((const uint8_t*)sK2)[wpc * 16];
+      *(bf16x8*)&sK1[woff0] = e4m3x8_to_bf16(x[0], x[1]);
+      *(bf16x8*)&sK1[woff1] = e4m3x8_to_bf16(x[2], x[3]);
+    } else {
+      widen(sS1, sV1);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  } else {
+    tile_load_lds<D, BC, NWV>(kh, head_bytes, t_lo * BC, sK0, w, lane);
+    tile_load_lds<D, BC, NWV>(vh, head_bytes, t_lo * BC, sV0, w, lane);
+    tile_load_lds<D, BC, NWV>(kh, head_bytes, (t_lo + 1) * BC, sK1, w, lane);
+    tile_load_lds<D, BC, NWV>(vh, head_bytes, (t_lo + 1) * BC, sV1, w, lane);
+    tile_load_lds<D, BC, NWV>(kh, head_bytes, (t_lo + 2) * BC, sK2, w, lane);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     snx[mt] = (f32x16){};
@@ -519,20 +675,39 @@ __global__ __launch_bounds__(2 * NG * 64, 2) void fwd_pp_kernel(FwdKParams p) {
       snx[mt] = mfma32(tile_row8<D>(sK0, 32 * mt + n, 2 * ks + h), qop[ks], snx[mt]);
   }
   mask_tile(t_lo, snx);
-  softmax_step();
+  if constexpr (F8) {
+    tile_consts(0);
+    softmax_step_f8();
+  } else {
+    softmax_step();
+  }
   __syncthreads();  // every wave has read K_0 before its slot is refilled
 
   // Half-step end: the wait for the fetches issued two half-steps earlier
   // (this wave's two latest stay in flight), then the barrier; so the tiles
   // that M(u+1) reads are in LDS for every wave from the half-step before it.
+  // e4m3: one staging load per wave and fetch, so the wait leaves that one
+  // in flight, and the widening stores must be done before the barrier.
   auto end_half = [&]() {
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(2));
+    if constexpr (F8) __builtin_amdgcn_s_waitcnt(waitcnt_vm(1) & ~(0xF << 8));
+    else __builtin_amdgcn_s_waitcnt(waitcnt_vm(2));
     __builtin_amdgcn_s_barrier();
   };
   // Fetches of even half-step 2u: K_{u+3} into K_u's slot, V_{u+2} into V_{u-1}'s.
-  auto fetch = [&](int u, __bf16* Kf, __bf16* Vf) {
-    tile_load_lds<D, BC, NWV>(kh, head_bytes, (t_lo + u + 3) * BC, Kf, w, lane);
-    tile_load_lds<D, BC, NWV>(vh, head_bytes, (t_lo + u + 2) * BC, Vf, w, lane);
+  // e4m3: K_{u+4} and V_{u+3} into staging slot u % 3 (Kf: that slot; Vf
+  // unused); the first group widens K_{u+2} during M(u) (half-step 2u), the
+  // second V_{u+2} during M(u) (half-step 2u + 1), each from the slot that
+  // fetch(u-2) or fetch(u-1) filled.
+  auto fetch = [&](int u, auto* Kf, auto* Vf) {
+    if constexpr (F8) {
+      (void)Vf;
+      stage(t_lo + u + (lead ? 4 : 3), (uint8_t*)Kf);
+      // (Kf is staging slot u % 3, and so names the descale set.)
+      load_scales(t_lo + u + 2, (uint8_t*)Kf == sS0 ? 0 : (uint8_t*)Kf == sS1 ? 1 : 2);
+    } else {
+      tile_load_lds<D, BC, NWV>(kh, head_bytes, (t_lo + u + 3) * BC, Kf, w, lane);
+      tile_load_lds<D, BC, NWV>(vh, head_bytes, (t_lo + u + 2) * BC, Vf, w, lane);
+    }
   };
   // M(u): S of tile u+1 from Kn (into snx) and O~ += V_u^T P~_u^T from Vc,
   // the two kinds of MFMA alternating; operand i is read AHEAD MFMAs before
@@ -547,18 +722,35 @@ __global__ __launch_bounds__(2 * NG * 64, 2) void fwd_pp_kernel(FwdKParams p) {
 #pragma unroll
     for (int i = 0; i < AHEAD; ++i) issue(i, Kn, Vc);
   };
-  auto mstep = [&](const __bf16* Kn, const __bf16* Vc) {
+  // Wsrc, Wdst (e4m3): the staging slot and bf16 slot of this group's
+  // widening, spread over three of the half-step's MFMAs.
+  // vset: the descale set of V(u)'s tile, t_lo + u + 1, which fetch(u-1)
+  // filled: (u + 2) % 3 (a constant at every call).
+  auto mstep = [&](const __bf16* Kn, const __bf16* Vc, const uint8_t* Wsrc = nullptr,
+                   __bf16* Wdst = nullptr, int vset = 0) {
+    tile_consts(vset);
     hide();
     f32x16 s[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) s[mt] = (f32x16){};
+    u32x4 wx;
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < 2 * NSM; ++i) {
       if (i + AHEAD < 2 * NSM) issue(i + AHEAD, Kn, Vc);
+      if constexpr (F8) {
+        if (i == 2) wx = *(const u32x4*)&Wsrc[(lead ? 0 : BC * D) + wpc * 16];
+        if (i == 6) *(bf16x8*)&Wdst[woff0] = widen8(wx[0], wx[1]);
+        if (i == 10) *(bf16x8*)&Wdst[woff1] = widen8(wx[2], wx[3]);
+      }
       if (i & 1) {
         const int j = i >> 1;
-        oacc[j % DT] = mfma32(va[j], pop[j / DT], oacc[j % DT]);
+        if constexpr (F8)
+          oacc[j % DT] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+              __builtin_bit_cast(f16x8, va[j]), __builtin_bit_cast(f16x8, pop[j / DT]),
+              oacc[j % DT], 0, 0, 0);
+        else
+          oacc[j % DT] = mfma32(va[j], pop[j / DT], oacc[j % DT]);
       } else {
         const int si = i >> 1;
         s[si / KS] = mfma32(ka[si], qop[si % KS], s[si / KS]);
@@ -573,7 +765,8 @@ __global__ __launch_bounds__(2 * NG * 64, 2) void fwd_pp_kernel(FwdKParams p) {
   auto vstep = [&](int u, int Tg) {
     if (u >= 0 && u + 1 < Tg) {
       mask_tile(t_lo + u + 1, snx);
-      softmax_step();
+      if constexpr (F8) softmax_step_f8();
+      else softmax_step();
     }
   };
 
@@ -588,84 +781,102 @@ __global__ __launch_bounds__(2 * NG * 64, 2) void fwd_pp_kernel(FwdKParams p) {
     const int Tg = p.causal ? min(T, (q0 + 32 * NG - 1) / BC - t_lo + 1) : T;
     prefetch(sK1, sV0);
     for (; u + 3 <= Tg; u += 3) {
-      fetch(u, sK0, sV2);
-      mstep(sK1, sV0);
+      if constexpr (F8) fetch(u, sS0, sV2), mstep(sK1, sV0, sS1, sK2, 2);
+      else fetch(u, sK0, sV2), mstep(sK1, sV0);
       end_half();
       prefetch(sK2, sV1);
       vstep(u, Tg);
       end_half();
-      fetch(u + 1, sK1, sV0);
-      mstep(sK2, sV1);
+      if constexpr (F8) fetch(u + 1, sS1, sV0), mstep(sK2, sV1, sS2, sK0, 0);
+      else fetch(u + 1, sK1, sV0), mstep(sK2, sV1);
       end_half();
       prefetch(sK0, sV2);
       vstep(u + 1, Tg);
       end_half();
-      fetch(u + 2, sK2, sV1);
-      mstep(sK0, sV2);
+      if constexpr (F8) fetch(u + 2, sS2, sV1), mstep(sK0, sV2, sS0, sK1, 1);
+      else fetch(u + 2, sK2, sV1), mstep(sK0, sV2);
       end_half();
       prefetch(sK1, sV0);
       vstep(u + 2, Tg);
       end_half();
     }
     if (u < Tg) {
-      fetch(u, sK0, sV2);
-      mstep(sK1, sV0);
+      if constexpr (F8) fetch(u, sS0, sV2), mstep(sK1, sV0, sS1, sK2, 2);
+      else fetch(u, sK0, sV2), mstep(sK1, sV0);
       end_half();
       prefetch(sK2, sV1);
       vstep(u, Tg);
       end_half();
     }
     if (u + 1 < Tg) {
-      fetch(u + 1, sK1, sV0);
-      mstep(sK2, sV1);
+      if constexpr (F8) fetch(u + 1, sS1, sV0), mstep(sK2, sV1, sS2, sK0, 0);
+      else fetch(u + 1, sK1, sV0), mstep(sK2, sV1);
       end_half();
       prefetch(sK0, sV2);
       vstep(u + 1, Tg);
       end_half();
     }
     for (u += (u < Tg) + (u + 1 < Tg); u < T; ++u) {
-      if (u % 3 == 0) fetch(u, sK0, sV2);
-      else if (u % 3 == 1) fetch(u, sK1, sV0);
-      else fetch(u, sK2, sV1);
+      if constexpr (F8) {
+        // Still widens the K tiles that the other group reads.
+        // (Widening first: its reads then follow no pending copy.)
+        if (u % 3 == 0) widen(sS1, sK2), fetch(u, sS0, sV2);
+        else if (u % 3 == 1) widen(sS2, sK0), fetch(u, sS1, sV0);
+        else widen(sS0, sK1), fetch(u, sS2, sV1);
+      } else {
+        if (u % 3 == 0) fetch(u, sK0, sV2);
+        else if (u % 3 == 1) fetch(u, sK1, sV0);
+        else fetch(u, sK2, sV1);
+      }
       end_half();
       end_half();
     }
     end_half();
   } else {
     for (; u + 3 <= T; u += 3) {
-      fetch(u, sK0, sV2);
+      if constexpr (F8) fetch(u, sS0, sV2);
+      else fetch(u, sK0, sV2);
       prefetch(sK1, sV0);
       vstep(u - 1, T);
       end_half();
-      mstep(sK1, sV0);
+      if constexpr (F8) mstep(sK1, sV0, sS2, sV2, 2);
+      else mstep(sK1, sV0);
       end_half();
-      fetch(u + 1, sK1, sV0);
+      if constexpr (F8) fetch(u + 1, sS1, sV0);
+      else fetch(u + 1, sK1, sV0);
       prefetch(sK2, sV1);
       vstep(u, T);
       end_half();
-      mstep(sK2, sV1);
+      if constexpr (F8) mstep(sK2, sV1, sS0, sV0, 0);
+      else mstep(sK2, sV1);
       end_half();
-      fetch(u + 2, sK2, sV1);
+      if constexpr (F8) fetch(u + 2, sS2, sV1);
+      else fetch(u + 2, sK2, sV1);
       prefetch(sK0, sV2);
       vstep(u + 1, T);
       end_half();
-      mstep(sK0, sV2);
+      if constexpr (F8) mstep(sK0, sV2, sS1, sV1, 1);
+      else mstep(sK0, sV2);
       end_half();
     }
     if (u < T) {
-      fetch(u, sK0, sV2);
+      if constexpr (F8) fetch(u, sS0, sV2);
+      else fetch(u, sK0, sV2);
       prefetch(sK1, sV0);
       vstep(u - 1, T);
       end_half();
-      mstep(sK1, sV0);
+      if constexpr (F8) mstep(sK1, sV0, sS2, sV2, 2);
+      else mstep(sK1, sV0);
       end_half();
     }
     if (u + 1 < T) {
-      fetch(u + 1, sK1, sV0);
+      if constexpr (F8) fetch(u + 1, sS1, sV0);
+      else fetch(u + 1, sK1, sV0);
       prefetch(sK2, sV1);
       vstep(u, T);
       end_half();
-      mstep(sK2, sV1);
+      if constexpr (F8) mstep(sK2, sV1, sS0, sV0, 0);
+      else mstep(sK2, sV1);
       end_half();
     }
     end_half();
@@ -674,7 +885,7 @@ __global__ __launch_bounds__(2 * NG * 64, 2) void fwd_pp_kernel(FwdKParams p) {
 
   const float l_tot = halves_sum(l_run);
   if (my_q < N) {
-    const float inv = 1.f / l_tot;
+    const float inv = (IN == 1 ? p.v_descale : 1.f) / l_tot;
     const size_t row = head + (size_t)my_q * D;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
@@ -691,8 +902,18 @@ __global__ __launch_bounds__(2 * NG * 64, 2) void fwd_pp_kernel(FwdKParams p) {
         }
       }
     if (h == 0 && p.lse)
-      p.lse[(size_t)bh * N + my_q] = (m_run * s2 + __builtin_amdgcn_logf(l_tot)) * kLn2;
+      p.lse[(size_t)bh * N + my_q] =
+          ((F8 ? m_run : m_run * s2) + __builtin_amdgcn_logf(l_tot)) * kLn2;
   }
+}
+
+template <int D, int NG, int BC>
+__global__ __launch_bounds__(2 * NG * 64, 2) void fwd_pp_kernel(FwdKParams p) {
+  fwd_pp_body<D, NG, BC, 0>(p);
+}
+template <int D, int NG, int BC, bool BLOCKS>
+__global__ __launch_bounds__(2 * NG * 64, 2) void fwd_fp8_pp_kernel(FwdKParams p) {
+  fwd_pp_body<D, NG, BC, BLOCKS ? 2 : 1>(p);
 }
 
 // Kernel parameters for workgroups of `rows` queries.
@@ -712,6 +933,8 @@ static FwdKParams fwd_params(const FwdArgs& a, int rows) {
   p.window = a.window;
   p.out_f32 = a.out_f32;
   p.drop = make_dropout(a.drop);
+  p.q_descale = p.k_descale = p.v_descale = 1.f;
+  p.qs = p.ks = p.vs = nullptr;
   return p;
 }
 
@@ -732,6 +955,30 @@ static hipError_t launch_fwd_pp(const FwdArgs& a, hipStream_t stream, const char
   return go<fwd_pp_kernel<D, NG, BC>>(name, kname("attn::fwd_pp_kernel", D, NG, BC),
                                       dim3((unsigned)(a.BH * p.n_qtiles)), dim3(2 * NG * 64),
                                       stream, p);
+}
+
+// e4m3 inputs on the ping-pong kernel (same tiles as bf16).
+template <int D, int BC>
+static hipError_t launch_fwd_fp8_d(const FwdArgs& a, hipStream_t stream, const char** name) {
+  constexpr int NG = 4;
+  FwdKParams p = fwd_params(a, 64 * NG);
+  p.q_descale = a.q_descale;
+  p.k_descale = a.k_descale;
+  p.v_descale = a.v_descale;
+  p.qs = a.q_scales;
+  p.ks = a.k_scales;
+  p.vs = a.v_scales;
+  const dim3 grid((unsigned)(a.BH * p.n_qtiles)), block(2 * NG * 64);
+  if (a.q_scales)
+    return go<fwd_fp8_pp_kernel<D, NG, BC, true>>(
+        name, kname("attn::fwd_fp8_pp_kernel", D, NG, BC, true), grid, block, stream, p);
+  return go<fwd_fp8_pp_kernel<D, NG, BC, false>>(
+      name, kname("attn::fwd_fp8_pp_kernel", D, NG, BC, false), grid, block, stream, p);
+}
+
+hipError_t launch_fwd_fp8(const FwdArgs& a, hipStream_t stream, const char** name) {
+  if (a.d == 128) return launch_fwd_fp8_d<128, 32>(a, stream, name);
+  return launch_fwd_fp8_d<64, 64>(a, stream, name);
 }
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream, const char** name) {

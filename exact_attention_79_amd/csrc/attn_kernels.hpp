@@ -141,6 +141,7 @@ hipError_t go(const char** name, const KName& sym, dim3 grid, dim3 block, hipStr
 // attention arithmetic) for these arguments.
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream, const char** name = nullptr);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+// e4m3 inputs, widened in LDS, on the ping-pong forward (attn_fwd.hip).
 hipError_t launch_fwd_fp8(const FwdArgs& a, hipStream_t stream, const char** name = nullptr);
 // The backward stages; launch_bwd = dq (which also fills the workspace),
 // then dkdv.  preprocess fills the workspace on its own.

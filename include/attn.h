@@ -176,14 +176,15 @@ attn_status attn_bwd_preprocess(const attn_desc* desc, const void* o,
                                 size_t workspace_bytes, void* stream);
 
 /* Forward with fp8 inputs (FLASH-ATTN page, FlashAttention-3 summary,
- * "Low-precision with FP8": both products on the fp8 matrix cores, one scale
- * per tensor).  q8 [B,H,N,d] and k8, v8 [B,H_kv,N,d] are E4M3 codes; the inputs are
- * code * descale.  Within each 64-key tile the probabilities of every query
- * row are scaled by the power of two that brings the row's largest one into
- * [128, 256) and are carried as two E4M3 terms, hi + 2^-4 lo, through the
- * P V product; the matrix core's per-lane block scale removes the power of
- * two again, so the fp32 accumulator holds the unscaled product.  o and lse
- * as in attn_fwd. */
+ * "Low-precision with FP8": E4M3 inputs with one scale per tensor).  q8
+ * [B,H,N,d] and k8, v8 [B,H_kv,N,d] are E4M3 codes; the inputs are
+ * code * descale.  Both products run on the 16-bit matrix cores: each tile
+ * is widened in LDS, exactly, to bf16 (Q, K) or fp16 (V); the scores are
+ * summed in fp32 and the probabilities enter the P V product as fp16.  (The
+ * fp8 matrix instruction keeps too few bits of its 64-product sums for
+ * inputs with outlier channels, and an fp8 P accurate enough for them needs
+ * two E4M3 terms, i.e. as many matrix cycles as fp16.)  o and lse as in
+ * attn_fwd. */
 attn_status attn_fwd_fp8(const attn_desc* desc, const uint8_t* q8,
                          const uint8_t* k8, const uint8_t* v8, float q_descale,
                          float k_descale, float v_descale, void* o,
@@ -198,7 +199,8 @@ attn_status attn_fwd_fp8(const attn_desc* desc, const uint8_t* q8,
  *   k_descales : fp32 [B,H_kv,ceil(N/64)] (key block kb covers rows 64 kb ..)
  *   v_descales : fp32 [B,H_kv,ceil(N/64)]
  * The real inputs are code * the descale of the code's block; every descale
- * must be finite and > 0 (device memory: not checked).  Incoherent processing
+ * must be finite and > 0, and every value descale below 255 (the fp16
+ * probabilities carry it); device memory, so not checked.  Incoherent processing
  * (multiplying Q and K by one random orthogonal matrix before quantising,
  * same page) needs nothing from the kernel, since (QM)(KM)^T = QK^T: the
  * caller transforms and quantises.  Other arguments as attn_fwd_fp8. */

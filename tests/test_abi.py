@@ -242,8 +242,9 @@ def test_decode_rejects_small_workspace_and_null_pointers(ea):
     (2, 4, 16, 2048, 64, False, 0.0, "attn::bwd_dkdv_pp_kernel<64, 4>"),
     (2, 4, 16, 2048, 64, True, 0.0, "attn::bwd_dkdv_kernel<64, 4, 32, false>"),
     (2, 4, 16, 2048, 128, True, 0.1, "attn::bwd_dkdv_kernel<128, 4, 32, true>"),
-    (3, 2, 32, 8192, 128, False, 0.0, "attn::fwd_fp8_kernel<128, 4, false>"),
-    (3, 2, 32, 8192, 64, False, 0.0, "attn::fwd_fp8_kernel<64, 4, false>"),
+    (3, 2, 32, 8192, 128, False, 0.0, "attn::fwd_fp8_pp_kernel<128, 4, 32, false>"),
+    (3, 2, 32, 8192, 64, False, 0.0, "attn::fwd_fp8_pp_kernel<64, 4, 64, false>"),
+    (3, 1, 1, 256, 128, True, 0.0, "attn::fwd_fp8_pp_kernel<128, 4, 32, false>"),
 ])
 def test_kernel_name_follows_the_dispatch(ea, stage, B, H, N, d, causal, p, expect):
     """The name query walks the same dispatch as the launch, without launching."""

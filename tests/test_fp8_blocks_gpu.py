@@ -4,7 +4,7 @@ page, FlashAttention-3 summary, the two techniques for FP8 accuracy).
 Parity: attn_fwd_fp8_blocks against the fp64 oracle on the block-dequantised
 (and, with incoherent processing, transformed) inputs exactly as the kernel
 receives them; bars as for the fp8 forward (O max abs <= 1e-1; LSE within
-the derived fp8 dot-product bound).
+the bound derived from the precision of the scores).
 
 Accuracy: against exact attention of the original, unquantised fp64 inputs
 (Q, K, V ~ N(0,1) with one x10 outlier channel), the two techniques must
@@ -112,3 +112,27 @@ def test_techniques_reduce_error_against_unquantised_attention(ea):
     log(f"    reduction with both techniques: O {base[0] / both[0]:.2f}x, "
         f"LSE {base[1] / both[1]:.2f}x")
     assert base[0] / both[0] >= 2.0 and base[1] / both[1] >= 2.0
+
+
+@pytest.mark.parametrize("d,causal,window", [(128, False, 0), (128, True, 0), (128, True, 100),
+                                             (64, False, 0), (64, True, 0)])
+def test_block_parity_grouped_query(ea, d, causal, window):
+    """Block descales with grouped-query K/V (8 query heads on 2 key/value
+    heads): each query head reads the K/V blocks and the block descales of
+    its own key/value head."""
+    B, H, Hkv, N = 1, 8, 2, 700
+    log(f"case: fp8 blocks gqa B{B} H{H} Hkv{Hkv} N{N} d{d} causal={causal} window={window}")
+    f8 = attn_synth.fp8_attention_inputs_v2(983, B, H, N, d, blocks=True)
+    for n in ("k", "v"):
+        f8[n] = np.ascontiguousarray(f8[n][:, :Hkv])
+        f8[n + "_descale"] = np.ascontiguousarray(f8[n + "_descale"][:, :Hkv])
+    ref = dequantised(f8, True)
+    s = 1 / math.sqrt(d)
+    o, lse = run_gpu(ea, f8, True, causal, window)
+    o_ref, l_ref = oracle.fwd_gqa(ref["q"], ref["k"], ref["v"], s, causal, window)
+    assert_close(o, o_ref, FP8_MAX, None, "O")
+    G = H // Hkv
+    for h in range(H):
+        assert_lse(lse[0, h], l_ref[0, h],
+                   fp8_lse_bound(ref["q"][0, h], ref["k"][0, h // G], s, causal, window),
+                   f"LSE head {h}")

@@ -6,13 +6,14 @@ channels of Q, K and V scaled by 10, quantised per tensor (descale =
 amax / 448).  Bar: O max abs <= 1e-1.  Errors are also reported separately
 for the outlier channels and the others.
 
-The LSE has no stated bar for fp8.  The fp8 matrix-core instruction
-(v_mfma_scale_f32_32x32x64_f8f6f4) does not accumulate its 64 products
-exactly in fp32: measured on MI355X, 448*448 + 1 returns 200704, and random
-e4m3 dot products deviate by up to 2.6e-4 (about 2^-12) of sum |a||b|.  A
-score S_ij therefore carries an error up to eps * s * sum_k |q_ik||k_jk|, and
-L_i, a P-weighted mean of its scores' errors, at most the row's largest such
-bound.  The bar used is eps = 2^-10 (4x the measured worst case) plus 1e-3.
+The LSE has no stated bar for fp8.  The kernel widens the e4m3 codes to bf16
+(exactly) and sums the scores on the bf16 matrix cores in fp32, so a score
+S_ij carries a rounding error of order n * 2^-24 * s * sum_k |q_ik||k_jk|
+(n the number of additions), and L_i, a P-weighted mean of its scores'
+errors, at most the row's largest such bound, plus the rounding of L itself
+(a few fp32 ulps of values up to about 100 with outlier channels).  The bar
+used is eps = 2^-16 times the row's largest s * sum_k |q_ik||k_jk|, plus
+1e-4; the errors measured on MI355X stay below a quarter of it.
 """
 import math
 
@@ -49,11 +50,11 @@ def run_fp8(ea, f8, dev, causal, window, out_dtype=torch.bfloat16):
     return o.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
 
 
-EPS_FP8_DOT = 2.0 ** -10
+EPS_FP8_DOT = 2.0 ** -16
 
 
 def fp8_lse_bound(q, k, s, causal, window, rows=None):
-    """Per-row bound on |L_gpu - L_oracle| from the fp8 dot-product precision."""
+    """Per-row bound on |L_gpu - L_oracle| from the precision of the scores."""
     import torch as _t
     qa = _t.from_numpy(np.abs(q if rows is None else q[rows]))
     ka = _t.from_numpy(np.abs(k))
@@ -66,7 +67,7 @@ def fp8_lse_bound(q, k, s, causal, window, rows=None):
         vis &= j <= i
     if window > 0:
         vis &= (i - j).abs() < window
-    return (mag.masked_fill(~vis, 0).amax(dim=1).numpy() * EPS_FP8_DOT + 1e-3)
+    return (mag.masked_fill(~vis, 0).amax(dim=1).numpy() * EPS_FP8_DOT + 1e-4)
 
 
 def assert_lse(lse, lse_ref, bound, what):
@@ -106,39 +107,42 @@ def test_fp8_ragged_shapes_and_masks(ea, N, d, causal, window):
             assert_lse(lse[b, h], lse_ref[b, h], bound, f"LSE head ({b},{h})")
 
 
-def test_fp8_full_size_sampled(ea):
-    """B=2, H=32, N=8192, d=128, non-causal: two heads in full, sampled rows
-    of every head; bf16 output and, for the kernel's own error, fp32 output."""
+def lse_bound_loose(q, k, s):
+    """A cheaper upper bound of fp8_lse_bound for whole non-causal heads:
+    sum_k |q_ik||k_jk| <= sum_k |q_ik| max_j |k_jk|."""
+    return np.abs(q) @ np.abs(k).max(axis=0) * s * EPS_FP8_DOT + 1e-4
+
+
+def test_fp8_full_size_every_row(ea):
+    """B=2, H=32, N=8192, d=128, non-causal (the fp8 workload): every row of
+    every head, with bf16 output and, for the kernel's own error, fp32
+    output; the LSE of two heads against the row bound, of every head
+    against a looser one."""
     B, H, N, d = 2, 32, 8192, 128
-    log(f"case: fp8 B{B} H{H} N{N} d{d} non-causal")
+    log(f"case: fp8 B{B} H{H} N{N} d{d} non-causal, every row")
     f8, dev, ref = fp8_case(5, B, H, N, d)
     s = 1 / math.sqrt(d)
     o, lse = run_fp8(ea, f8, dev, False, 0)
     o32, _ = run_fp8(ea, f8, dev, False, 0, torch.float32)
-    assert np.isfinite(o).all()
+    assert np.isfinite(o).all() and np.isfinite(o32).all()
+    o_ref, lse_ref = oracle.fwd(ref["q"], ref["k"], ref["v"], s)
+    report_split(o, o_ref, f8["channels"], "O bf16 out, every row")
+    report_split(o32, o_ref, f8["channels"], "O fp32 out, every row")
+    assert_close(o, o_ref, FP8_MAX, None, "O bf16 out")
+    assert_close(o32, o_ref, FP8_MAX, None, "O fp32 out")
     for b, h in ((0, 0), (1, 31)):
-        o_ref, lse_ref = oracle.fwd(ref["q"][b, h], ref["k"][b, h], ref["v"][b, h], s)
-        report_split(o[b, h], o_ref, f8["channels"], f"O head ({b},{h}) bf16 out")
-        report_split(o32[b, h], o_ref, f8["channels"], f"O head ({b},{h}) fp32 out")
-        assert_close(o[b, h], o_ref, FP8_MAX, None, f"O head ({b},{h})")
         bound = fp8_lse_bound(ref["q"][b, h], ref["k"][b, h], s, False, 0)
-        assert_lse(lse[b, h], lse_ref, bound, f"LSE head ({b},{h})")
-    rng = np.random.default_rng(7)
-    got, want = [], []
+        assert_lse(lse[b, h], lse_ref[b, h], bound, f"LSE head ({b},{h})")
     for b in range(B):
         for h in range(H):
-            rows = np.unique(rng.integers(0, N, 6))
-            o_ref, _ = oracle.fwd_rows(ref["q"][b, h], ref["k"][b, h], ref["v"][b, h],
-                                       rows, s)
-            got.append(o[b, h][rows]); want.append(o_ref)
-    got, want = np.concatenate(got), np.concatenate(want)
-    report_split(got, want, f8["channels"], "O sampled rows, all heads")
-    assert_close(got, want, FP8_MAX, None, "O sampled rows")
+            assert_lse(lse[b, h], lse_ref[b, h],
+                       lse_bound_loose(ref["q"][b, h], ref["k"][b, h], s),
+                       f"LSE head ({b},{h}), loose bound")
 
 
 def test_fp8_step_shape_sampled(ea):
-    """The fp8 launch bench.py times: B=4, H=16, N=2048, d=128, non-causal;
-    two heads in full and sampled rows of every head."""
+    """A second fp8 shape, B=4, H=16, N=2048, d=128, non-causal: two heads
+    in full and sampled rows of every head."""
     B, H, N, d = 4, 16, 2048, 128
     log(f"case: fp8 B{B} H{H} N{N} d{d} non-causal")
     f8, dev, ref = fp8_case(2, B, H, N, d)
