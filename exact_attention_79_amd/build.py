@@ -38,7 +38,9 @@ def _compile(src: str) -> str:
 PROBES = {os.path.join(HERE, "probes", "dq_atomic_adds.hip"):
           os.path.join(HERE, "probes", "dq_atomic_adds"),
           os.path.join(HERE, "probes", "valu_rates.hip"):
-          os.path.join(HERE, "probes", "valu_rates")}
+          os.path.join(HERE, "probes", "valu_rates"),
+          os.path.join(HERE, "probes", "dot_precision.hip"):
+          os.path.join(HERE, "probes", "dot_precision")}
 
 
 def _build_probe(src: str, exe: str):
