@@ -44,8 +44,7 @@ def test_oracle_under_asan_ubsan(tmp_path):
 
 
 def test_abi_layer_under_asan_ubsan(tmp_path):
-    objs = [os.path.join(BUILD, f"{n}.o") for n in ("attn_fwd", "attn_bwd", "attn_fwd_fp8",
-                                                   "attn_decode")]
+    objs = [os.path.join(BUILD, f"{n}.o") for n in ("attn_fwd", "attn_bwd", "attn_decode")]
     if not (os.path.exists(HIPCC) and os.path.exists(CLANGXX) and all(map(os.path.exists, objs))):
         pytest.skip("hipcc, ROCm's clang++ or the built kernel objects are missing")
     api = str(tmp_path / "attn_api_san.o")
