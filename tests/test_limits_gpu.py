@@ -1,6 +1,6 @@
 """The largest problem the library accepts: B*H*N*d just under 2^31 elements
-(B1 H8191 N2048 d128, 4.3 GB per bf16 tensor), forward and backward, and the
-rejection one head above it.
+(B1 H8191 N2048 d128, 4.3 GB per bf16 tensor), forward and backward, the fp8
+forward at that size, and the rejection one head above it.
 
 Heads are independent, so only the checked heads need oracle inputs: the
 first, a middle and the last head get the seeded host-generated bf16 values
@@ -71,6 +71,38 @@ def test_largest_forward_and_backward(ea, big, causal):
         for name, g, w in zip(("dQ", "dK", "dV"), (dq, dk, dv), want):
             assert_close(np64(g[0, h]), w[0, 0], BF16_MAX, BF16_MEAN, f"{name} head {h}")
     del o, lse, dq, dk, dv
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_largest_fp8_forward(ea, causal):
+    """The fp8 forward at the same size (e4m3 codes, 2.1 GB per tensor):
+    the checked heads carry the fp8 workload recipe's codes (one x10 outlier
+    channel) and the tensors' descales; the other heads are device-drawn
+    codes under the same descales."""
+    import attn_synth
+    from helpers import FP8_MAX
+    gen = torch.Generator(device="cuda").manual_seed(32)
+    t = {}
+    for n in ("q", "k", "v"):
+        t[n] = torch.empty((B, H, N, D), device="cuda", dtype=torch.uint8)
+        for h0 in range(0, H, 1024):
+            x = torch.randn((B, min(1024, H - h0), N, D), device="cuda", generator=gen)
+            t[n][:, h0:h0 + x.shape[1]] = (x * 16).to(torch.float8_e4m3fn).view(torch.uint8)
+            del x
+    f8 = attn_synth.fp8_attention_inputs(3200, 1, len(CHECKED), N, D)
+    for i, h in enumerate(CHECKED):
+        for n in ("q", "k", "v"):
+            t[n][0, h].copy_(torch.from_numpy(f8[n][0, i]))
+    s = 1 / math.sqrt(D)
+    o, lse = ea.attn_fwd_fp8(t["q"], t["k"], t["v"], f8["q_descale"], f8["k_descale"],
+                             f8["v_descale"], causal=causal)
+    torch.cuda.synchronize()
+    ref = {n: oracle.decode_e4m3(f8[n], f8[n + "_descale"]) for n in ("q", "k", "v")}
+    for i, h in enumerate(CHECKED):
+        o_r, _ = oracle.fwd(ref["q"][0, i], ref["k"][0, i], ref["v"][0, i], s, causal)
+        assert_close(np64(o[0, h]), o_r, FP8_MAX, None, f"fp8 O head {h}")
+    del o, lse, t
+    torch.cuda.empty_cache()
 
 
 def test_one_head_more_is_refused(ea):
