@@ -465,9 +465,10 @@ __device__ __forceinline__ void fwd_pp_body(const FwdKParams& p) {
   const float tau = 8.0f / s2;
   const TrCoord trc(lane);
   // e4m3 inputs: the running max is kept in base-2 logit units (so that
-  // tiles with different key descales compare directly); tile t's code
-  // products are scaled by st(t), and with block descales log2 of its value
-  // descale, lv(t), is folded into its weights.
+  // tiles with different key descales compare directly).  A tile's code
+  // products are scaled by s log2(e) dq dk (s2k with per-tensor descales,
+  // s2q dk(tile) with block descales), and with block descales log2 of the
+  // tile's value descale is folded into its weights.
   const int kvh = kv_head(bh, p.H, p.Hkv);
   const int n_kb = (N + 63) / 64;
   float s2q = 0.f, s2k = 0.f;
