@@ -40,7 +40,9 @@ PROBES = {os.path.join(HERE, "probes", "dq_atomic_adds.hip"):
           os.path.join(HERE, "probes", "valu_rates.hip"):
           os.path.join(HERE, "probes", "valu_rates"),
           os.path.join(HERE, "probes", "dot_precision.hip"):
-          os.path.join(HERE, "probes", "dot_precision")}
+          os.path.join(HERE, "probes", "dot_precision"),
+          os.path.join(HERE, "probes", "mfma_power.hip"):
+          os.path.join(HERE, "probes", "mfma_power")}
 
 
 def _build_probe(src: str, exe: str):
