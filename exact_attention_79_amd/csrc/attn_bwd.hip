@@ -9,7 +9,7 @@
 // S = s Q K^T gives dQ = s dS K and dK = s dS^T Q.
 //
 // Two launches on the caller's stream (which kernel serves which head dim
-// and mask: without dropout, bwd_dq_pp_kernel at d = 128, bwd_dkdv_pair_kernel
+// and mask: without dropout, bwd_dq_pp_kernel at d = 128, bwd_dkdv_quad_kernel
 // at d = 128 and bwd_dkdv_pp_kernel at d = 64 non-causal; the single-wave
 // kernels otherwise):
 //  1. bwd_dq_kernel: one workgroup per query block, Q_i, dO_i, L_i, D_i
@@ -27,18 +27,19 @@
 // products per visible tile) but needs no atomics and no zeroed buffer, and
 // the result is deterministic.
 //
-// gfx950 mapping.  In the dK/dV kernel each wave owns 32 keys and computes
-// S = Q K^T with keys on the MFMA N side, so the C layout gives one key per
-// lane and P, dS (bf16) are directly the B operands of dV^T += dO^T P and
-// dK^T += Q^T dS; dO^T and Q^T are read from LDS with transposing reads in
-// the C layout's row permutation.  The dQ kernel is the mirror image: S^T =
-// K Q^T with one query per lane, and dQ^T += K^T dS^T with K^T read
-// transposed from LDS.  Q/dO (dK/dV kernel) and K/V (dQ kernel) tiles stream
-// through three-slot LDS rings (direct global -> LDS loads) with the same
-// swizzle as the forward.
+// gfx950 mapping.  In the dK/dV kernels a wave owns 32 keys (64 in the
+// four-role kernel) and computes S = Q K^T with keys on the MFMA N side, so
+// the C layout gives one key per lane and P, dS (bf16) are directly the B
+// operands of dV^T += dO^T P and dK^T += Q^T dS; dO^T and Q^T are read from
+// LDS with transposing reads in the C layout's row permutation.  The dQ
+// kernel is the mirror image: S^T = K Q^T with one query per lane, and
+// dQ^T += K^T dS^T with K^T read transposed from LDS.  Q/dO (dK/dV kernels)
+// and K/V (dQ kernel) tiles stream through LDS rings (direct global -> LDS
+// loads) with the same swizzle as the forward.
 #include <limits.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "attn_device.hpp"
 #include "attn_kernels.hpp"
@@ -452,37 +453,56 @@ __global__ __launch_bounds__(NW * 64, (dkdv_waves_per_simd<D, BQ>())) void bwd_d
   }
 }
 
-// ---------------------------------------------------------- dK, dV (paired)
+// --------------------------------------------------- dK, dV (four roles)
 // d = 128 without dropout.  The kernel above needs about 340 registers per
-// wave at d = 128, so it runs one wave per SIMD, and that wave mostly
-// alternates between matrix and vector work.  Here the four products of a
-// key slice are split over two waves that own the same 32 keys and share a
-// SIMD (waves w and w + NPAIR):
-//  * the P wave computes S = Q K^T, P = exp2(s log2(e) S - L log2(e)) and
-//    dV^T += dO^T P, and hands P (fp32) to its partner through LDS;
-//  * the dS wave computes D - dP = D - dO V^T (the MFMAs start from D and
-//    take -V, as above), dS = P (dP - D) (negated) and dK^T += Q^T dS, one
-//    query tile behind the P wave.
-// Each wave fits in 256 registers, so a SIMD holds both and overlaps one
-// wave's vector work with the other's MFMAs.  Every value is formed as in
-// the single-wave kernel, and each accumulator takes its products in the same
-// order, so the two kernels give the same results.
+// wave at d = 128, so it runs one wave per SIMD, which alternates between
+// matrix and vector work.  Here the four products of a key block are split
+// over four kinds of wave, and each wave keeps 64 keys of its product, so
+// that each operand tile read from LDS feeds two MFMAs (one per 32-key tile;
+// with 32 keys per wave the CU's LDS, which takes one wave instruction every
+// 4-5 clocks, would be issuing about two instructions per MFMA):
+//  * S wave (K^T resident): S = Q K^T of query tile s+1 and, between those
+//    MFMAs, P = exp2(s log2(e) S - L log2(e)) of tile s, written (fp32) to
+//    an LDS exchange buffer;
+//  * dP wave (-V^T resident): D - dP of tile s (the MFMAs start from D) and
+//    dS = P (dP - D) of tile s-1 (negated; P from the exchange), written
+//    (bf16) to a second exchange buffer;
+//  * dV wave: dV^T += dO^T P of tile s-2 (P rounded to bf16);
+//  * dK wave: dK^T += Q^T dS of tile s-3.
+// Two groups of 64 keys make the workgroup's 128 keys and 8 waves.  The
+// waves of a workgroup are placed on the SIMDs round-robin, so waves 0-3 =
+// S, dP, S, dP and 4-7 = dK, dV, dK, dV put one wave with vector work (the
+// exponentials, or dS) and one with MFMAs (and the rounding of P to bf16)
+// on every SIMD, with 32 MFMAs per step each.  Every value is formed as in
+// the kernel above, and each accumulator takes its products in the same
+// order.
 //
-// Query tiles of 32 rows stream through four LDS slots (tile s in slot
-// s % 4): at step s the P wave reads tile s+1 (the S products of the next
-// tile) and tile s (dV), the dS wave tile s (dP) and tile s-1 (dK), and
-// tile s+2 is fetched.  P of tile s goes to exchange buffer s % 2.  One
-// barrier ends each step.
-template <int D, int NPAIR>
-__global__ __launch_bounds__(2 * NPAIR * 64, 2) void bwd_dkdv_pair_kernel(BwdKParams p) {
+// Query tiles of 32 rows (Q, dO, L, D) sit in slot t % 6 of their rings,
+// one LDS array per slot (so that the compiler sees that a read of one slot
+// does not alias the direct loads into another and inserts no wait for
+// them); tile s+3 is fetched at step s and waited for at its end.  Every
+// wave reads all the operands of its next step (A tiles, and P or dS from
+// the exchange) during the current one, each register taking the next
+// tile's operand right after the MFMA that used it, so that no step starts
+// by waiting for LDS: the dV and dK waves run two and three tiles behind
+// the S wave, which is what lets them read P and dS a step after these
+// were written.  P of tile s goes to exchange buffer s % 2, dS of tile s-1
+// to buffer (s-1) % 2.  The loop runs U + 3 steps, one barrier each.
+template <int V>
+using IC = std::integral_constant<int, V>;
+
+template <int D>
+__global__ __launch_bounds__(512, 2) void bwd_dkdv_quad_kernel(BwdKParams p) {
   constexpr int BQ = 32;               // query rows per step
-  constexpr int NWV = 2 * NPAIR;       // waves
-  constexpr int BKV = 32 * NPAIR;      // keys per workgroup
+  constexpr int NWV = 8;               // waves
+  constexpr int BKV = 128;             // keys per workgroup
   constexpr int KS = D / 16;           // K-steps of S and dP
   constexpr int DT = D / 32;           // d-tiles of dK and dV
   constexpr int LDROWS = 64;           // L and D are staged one dword per lane
-  constexpr int PSZ = NPAIR * 16 * 64;  // floats of one P exchange buffer
-  constexpr int AHEAD = 3;             // operand reads ahead of their MFMA
+  constexpr int AHEAD = 3;             // operand reads ahead of their MFMAs
+  constexpr int PF = 2 * 8 * 64 * 4;   // floats of a P buffer: 2 groups x 8 chunks per lane
+  constexpr int SH = 2 * 4 * 64 * 8;   // bf16 of a dS buffer: 2 groups x 4 chunks per lane
+  static_assert(D == 128, "four-role dK/dV kernel is for d = 128");
   __shared__ __attribute__((aligned(16))) __bf16 sQ0[BQ * D];
   __shared__ __attribute__((aligned(16))) __bf16 sQ1[BQ * D];
   __shared__ __attribute__((aligned(16))) __bf16 sQ2[BQ * D];
@@ -499,13 +519,46 @@ __global__ __launch_bounds__(2 * NPAIR * 64, 2) void bwd_dkdv_pair_kernel(BwdKPa
       sL4[LDROWS], sL5[LDROWS];
   __shared__ __attribute__((aligned(16))) float sD0[LDROWS], sD1[LDROWS], sD2[LDROWS], sD3[LDROWS],
       sD4[LDROWS], sD5[LDROWS];
-  __shared__ __attribute__((aligned(16))) float sP0[PSZ];
-  __shared__ __attribute__((aligned(16))) float sP1[PSZ];
+  __shared__ __attribute__((aligned(16))) float sP0[PF];
+  __shared__ __attribute__((aligned(16))) float sP1[PF];
+  __shared__ __attribute__((aligned(16))) __bf16 sS0[SH];
+  __shared__ __attribute__((aligned(16))) __bf16 sS1[SH];
+  // Slot j (any integer constant, taken mod 6) of each ring; buffer j % 2.
+  auto sq = [&](auto J) -> __bf16* {
+    constexpr int j = (decltype(J)::value % 6 + 6) % 6;
+    if constexpr (j == 0) return sQ0; else if constexpr (j == 1) return sQ1;
+    else if constexpr (j == 2) return sQ2; else if constexpr (j == 3) return sQ3;
+    else if constexpr (j == 4) return sQ4; else return sQ5;
+  };
+  auto so = [&](auto J) -> __bf16* {
+    constexpr int j = (decltype(J)::value % 6 + 6) % 6;
+    if constexpr (j == 0) return sO0; else if constexpr (j == 1) return sO1;
+    else if constexpr (j == 2) return sO2; else if constexpr (j == 3) return sO3;
+    else if constexpr (j == 4) return sO4; else return sO5;
+  };
+  auto sl = [&](auto J) -> float* {
+    constexpr int j = (decltype(J)::value % 6 + 6) % 6;
+    if constexpr (j == 0) return sL0; else if constexpr (j == 1) return sL1;
+    else if constexpr (j == 2) return sL2; else if constexpr (j == 3) return sL3;
+    else if constexpr (j == 4) return sL4; else return sL5;
+  };
+  auto sd = [&](auto J) -> float* {
+    constexpr int j = (decltype(J)::value % 6 + 6) % 6;
+    if constexpr (j == 0) return sD0; else if constexpr (j == 1) return sD1;
+    else if constexpr (j == 2) return sD2; else if constexpr (j == 3) return sD3;
+    else if constexpr (j == 4) return sD4; else return sD5;
+  };
+  auto sp = [&](auto J) -> float* {
+    if constexpr ((decltype(J)::value % 2 + 2) % 2 == 0) return sP0; else return sP1;
+  };
+  auto ss = [&](auto J) -> __bf16* {
+    if constexpr ((decltype(J)::value % 2 + 2) % 2 == 0) return sS0; else return sS1;
+  };
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, kept scalar
-  const bool pwave = w < NPAIR;
-  const int pr = pwave ? w : w - NPAIR;  // key slice of this wave's pair
+  const int role = w < 4 ? (w & 1) : 3 - (w & 1);          // 0 S, 1 dP, 2 dV, 3 dK
+  const int kg = (w >> 1) & 1;                              // key group
   const int h = lane >> 5, n = lane & 31;
   const TileId id =
       tile_order(blockIdx.x, gridDim.x / p.n_tiles, p.n_tiles, p.causal, causal_group<D>());
@@ -516,48 +569,27 @@ __global__ __launch_bounds__(2 * NPAIR * 64, 2) void bwd_dkdv_pair_kernel(BwdKPa
   const int G = p.H / p.Hkv / p.split;  // query heads this workgroup walks
   const int bh0 = (bkv / p.Hkv) * p.H + (bkv % p.Hkv) * (p.H / p.Hkv) + share * G;
   const int k0 = kt * BKV;
-  const int kw0 = k0 + 32 * pr;
-  const int my_k = kw0 + n;
+  const int kg0 = k0 + 64 * kg;  // first key of this wave's group; tile t starts at kg0 + 32 t
   const size_t head = (size_t)bkv * N * D;
   const uint32_t head_bytes = (uint32_t)N * D * 2;
 
-  // Resident B operand (lane = key, 8 consecutive d per K-step): K^T for
-  // the P wave, -V^T for the dS wave.
-  bf16x8 bop[KS];
-  {
-    const auto r = make_rsrc((pwave ? p.k : p.v) + head, head_bytes);
-    const uint32_t sign = pwave ? 0u : 0x80008000u;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      bop[ks] = __builtin_bit_cast(
-          bf16x8, buf_load16(r, (uint32_t)(my_k * D + 16 * ks + 8 * h) * 2u) ^ sign);
-  }
-  f32x16 acc[DT];  // dV^T (P wave) or -dK^T / s (dS wave)
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt) acc[dt] = (f32x16){};
-
-  // Queries that can see any key of this block, and those that see my_k.
+  // Queries that can see any key of this block.
   const int k_last = min(k0 + BKV, N) - 1;
   int q_lo = p.causal ? k0 : 0, q_hi = N;
-  int qmin = p.causal ? my_k : INT_MIN, qmax = INT_MAX;
   if (W > 0) {
     q_lo = max(q_lo, k0 - W + 1);
     q_hi = min(q_hi, k_last + W);
-    if (!p.causal) qmin = my_k - W + 1;
-    qmax = my_k + W - 1;
   }
   const int t_lo = q_lo / BQ, t_hi = (q_hi + BQ - 1) / BQ;
   const int U = G * (t_hi - t_lo);  // tiles in the sequence (query head, tile)
+  const int NSTEP = U + 3;
 
-  const float s2 = p.scale * kLog2e;
   const TrCoord trc(lane);
-  // Byte offsets of this lane's operand reads inside a tile: row reads
-  // (K-step ks) and transposing reads (d-tile dt, rows +0 / +8; the swizzle
-  // of a transposing read does not depend on its K-step, which adds 16 rows).
-  // They are re-hidden from the optimizer at every step, so that each read
-  // is formed in its own block as offset + constant (slot and array) and the
-  // constant folds into the instruction instead of one hoisted address
-  // register per slot and read.
+  // This lane's byte offsets inside a tile (row reads of K-step ks;
+  // transposing reads of d-tile dt, rows +0 / +8), in an exchange buffer
+  // (chunk c of the lane at + 1024 c) and in an L or D row block.  Hidden
+  // from the optimizer at every step: otherwise the compiler hoists one
+  // address register per slot and read out of the loop.
   uint32_t roff[KS], toff[2 * DT];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) roff[ks] = (uint32_t)tile_off<D>(n, 2 * ks + h) * 2u;
@@ -568,8 +600,9 @@ __global__ __launch_bounds__(2 * NPAIR * 64, 2) void bwd_dkdv_pair_kernel(BwdKPa
       const int r = trc.row + 8 * x, col = 32 * dt + trc.col;
       toff[2 * dt + x] = (uint32_t)(tile_off<D>(r, col >> 3) + (col & 7)) * 2u;
     }
-  uint32_t poff = (uint32_t)((pr * 4 * 64 + lane) * 16);  // P exchange, this lane's first chunk
-  uint32_t lhoff = (uint32_t)(16 * h);                    // L, D rows 4h .. 4h+3 of group 0
+  uint32_t poff = (uint32_t)((kg * 8 * 64 + lane) * 16);
+  uint32_t soff = (uint32_t)((kg * 4 * 64 + lane) * 16);
+  uint32_t lhoff = (uint32_t)(16 * h);  // L, D rows 4h .. 4h+3 of group 0
   auto rrow = [&](const __bf16* t, int ks) {
     return *(const bf16x8*)((const char*)t + roff[ks]);
   };
@@ -582,241 +615,370 @@ __global__ __launch_bounds__(2 * NPAIR * 64, 2) void bwd_dkdv_pair_kernel(BwdKPa
     return *(const f32x4*)((const char*)t + lhoff + 32 * g);
   };
 
-  // Load cursor (lj, lt), two tiles ahead of the step; past the last head it
-  // keeps reading the last head's rows (in bounds, never used).
-  int lj = 0, lt = t_lo, ct = t_lo;
-  auto load_tile = [&](__bf16* Qf, __bf16* Of, float* Lf, float* Df) {
+  // Fetch cursor (query head lj of the group, tile lt), three tiles ahead
+  // of the step; past the last head it keeps reading the last head's rows
+  // (in bounds, never used).  The buffer resources span the whole query
+  // head (rows past N read as zero) and change only with the head; each
+  // wave moves one 1 KB piece of the Q and dO tiles (as tile_load_lds),
+  // lane L the global chunk that the swizzle puts at LDS chunk 64 w + L.
+  static_assert(BQ * D / 8 == 64 * NWV, "one 16-byte chunk per lane and tile");
+  int lj = 0, lt = t_lo;
+  uint32_t chunk_off;
+  {
+    const int pc = w * 64 + lane, row = pc / (D / 8), ch = (pc % (D / 8)) ^ swz<D>(row);
+    chunk_off = (uint32_t)(row * D + ch * 8) * 2u;
+  }
+  __amdgpu_buffer_rsrc_t rq, ro, rl, rd;
+  auto set_head = [&]() {
     const int bhq = bh0 + min(lj, G - 1);
-    const size_t qhead = (size_t)bhq * N * D;
-    tile_load_lds<D, BQ, NWV>(p.q + qhead, head_bytes, lt * BQ, Qf, w, lane);
-    tile_load_lds<D, BQ, NWV>(p.dout + qhead, head_bytes, lt * BQ, Of, w, lane);
+    rq = make_rsrc(p.q + (size_t)bhq * N * D, head_bytes);
+    ro = make_rsrc(p.dout + (size_t)bhq * N * D, head_bytes);
+    rl = make_rsrc(p.lse2 + (size_t)bhq * N, (uint32_t)N * 4);
+    rd = make_rsrc(p.delta + (size_t)bhq * N, (uint32_t)N * 4);
+  };
+  set_head();
+  auto load_tile = [&](auto J) {
+    const uint32_t voff = chunk_off + (uint32_t)lt * (BQ * D * 2);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (LDS_AS void*)(sq(J) + w * 64 * 8), 16,
+                                             (int)voff, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ro, (LDS_AS void*)(so(J) + w * 64 * 8), 16,
+                                             (int)voff, 0, 0, 0);
     if (w == 0)
-      vec_load_lds<LDROWS>(make_rsrc(p.lse2 + (size_t)bhq * N, (uint32_t)N * 4), lt * BQ,
-                           Lf, lane);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, (LDS_AS void*)sl(J), 4,
+                                               (int)((uint32_t)(lt * BQ + lane) * 4u), 0, 0, 0);
     if (w == 1)
-      vec_load_lds<LDROWS>(make_rsrc(p.delta + (size_t)bhq * N, (uint32_t)N * 4), lt * BQ,
-                           Df, lane);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rd, (LDS_AS void*)sd(J), 4,
+                                               (int)((uint32_t)(lt * BQ + lane) * 4u), 0, 0, 0);
     if (++lt == t_hi) {
       lt = t_lo;
       ++lj;
+      set_head();
     }
   };
-
-  // Prologue: tiles 0 to 3.  The dS wave's first step has no tile
-  // before it; it runs on zeros (P buffer 1, slot 5 and its running D - dP),
-  // so that its dK products add exactly nothing.
-  load_tile(sQ0, sO0, sL0, sD0);
-  load_tile(sQ1, sO1, sL1, sD1);
-  load_tile(sQ2, sO2, sL2, sD2);
-  load_tile(sQ3, sO3, sL3, sD3);
-  for (int i = tid; i < BQ * D / 8; i += NWV * 64) ((u32x4*)sQ5)[i] = (u32x4){};
-  for (int i = tid; i < PSZ / 4; i += NWV * 64) ((f32x4*)sP1)[i] = (f32x4){};
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  // P wave: S of the current tile (raw, unmasked); dS wave: D - dP of the
-  // tile before the current one.
-  f32x16 cur = {};
-  if (pwave) {
+  // Only the offsets that a role uses are hidden (and so kept) in its loop.
+  auto hide_offsets = [&]() {
+    if (role < 2) {
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      cur = mfma32(tile_row8<D>(sQ0, n, 2 * ks + h), bop[ks], cur);
-  }
-
-  // Step s: slots c (tile s), nx (tile s+1), pv (tile s-1), f (filled with
-  // tile s+4; tile s+3 is in flight); P of tile s is written to Pw, P of
-  // tile s-1 read from Pr.
-  // The two roles run separate loops (so that neither's registers are
-  // shuffled at joins with the other's code); each step ends with the one
-  // barrier, which the hardware counts per workgroup, not per instruction.
-  auto begin_step = [&](__bf16* Qf, __bf16* Of, float* Lf, float* Df) {
-    load_tile(Qf, Of, Lf, Df);
+      for (int i = 0; i < KS; ++i) asm volatile("" : "+v"(roff[i]));
+      asm volatile("" : "+v"(lhoff));
+    } else {
 #pragma unroll
-    for (int i = 0; i < KS; ++i) asm volatile("" : "+v"(roff[i]));
-#pragma unroll
-    for (int i = 0; i < 2 * DT; ++i) asm volatile("" : "+v"(toff[i]));
-    asm volatile("" : "+v"(poff), "+v"(lhoff));
+      for (int i = 0; i < 2 * DT; ++i) asm volatile("" : "+v"(toff[i]));
+    }
+    if (role != 3) asm volatile("" : "+v"(poff));
+    if (role & 1) asm volatile("" : "+v"(soff));
   };
-  // Tile s+3 has landed for every wave (this step's loads stay in flight:
-  // two, plus L or D for waves 0 and 1); the slot of tile s-1 may be
-  // refilled next step.
+  // Step s (slot j = s % 6) fetches tile s+3.
+  auto begin_step = [&](auto J) {
+    load_tile(IC<decltype(J)::value + 3>());
+    hide_offsets();
+  };
+  // This step's tile has landed for every wave after the barrier.
   auto end_step = [&]() {
-    if (w < 2)
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm(3));
-    else
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm(2));
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     __builtin_amdgcn_s_barrier();
   };
-  // The first AHEAD operand rows of a wave's next step are read at the end
-  // of this one, before the barrier: that step's tile has been in LDS for
-  // every wave since the previous barrier (tiles are fetched four steps
-  // ahead).
-  bf16x8 pre[AHEAD];
-  auto prefetch = [&](const __bf16* t) {
-#pragma unroll
-    for (int i = 0; i < AHEAD; ++i) pre[i] = rrow(t, i);
-  };
-  // P wave, step s < U: mask S of tile s, P = exp2(S s2 - L log2 e) (to Pw
-  // and as the bf16 B operand), S of tile s+1, dV^T += dO^T P.
-  auto pstep = [&](const __bf16* Oc, const float* Lc, const __bf16* Qnx, __bf16* Qf,
-                   __bf16* Of, float* Lf, float* Df, float* Pw, const __bf16* Qnext) {
-    begin_step(Qf, Of, Lf, Df);
-    const int i0 = ct * BQ;  // first query of tile s
-    if (++ct == t_hi) ct = t_lo;
-    bool need_mask = false;
-    if (p.causal) need_mask |= i0 < kw0 + 31;
-    if (W > 0) {
-      need_mask |= (i0 + BQ - 1) - kw0 >= W;
-      if (!p.causal) need_mask |= (kw0 + 31) - i0 >= W;
+  // Steps 0 .. NSTEP-1, unrolled by six (slot j = s % 6).
+  auto run = [&](auto&& step) {
+    int s = 0;
+    for (; s + 6 <= NSTEP; s += 6) {
+      step(IC<0>(), s);
+      step(IC<1>(), s + 1);
+      step(IC<2>(), s + 2);
+      step(IC<3>(), s + 3);
+      step(IC<4>(), s + 4);
+      step(IC<5>(), s + 5);
     }
-    if (need_mask) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int q = i0 + 8 * (r >> 2) + 4 * h + (r & 3);
-        cur[r] = (q < qmin || q > qmax) ? -__builtin_inff() : cur[r];
-      }
-    }
-    // L log2(e) of the rows this lane holds: register 4g + c is row 8g + 4h + c.
-    f32x4 lb[4];
-#pragma unroll
-    for (int g = 0; g < 4; ++g) lb[g] = rvec4(Lc, g);
-    f32x16 snext = {};
-    bf16x8 aop[KS], top[2 * DT], pop[2];
-    float pv[16];
-#pragma unroll
-    for (int i = 0; i < AHEAD; ++i) aop[i] = pre[i];
-    __builtin_amdgcn_sched_barrier(0);
-    // S of tile s+1, with two elements of P of tile s per bundle.
-#pragma unroll
-    for (int i = 0; i < KS; ++i) {
-      if (i + AHEAD < KS) aop[i + AHEAD] = rrow(Qnx, i + AHEAD);
-      if (i >= KS - AHEAD) top[i - (KS - AHEAD)] = rtr(Oc, i - (KS - AHEAD));
-      snext = mfma32(aop[i], bop[i], snext);
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int e = 2 * i + u;
-        const float x = fast_exp2(fmaf(cur[e], s2, -lb[e >> 2][e & 3]));
-        pv[e] = x;
-        pop[e >> 3][e & 7] = (__bf16)x;
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
-      *(f32x4*)((char*)Pw + poff + 1024 * k) =
-          (f32x4){pv[4 * k], pv[4 * k + 1], pv[4 * k + 2], pv[4 * k + 3]};
-    // dV^T += dO^T P (K-step j / DT over the tile's rows, d-tile j % DT).
-#pragma unroll
-    for (int j = 0; j < 2 * DT; ++j) {
-      if (j + AHEAD < 2 * DT) top[j + AHEAD] = rtr(Oc, j + AHEAD);
-      acc[j % DT] = mfma32(top[j], pop[j / DT], acc[j % DT]);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    cur = snext;
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): P of tile s is in LDS
-    prefetch(Qnext);
-    end_step();
-  };
-  // dS wave, step s <= U: D - dP of tile s (from D, with -V), dS = P (dP - D)
-  // of tile s-1 (negated; P from Pr), dK^T += Q^T dS of tile s-1.
-  auto dstep = [&](const __bf16* Oc, const float* Dc, const __bf16* Qpv, __bf16* Qf,
-                   __bf16* Of, float* Lf, float* Df, const float* Pr, const __bf16* Onext) {
-    begin_step(Qf, Of, Lf, Df);
-    f32x16 dpn;
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const f32x4 v = rvec4(Dc, g);
-#pragma unroll
-      for (int c = 0; c < 4; ++c) dpn[4 * g + c] = v[c];
-    }
-    f32x4 pp[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) pp[k] = *(const f32x4*)((const char*)Pr + poff + 1024 * k);
-    bf16x8 aop[KS], top[2 * DT], dsop[2];
-#pragma unroll
-    for (int i = 0; i < AHEAD; ++i) aop[i] = pre[i];
-    __builtin_amdgcn_sched_barrier(0);
-    // D - dP of tile s, with two elements of dS of tile s-1 per bundle.
-#pragma unroll
-    for (int i = 0; i < KS; ++i) {
-      if (i + AHEAD < KS) aop[i + AHEAD] = rrow(Oc, i + AHEAD);
-      if (i >= KS - AHEAD) top[i - (KS - AHEAD)] = rtr(Qpv, i - (KS - AHEAD));
-      dpn = mfma32(aop[i], bop[i], dpn);
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int e = 2 * i + u;
-        dsop[e >> 3][e & 7] = (__bf16)(pp[e >> 2][e & 3] * cur[e]);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    // dK^T += Q^T dS of tile s-1.
-#pragma unroll
-    for (int j = 0; j < 2 * DT; ++j) {
-      if (j + AHEAD < 2 * DT) top[j + AHEAD] = rtr(Qpv, j + AHEAD);
-      acc[j % DT] = mfma32(top[j], dsop[j / DT], acc[j % DT]);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    cur = dpn;
-    prefetch(Onext);
-    end_step();
+    if (s < NSTEP) step(IC<0>(), s);
+    if (s + 1 < NSTEP) step(IC<1>(), s + 1);
+    if (s + 2 < NSTEP) step(IC<2>(), s + 2);
+    if (s + 3 < NSTEP) step(IC<3>(), s + 3);
+    if (s + 4 < NSTEP) step(IC<4>(), s + 4);
   };
 
-  // Step s uses slot s % 6 as c, (s+1) % 6 as nx, (s+5) % 6 as pv and fills
-  // (s+4) % 6; P buffer s % 2 is written and (s+1) % 2 read.  The P wave
-  // works on tiles 0 .. U-1 and then joins the last barrier; the dS wave on
-  // tiles -1 .. U-1 (its dP products of tile U are never used).
-  if (pwave) {
-    int s = 0;
-    prefetch(sQ1);
-    for (; s + 6 <= U; s += 6) {
-      pstep(sO0, sL0, sQ1, sQ4, sO4, sL4, sD4, sP0, sQ2);
-      pstep(sO1, sL1, sQ2, sQ5, sO5, sL5, sD5, sP1, sQ3);
-      pstep(sO2, sL2, sQ3, sQ0, sO0, sL0, sD0, sP0, sQ4);
-      pstep(sO3, sL3, sQ4, sQ1, sO1, sL1, sD1, sP1, sQ5);
-      pstep(sO4, sL4, sQ5, sQ2, sO2, sL2, sD2, sP0, sQ0);
-      pstep(sO5, sL5, sQ0, sQ3, sO3, sL3, sD3, sP1, sQ1);
-    }
-    if (s < U) pstep(sO0, sL0, sQ1, sQ4, sO4, sL4, sD4, sP0, sQ2);
-    if (s + 1 < U) pstep(sO1, sL1, sQ2, sQ5, sO5, sL5, sD5, sP1, sQ3);
-    if (s + 2 < U) pstep(sO2, sL2, sQ3, sQ0, sO0, sL0, sD0, sP0, sQ4);
-    if (s + 3 < U) pstep(sO3, sL3, sQ4, sQ1, sO1, sL1, sD1, sP1, sQ5);
-    if (s + 4 < U) pstep(sO4, sL4, sQ5, sQ2, sO2, sL2, sD2, sP0, sQ0);
-    end_step();
-  } else {
-    int s = 0;
-    prefetch(sO0);
-    for (; s + 6 <= U + 1; s += 6) {
-      dstep(sO0, sD0, sQ5, sQ4, sO4, sL4, sD4, sP1, sO1);
-      dstep(sO1, sD1, sQ0, sQ5, sO5, sL5, sD5, sP0, sO2);
-      dstep(sO2, sD2, sQ1, sQ0, sO0, sL0, sD0, sP1, sO3);
-      dstep(sO3, sD3, sQ2, sQ1, sO1, sL1, sD1, sP0, sO4);
-      dstep(sO4, sD4, sQ3, sQ2, sO2, sL2, sD2, sP1, sO5);
-      dstep(sO5, sD5, sQ4, sQ3, sO3, sL3, sD3, sP0, sO0);
-    }
-    if (s <= U) dstep(sO0, sD0, sQ5, sQ4, sO4, sL4, sD4, sP1, sO1);
-    if (s + 1 <= U) dstep(sO1, sD1, sQ0, sQ5, sO5, sL5, sD5, sP0, sO2);
-    if (s + 2 <= U) dstep(sO2, sD2, sQ1, sQ0, sO0, sL0, sD0, sP1, sO3);
-    if (s + 3 <= U) dstep(sO3, sD3, sQ2, sQ1, sO1, sL1, sD1, sP0, sO4);
-    if (s + 4 <= U) dstep(sO4, sD4, sQ3, sQ2, sO2, sL2, sD2, sP1, sO5);
+  // Prologue: tiles 0 to 2; the slots that the dK and dV waves read before
+  // their first tiles arrive (Q slots 4 and 5, dO slot 5) are cleared.
+  load_tile(IC<0>());
+  load_tile(IC<1>());
+  load_tile(IC<2>());
+  for (int i = tid; i < BQ * D / 8; i += NWV * 64) {
+    ((u32x4*)sQ4)[i] = (u32x4){};
+    ((u32x4*)sQ5)[i] = (u32x4){};
+    ((u32x4*)sO5)[i] = (u32x4){};
   }
-  __builtin_amdgcn_s_waitcnt(0);  // no load may land after the workgroup ends
 
-  // With the group split, this share's partial sums go to the workspace.
-  float* out = pwave ? p.dv : p.dk;
-  if (p.split > 1) {
-    const size_t part = (size_t)(gridDim.x / p.n_tiles / p.split) * N * D;
-    out = (pwave ? p.dv_part : p.dk_part) + share * part;
-  }
-  if (my_k < N) {
-    const size_t row = head + (size_t)my_k * D;
-    const float sc = pwave ? 1.f : -p.scale;  // (dS negated)
+  if (role == 0) {
+    // ---- S wave
+    bf16x8 bop[2][KS];  // K^T: lane = key, 8 consecutive d per K-step
+    {
+      const auto r = make_rsrc(p.k + head, head_bytes);
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          bop[t][ks] = __builtin_bit_cast(
+              bf16x8, buf_load16(r, (uint32_t)((kg0 + 32 * t + n) * D + 16 * ks + 8 * h) * 2u));
+    }
+    // Queries that see key kg0 + 32 t + n.
+    int qmin[2], qmax[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int my_k = kg0 + 32 * t + n;
+      qmin[t] = p.causal ? my_k : INT_MIN;
+      qmax[t] = INT_MAX;
+      if (W > 0) {
+        if (!p.causal) qmin[t] = my_k - W + 1;
+        qmax[t] = my_k + W - 1;
+      }
+    }
+    const float s2 = p.scale * kLog2e;
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_s_barrier();
+    f32x16 cur[2] = {};  // S of the current tile (raw, unmasked)
+    bf16x8 aop[KS];      // rows of Q of the next tile
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const bf16x8 a0 = rrow(sQ0, ks);
+#pragma unroll
+      for (int t = 0; t < 2; ++t) cur[t] = mfma32(a0, bop[t][ks], cur[t]);
+    }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) aop[ks] = rrow(sQ1, ks);
+    f32x4 lb[4];  // L log2(e) of the rows this lane holds (register 4g + c: row 8g + 4h + c)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) lb[g] = rvec4(sL0, g);
+    int ct = t_lo;
+    run([&](auto J, int) {
+      begin_step(J);
+      const int i0 = ct * BQ;  // first query of tile s
+      if (++ct == t_hi) ct = t_lo;
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int kw0 = kg0 + 32 * t;
+        bool need_mask = false;
+        if (p.causal) need_mask |= i0 < kw0 + 31;
+        if (W > 0) {
+          need_mask |= (i0 + BQ - 1) - kw0 >= W;
+          if (!p.causal) need_mask |= (kw0 + 31) - i0 >= W;
+        }
+        if (need_mask) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int q = i0 + 8 * (r >> 2) + 4 * h + (r & 3);
+            cur[t][r] = (q < qmin[t] || q > qmax[t]) ? -__builtin_inff() : cur[t][r];
+          }
+        }
+      }
+      const __bf16* qx = sq(IC<decltype(J)::value + 2>());  // Q of tile s+2
+      char* pw = (char*)sp(J);
+      f32x16 snext[2] = {};
+      float pv[32];
+      __builtin_amdgcn_sched_barrier(0);
+      // S of tile s+1 (operands read during the step before); four elements
+      // of P of tile s per K-step (element e = 16 t + r is register r of
+      // tile t; chunk e / 4 is complete after K-step e / 4 and goes out at
+      // once); each operand register takes the next tile's row once used.
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          snext[t] = mfma32(aop[ks], bop[t][ks], snext[t]);
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const int e = 4 * ks + 2 * t + u, te = e >> 4, r = e & 15;
+            pv[e] = fast_exp2(fmaf(cur[te][r], s2, -lb[r >> 2][r & 3]));
+          }
+        }
+        aop[ks] = rrow(qx, ks);
+        *(f32x4*)(pw + poff + 1024 * ks) =
+            (f32x4){pv[4 * ks], pv[4 * ks + 1], pv[4 * ks + 2], pv[4 * ks + 3]};
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int g = 0; g < 4; ++g) lb[g] = rvec4(sl(IC<decltype(J)::value + 1>()), g);
+      cur[0] = snext[0];
+      cur[1] = snext[1];
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): P of tile s is in LDS
+      end_step();
+    });
+  } else if (role == 1) {
+    // ---- dP wave
+    bf16x8 bop[2][KS];  // -V^T
+    {
+      const auto r = make_rsrc(p.v + head, head_bytes);
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          bop[t][ks] = __builtin_bit_cast(
+              bf16x8,
+              buf_load16(r, (uint32_t)((kg0 + 32 * t + n) * D + 16 * ks + 8 * h) * 2u) ^
+                  0x80008000u);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_s_barrier();
+    f32x16 cur[2] = {};  // D - dP of the tile before the current one
+    bf16x8 aop[KS];      // rows of dO of the current tile
+    f32x4 dv[4];         // D of the rows this lane holds
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) aop[ks] = rrow(sO0, ks);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) dv[g] = rvec4(sD0, g);
+    run([&](auto J, int) {
+      begin_step(J);
+      f32x16 dpn[2];
 #pragma unroll
       for (int g = 0; g < 4; ++g)
-        *(f32x4*)(out + row + 32 * dt + 8 * g + 4 * h) =
-            (f32x4){acc[dt][4 * g] * sc, acc[dt][4 * g + 1] * sc, acc[dt][4 * g + 2] * sc,
-                    acc[dt][4 * g + 3] * sc};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) dpn[0][4 * g + c] = dv[g][c];
+      dpn[1] = dpn[0];
+      const char* pr = (const char*)sp(IC<decltype(J)::value + 1>());  // P of tile s-1
+      char* sw = (char*)ss(IC<decltype(J)::value + 1>());              // dS of tile s-1
+      const __bf16* ox = so(IC<decltype(J)::value + 1>());             // dO of tile s+1
+      f32x4 pp[8];
+      bf16x8 dsop[2][2];
+      __builtin_amdgcn_sched_barrier(0);
+      // D - dP of tile s, and dS of tile s-1 from K-step 2 on (elements
+      // EB[ks] .. EB[ks+1]-1 in K-step ks; element e = 16 t + r is register
+      // r of key tile t), so that the first MFMAs do not wait for P, which
+      // is read from K-step 0 on; chunk e / 8 of dS goes out once complete;
+      // each operand register takes the next tile's row once used.
+      constexpr int EB[KS + 1] = {0, 0, 0, 4, 10, 16, 22, 28, 32};
+      constexpr int PK[8] = {0, 0, 1, 2, 3, 3, 4, 5};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        // P chunk c is read in K-step PK[c], at least one K-step before use.
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+          if (PK[c] == ks) pp[c] = *(const f32x4*)(pr + poff + 1024 * c);
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          dpn[t] = mfma32(aop[ks], bop[t][ks], dpn[t]);
+          const int half = (EB[ks + 1] - EB[ks]) / 2;
+          const int e0 = EB[ks] + t * half, e1 = t ? EB[ks + 1] : EB[ks] + half;
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {  // constant trip count: fully unrolled
+            const int e = e0 + u;
+            if (e < e1) {
+              const int te = e >> 4, r = e & 15;
+              dsop[te][r >> 3][r & 7] = (__bf16)(pp[e >> 2][e & 3] * cur[te][r]);
+            }
+          }
+        }
+        aop[ks] = rrow(ox, ks);
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          if (8 * c + 8 > EB[ks] && 8 * c + 8 <= EB[ks + 1])
+            *(bf16x8*)(sw + soff + 1024 * c) = dsop[c >> 1][c & 1];
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int g = 0; g < 4; ++g) dv[g] = rvec4(sd(IC<decltype(J)::value + 1>()), g);
+      cur[0] = dpn[0];
+      cur[1] = dpn[1];
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): dS of tile s-1 is in LDS
+      end_step();
+    });
+  } else {
+    // ---- dV wave (role 2: tile s-2 at step s) and dK wave (role 3: tile s-3)
+    const bool vwave = role == 2;
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_s_barrier();
+    f32x16 acc[2][DT];  // dV^T, or -dK^T / s, of key tiles 0 and 1
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) acc[t][dt] = (f32x16){};
+    bf16x8 top[2 * DT];  // A operands (K-step j / DT, d-tile j % DT), read the step before
+    bf16x8 bo[2][2];     // B operands (P or dS, bf16) of key tile t, K-step kk
+#pragma unroll
+    for (int j = 0; j < 2 * DT; ++j) top[j] = (bf16x8){};
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) bo[t][kk] = (bf16x8){};
+    // This step's products, each A operand register taking the next tile's
+    // operand once used.  The MFMAs run at every step; outside a wave's
+    // tiles its B operands are zero (and its A operands finite: the slots
+    // read before their first tile arrives were cleared), so they add
+    // exactly nothing.
+    auto product = [&](const __bf16* ax) {
+#pragma unroll
+      for (int j = 0; j < 2 * DT; ++j) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+          acc[t][j % DT] = mfma32(top[j], bo[t][j / DT], acc[t][j % DT]);
+        top[j] = rtr(ax, j);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    if (vwave) {
+      // Step s: dV += dO_{s-2}^T P_{s-2}; reads dO of tile s-1 (slot s+5)
+      // and P of tile s-1 (buffer s+1).
+      run([&](auto J, int s) {
+        begin_step(J);
+        __builtin_amdgcn_sched_barrier(0);
+        product(so(IC<decltype(J)::value + 5>()));
+        const char* pr = (const char*)sp(IC<decltype(J)::value + 1>());
+        const bool next = s + 1 >= 2 && s + 1 <= U + 1;  // dV of tile s-1 at step s+1
+        f32x4 pp[8];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) pp[c] = *(const f32x4*)(pr + poff + 1024 * c);
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int kk = 0; kk < 2; ++kk) {
+            bf16x8 b;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) b[j] = (__bf16)pp[4 * t + 2 * kk + (j >> 2)][j & 3];
+            bo[t][kk] = next ? b : (bf16x8){};
+          }
+        end_step();
+      });
+    } else {
+      // Step s: dK += Q_{s-3}^T dS_{s-3}; reads Q of tile s-2 (slot s+4)
+      // and dS of tile s-2 (buffer s).
+      run([&](auto J, int s) {
+        begin_step(J);
+        __builtin_amdgcn_sched_barrier(0);
+        product(sq(IC<decltype(J)::value + 4>()));
+        const char* sr = (const char*)ss(J);
+        const bool next = s + 1 >= 3;  // dK of tile s-2 at step s+1
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int kk = 0; kk < 2; ++kk) {
+            const bf16x8 b = *(const bf16x8*)(sr + soff + 1024 * (2 * t + kk));
+            bo[t][kk] = next ? b : (bf16x8){};
+          }
+        end_step();
+      });
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // no load may land after the workgroup ends
+    // With the group split, this share's partial sums go to the workspace.
+    float* out = vwave ? p.dv : p.dk;
+    if (p.split > 1) {
+      const size_t part = (size_t)(gridDim.x / p.n_tiles / p.split) * N * D;
+      out = (vwave ? p.dv_part : p.dk_part) + share * part;
+    }
+    const float sc = vwave ? 1.f : -p.scale;  // (dS negated)
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int my_k = kg0 + 32 * t + n;
+      if (my_k < N) {
+        const size_t row = head + (size_t)my_k * D;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+            *(f32x4*)(out + row + 32 * dt + 8 * g + 4 * h) =
+                (f32x4){acc[t][dt][4 * g] * sc, acc[t][dt][4 * g + 1] * sc,
+                        acc[t][dt][4 * g + 2] * sc, acc[t][dt][4 * g + 3] * sc};
+      }
+    }
+    return;
   }
+  __builtin_amdgcn_s_waitcnt(0);  // no load may land after the workgroup ends
 }
 
 // --------------------------------------------------- dK, dV ping-pong (d = 64)
@@ -1829,8 +1991,8 @@ hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream, const char** na
     e = go<bwd_dkdv_kernel<128, W, kDropQTile, true>>(
         name, kname("attn::bwd_dkdv_kernel", 128, W, kDropQTile, true), grid, block, stream, p);
   else if (a.d == 128)
-    e = go<bwd_dkdv_pair_kernel<128, W>>(name, kname("attn::bwd_dkdv_pair_kernel", 128, W),
-                                         grid, dim3(2 * 64 * W), stream, p);
+    e = go<bwd_dkdv_quad_kernel<128>>(name, kname("attn::bwd_dkdv_quad_kernel", 128), grid,
+                                      dim3(512), stream, p);
   else if (drop)
     e = go<bwd_dkdv_kernel<64, W, kDropQTile, true>>(
         name, kname("attn::bwd_dkdv_kernel", 64, W, kDropQTile, true), grid, block, stream, p);

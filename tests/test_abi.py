@@ -238,7 +238,7 @@ def test_decode_rejects_small_workspace_and_null_pointers(ea):
     (1, 4, 16, 2048, 128, True, 0.0, "attn::bwd_dq_pp_kernel<128, 4>"),
     (1, 4, 16, 2048, 64, True, 0.0, "attn::bwd_dq_kernel<64, 4, 64, false>"),
     (1, 4, 16, 2048, 64, True, 0.1, "attn::bwd_dq_kernel<64, 4, 64, true>"),
-    (2, 4, 16, 2048, 128, False, 0.0, "attn::bwd_dkdv_pair_kernel<128, 4>"),
+    (2, 4, 16, 2048, 128, False, 0.0, "attn::bwd_dkdv_quad_kernel<128>"),
     (2, 4, 16, 2048, 64, False, 0.0, "attn::bwd_dkdv_pp_kernel<64, 4>"),
     (2, 4, 16, 2048, 64, True, 0.0, "attn::bwd_dkdv_kernel<64, 4, 32, false>"),
     (2, 4, 16, 2048, 128, True, 0.1, "attn::bwd_dkdv_kernel<128, 4, 32, true>"),
