@@ -56,10 +56,10 @@ def test_ragged_shapes_and_masks(ea, N, d, causal, window):
 
 
 # At d = 128 the dK/dV pass walks 32-row query tiles in a loop unrolled six
-# steps deep, with separate tails for its two wave roles.  Non-causal, every
-# key block walks N / 32 tiles: N = 32 .. 384 covers walks of 1 to 12 tiles
-# (every remainder of the unrolled loop, twice); causal at N = 416 the four
-# key blocks walk 13, 9, 5 and 1.
+# steps deep: U tiles take U + 3 steps, its four wave roles running up to
+# three tiles apart.  Non-causal, every key block walks N / 32 tiles: N = 32
+# .. 384 covers walks of 1 to 12 tiles (every remainder of the unrolled loop,
+# twice); causal at N = 416 the four key blocks walk 13, 9, 5 and 1.
 @pytest.mark.parametrize("N,causal", [(32 * u, False) for u in range(1, 13)] + [(416, True)])
 def test_dkdv_tile_walk_lengths(ea, N, causal):
     d = 128
