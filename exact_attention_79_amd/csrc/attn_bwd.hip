@@ -491,6 +491,13 @@ __global__ __launch_bounds__(NW * 64, (dkdv_waves_per_simd<D, BQ>())) void bwd_d
 template <int V>
 using IC = std::integral_constant<int, V>;
 
+// Heads per group of the causal walk of the kernel below (see causal_group):
+// two, against four for the other kernels.  Measured on one box (causal
+// dK/dV launch, ms): B4 H16 N2048 0.186 with two or four heads, N4096 0.558
+// / 0.559, B2 H32 N8192 1.985 / 2.017, B1 H32 N16384 3.71 / 3.86; one head
+// per group is slower at N <= 4096 (0.21 and 0.58).
+constexpr int kQuadCausalGroup = 2;
+
 template <int D>
 __global__ __launch_bounds__(512, 2) void bwd_dkdv_quad_kernel(BwdKParams p) {
   constexpr int BQ = 32;               // query rows per step
@@ -561,7 +568,7 @@ __global__ __launch_bounds__(512, 2) void bwd_dkdv_quad_kernel(BwdKParams p) {
   const int kg = (w >> 1) & 1;                              // key group
   const int h = lane >> 5, n = lane & 31;
   const TileId id =
-      tile_order(blockIdx.x, gridDim.x / p.n_tiles, p.n_tiles, p.causal, causal_group<D>());
+      tile_order(blockIdx.x, gridDim.x / p.n_tiles, p.n_tiles, p.causal, kQuadCausalGroup);
   const int bkv = id.bh / p.split;  // key/value head (b * Hkv + hk)
   const int share = id.bh % p.split;
   const int kt = id.rank;
