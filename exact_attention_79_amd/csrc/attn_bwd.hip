@@ -623,9 +623,9 @@ __global__ __launch_bounds__(512, 2) void bwd_dkdv_quad_kernel(BwdKParams p) {
   };
 
   // Fetch cursor (query head lj of the group, tile lt), three tiles ahead
-  // of the step; past the last head it keeps reading the last head's rows
-  // (in bounds, never used).  The buffer resources span the whole query
-  // head (rows past N read as zero) and change only with the head; each
+  // of the step.  The buffer resources span the whole query head (rows past
+  // N read as zero) and change only with the head; past the last head they
+  // are empty, so the tiles fetched after the last one are zeros.  Each
   // wave moves one 1 KB piece of the Q and dO tiles (as tile_load_lds),
   // lane L the global chunk that the swizzle puts at LDS chunk 64 w + L.
   static_assert(BQ * D / 8 == 64 * NWV, "one 16-byte chunk per lane and tile");
@@ -637,11 +637,12 @@ __global__ __launch_bounds__(512, 2) void bwd_dkdv_quad_kernel(BwdKParams p) {
   }
   __amdgpu_buffer_rsrc_t rq, ro, rl, rd;
   auto set_head = [&]() {
+    const bool live = lj < G;
     const int bhq = bh0 + min(lj, G - 1);
-    rq = make_rsrc(p.q + (size_t)bhq * N * D, head_bytes);
-    ro = make_rsrc(p.dout + (size_t)bhq * N * D, head_bytes);
-    rl = make_rsrc(p.lse2 + (size_t)bhq * N, (uint32_t)N * 4);
-    rd = make_rsrc(p.delta + (size_t)bhq * N, (uint32_t)N * 4);
+    rq = make_rsrc(p.q + (size_t)bhq * N * D, live ? head_bytes : 0u);
+    ro = make_rsrc(p.dout + (size_t)bhq * N * D, live ? head_bytes : 0u);
+    rl = make_rsrc(p.lse2 + (size_t)bhq * N, live ? (uint32_t)N * 4 : 0u);
+    rd = make_rsrc(p.delta + (size_t)bhq * N, live ? (uint32_t)N * 4 : 0u);
   };
   set_head();
   auto load_tile = [&](auto J) {
@@ -906,9 +907,9 @@ __global__ __launch_bounds__(512, 2) void bwd_dkdv_quad_kernel(BwdKParams p) {
       for (int kk = 0; kk < 2; ++kk) bo[t][kk] = (bf16x8){};
     // This step's products, each A operand register taking the next tile's
     // operand once used.  The MFMAs run at every step; outside a wave's
-    // tiles its B operands are zero (and its A operands finite: the slots
-    // read before their first tile arrives were cleared), so they add
-    // exactly nothing.
+    // tiles its A and B operands are zero (the slots read before the first
+    // tile arrives were cleared, the tiles after the last one are fetched
+    // as zeros), so they add exactly nothing whatever the inputs hold.
     auto product = [&](const __bf16* ax) {
 #pragma unroll
       for (int j = 0; j < 2 * DT; ++j) {
