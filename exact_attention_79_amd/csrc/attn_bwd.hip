@@ -506,7 +506,6 @@ __global__ __launch_bounds__(512, 2) void bwd_dkdv_quad_kernel(BwdKParams p) {
   constexpr int KS = D / 16;           // K-steps of S and dP
   constexpr int DT = D / 32;           // d-tiles of dK and dV
   constexpr int LDROWS = 64;           // L and D are staged one dword per lane
-  constexpr int AHEAD = 3;             // operand reads ahead of their MFMAs
   constexpr int PF = 2 * 8 * 64 * 4;   // floats of a P buffer: 2 groups x 8 chunks per lane
   constexpr int SH = 2 * 4 * 64 * 8;   // bf16 of a dS buffer: 2 groups x 4 chunks per lane
   static_assert(D == 128, "four-role dK/dV kernel is for d = 128");
@@ -623,17 +622,24 @@ __global__ __launch_bounds__(512, 2) void bwd_dkdv_quad_kernel(BwdKParams p) {
   };
 
   // Fetch cursor (query head lj of the group, tile lt), three tiles ahead
-  // of the step.  The buffer resources span the whole query head (rows past
-  // N read as zero) and change only with the head; past the last head they
-  // are empty, so the tiles fetched after the last one are zeros.  Each
-  // wave moves one 1 KB piece of the Q and dO tiles (as tile_load_lds),
-  // lane L the global chunk that the swizzle puts at LDS chunk 64 w + L.
-  static_assert(BQ * D / 8 == 64 * NWV, "one 16-byte chunk per lane and tile");
+  // of the step, kept by the dK and dV waves (waves 4-7), which fetch every
+  // tile: the S wave's own instruction stream is the step's critical path.
+  // The buffer resources span the whole query head (rows past N read as
+  // zero) and change only with the head; past the last head they are empty,
+  // so the tiles fetched after the last one are zeros.  Wave 4 + f moves
+  // 1 KB pieces f and f + 4 of the Q and dO tiles (as tile_load_lds), lane L
+  // of piece c the global chunk that the swizzle puts at LDS chunk 64 c + L.
+  constexpr int NFW = 4;  // fetching waves
+  static_assert(BQ * D / 8 == 2 * 64 * NFW, "two 16-byte chunks per lane and tile");
+  const bool fetcher = w >= NWV - NFW;
+  const int fw = w - (NWV - NFW);
   int lj = 0, lt = t_lo;
-  uint32_t chunk_off;
-  {
-    const int pc = w * 64 + lane, row = pc / (D / 8), ch = (pc % (D / 8)) ^ swz<D>(row);
-    chunk_off = (uint32_t)(row * D + ch * 8) * 2u;
+  uint32_t chunk_off[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int pc = (fw + NFW * i) * 64 + lane, row = pc / (D / 8);
+    const int ch = (pc % (D / 8)) ^ swz<D>(row);
+    chunk_off[i] = (uint32_t)(row * D + ch * 8) * 2u;
   }
   __amdgpu_buffer_rsrc_t rq, ro, rl, rd;
   auto set_head = [&]() {
@@ -646,15 +652,20 @@ __global__ __launch_bounds__(512, 2) void bwd_dkdv_quad_kernel(BwdKParams p) {
   };
   set_head();
   auto load_tile = [&](auto J) {
-    const uint32_t voff = chunk_off + (uint32_t)lt * (BQ * D * 2);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (LDS_AS void*)(sq(J) + w * 64 * 8), 16,
-                                             (int)voff, 0, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(ro, (LDS_AS void*)(so(J) + w * 64 * 8), 16,
-                                             (int)voff, 0, 0, 0);
-    if (w == 0)
+    if (!fetcher) return;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const uint32_t voff = chunk_off[i] + (uint32_t)lt * (BQ * D * 2);
+      const int c = fw + NFW * i;  // piece of the tile
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (LDS_AS void*)(sq(J) + c * 64 * 8), 16,
+                                               (int)voff, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ro, (LDS_AS void*)(so(J) + c * 64 * 8), 16,
+                                               (int)voff, 0, 0, 0);
+    }
+    if (fw == 0)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, (LDS_AS void*)sl(J), 4,
                                                (int)((uint32_t)(lt * BQ + lane) * 4u), 0, 0, 0);
-    if (w == 1)
+    if (fw == 1)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rd, (LDS_AS void*)sd(J), 4,
                                                (int)((uint32_t)(lt * BQ + lane) * 4u), 0, 0, 0);
     if (++lt == t_hi) {
@@ -681,7 +692,7 @@ __global__ __launch_bounds__(512, 2) void bwd_dkdv_quad_kernel(BwdKParams p) {
     load_tile(IC<decltype(J)::value + 3>());
     hide_offsets();
   };
-  // This step's tile has landed for every wave after the barrier.
+  // This step's tile has landed (for every wave after the barrier).
   auto end_step = [&]() {
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     __builtin_amdgcn_s_barrier();
