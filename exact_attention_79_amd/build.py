@@ -42,13 +42,15 @@ PROBES = {os.path.join(HERE, "probes", "dq_atomic_adds.hip"):
           os.path.join(HERE, "probes", "dot_precision.hip"):
           os.path.join(HERE, "probes", "dot_precision"),
           os.path.join(HERE, "probes", "mfma_power.hip"):
-          os.path.join(HERE, "probes", "mfma_power")}
+          os.path.join(HERE, "probes", "mfma_power"),
+          os.path.join(HERE, "probes", "halfstep.hip"):
+          os.path.join(HERE, "probes", "halfstep")}
 
 
 def _build_probe(src: str, exe: str):
-    cmd = [HIPCC, "--offload-arch=gfx950", "-O3", "-munsafe-fp-atomics",
+    cmd = [HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-munsafe-fp-atomics",
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-           "-Wno-unused-command-line-argument", src, "-o", exe]
+           "-Wno-unused-command-line-argument", "-I" + CSRC, src, "-o", exe]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
