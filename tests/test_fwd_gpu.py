@@ -160,3 +160,25 @@ def test_deterministic_and_stream_respecting(ea):
     side.synchronize()
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("N,d", [(512, 128), (700, 128), (512, 64), (700, 64)])
+@pytest.mark.parametrize("causal,window", [(False, 0), (True, 0), (False, 100)])
+def test_two_pipelines_agree_bitwise(ea, N, d, causal, window):
+    """The same head through both forward pipelines: alone (fewer than four
+    256-query workgroups: free-running waves, one barrier per tile) and as one
+    head of a larger launch (the ping-pong kernel: lockstep half-steps).  They
+    do the same arithmetic in the same order on differently scheduled LDS
+    rings, so any race in either ring shows up as a bit difference."""
+    log(f"case: two pipelines, N{N} d{d} causal={causal} window={window}")
+    dev, _ = bf16_case(700 + N + d, 2, 4, N, d)
+    q, k, v = dev["q"], dev["k"], dev["v"]
+    names = (ea.kernel_name(ea.STAGE_FWD, 1, 1, N, d, causal, window),
+             ea.kernel_name(ea.STAGE_FWD, 2, 4, N, d, causal, window))
+    assert "fwd_bf16_kernel" in names[0] and "fwd_pp_kernel" in names[1], names
+    o_all, l_all = ea.attn_fwd(q, k, v, causal=causal, window=window)
+    b, h = 1, 2
+    o_one, l_one = ea.attn_fwd(q[b:b + 1, h:h + 1].contiguous(), k[b:b + 1, h:h + 1].contiguous(),
+                               v[b:b + 1, h:h + 1].contiguous(), causal=causal, window=window)
+    torch.cuda.synchronize()
+    assert torch.equal(o_one[0, 0], o_all[b, h]) and torch.equal(l_one[0, 0], l_all[b, h])
