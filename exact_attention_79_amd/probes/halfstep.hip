@@ -92,7 +92,7 @@ __global__ __launch_bounds__(512, 1) void coissue(uint64_t* out, int iters, int 
     const uint64_t c1 = __builtin_amdgcn_s_memtime();
     float s = 0.f;
     for (int r = 0; r < 16; ++r) s += a0[r] + a1[r] + a2[r] + a3[r];
-    if (lane == 0) out[blockIdx.x * 4 + w] = (c1 - c0) + (s == 12345.f);
+    if (lane == 0) out[blockIdx.x * 8 + w] = (c1 - c0) + (s == 12345.f);
   } else {
     float x[11];
     for (int i = 0; i < 8; ++i) x[i] = lane * 0.01f - i * 0.1f;
@@ -113,7 +113,7 @@ __global__ __launch_bounds__(512, 1) void coissue(uint64_t* out, int iters, int 
     }
     float s = x[10];
     for (int i = 0; i < 8; ++i) s += x[i];
-    if (s == 12345.f && lane == 0) out[blockIdx.x * 4] += 1;  // keeps the work
+    if (lane == 0) out[blockIdx.x * 8 + w] = (s == 12345.f);  // keeps the work
   }
 }
 
@@ -124,9 +124,10 @@ static int part1(uint64_t* d, uint64_t* h, const char* name, bool print) {
     hipLaunchKernelGGL((coissue<VK, AG>), dim3(kCUs), dim3(512), 0, 0, d, iters, viters);
   CHECK(hipGetLastError());
   CHECK(hipDeviceSynchronize());
-  CHECK(hipMemcpy(h, d, kCUs * 4 * sizeof(uint64_t), hipMemcpyDeviceToHost));
+  CHECK(hipMemcpy(h, d, kCUs * 8 * sizeof(uint64_t), hipMemcpyDeviceToHost));
   double c = 0;
-  for (int i = 0; i < kCUs * 4; ++i) c += (double)h[i];
+  for (int b = 0; b < kCUs; ++b)
+    for (int w = 0; w < 4; ++w) c += (double)h[b * 8 + w];
   if (print) std::printf("| %s | %.1f |\n", name, c / (kCUs * 4) / (16.0 * iters));
   return 0;
 }
